@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 paged-KV hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input resident in
+HBM: encode the batch's bf16 K/V pages into the packed NVFP4 pool
+(kvfp4_quantize_pages), run single-token decode attention over the packed
+pool (kvfp4_paged_decode_attention, dequantizing in-kernel), and decode the
+pages back to bf16 (kvfp4_dequantize_pages).  Default workload: the
+Llama-3-8B-shaped layer (batch 32, 32 q / 8 KV heads, head_dim 128, 8192
+tokens, 64-token pages in a seeded permutation; 4096 pages).
+
+Timing: HIP events on the stream the kernels run on, around each kernel;
+between kernels an untimed 1 GiB write evicts the 256 MiB Infinity Cache so
+that bytes come from HBM.  `value` is the step's algorithmic bytes divided
+by its kernel time.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b",
+                   choices=["tiny", "llama3_8b", "qwen3_8b_long", "mla", "cold_pages"])
+    p.add_argument("--gs", default="calibrated", choices=["calibrated", "unit"])
+    p.add_argument("--no-flush", action="store_true", help="do not evict caches between kernels")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-pages", type=int, default=6)
+    return p.parse_args()
+
+
+def decode_bytes(wl) -> dict:
+    """Algorithmic bytes of one decode call: the packed K/V rows of every
+    cached token, Q, the output, the used page-table entries and lengths."""
+    nt, T, H, D = wl.geometry
+    L = wl.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * nt * H * D * 9 // 16
+    q = wl.batch * wl.num_q_heads * D * 2
+    out = wl.batch * wl.num_q_heads * wl.v_dim * 2 + wl.batch * wl.num_q_heads * 4
+    bt = int(np.sum(-(-L // T))) * 4 + wl.batch * 4
+    flops = 2 * int(L.sum()) * wl.num_q_heads * (D + wl.v_dim)
+    return {"bytes": kv + q + out + bt, "kv_bytes": kv, "flops": flops}
+
+
+def codec_bytes(geometry, pages: int) -> int:
+    nt, T, H, D = geometry
+    e = nt * T * H * D
+    return pages * (2 * e + e * 9 // 16)
+
+
+def cpu_baseline(wl, gs, pages: int, dec_bytes_per_token: float, step_bytes: float,
+                 step_unit_bytes: dict) -> dict:
+    """The oracle as it stands, on one host thread, over a bounded sample of
+    the same workload: `pages` pages encoded and decoded, and decode
+    attention for one sequence (all its query heads).  Reported in GB/s of
+    algorithmic bytes over the same byte accounting as the GPU figure."""
+    from threadpoolctl import threadpool_limits
+    from oracle import nvfp4 as O
+    from oracle import attention as A
+    g = O.Geometry(*wl.geometry)
+    slots = wl.used_slots[:pages]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        packed = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
+        O.quantize_pages(wl.hot_pool, g, pages, gs, packed, slots, slots)
+        t1 = time.perf_counter()
+        back = np.zeros((pages, *g.row_shape), np.uint16)
+        O.dequantize_pages(packed, g, pages, gs, back, slots, None)
+        t2 = time.perf_counter()
+        # decode over the first sequence: its pages are the first ones used
+        b = 0
+        need = -(-int(wl.seq_lens[b]) // wl.page_size)
+        bslots = wl.block_table[b, :need]
+        O.quantize_pages(wl.hot_pool, g, need, gs, packed, bslots, bslots)
+        t3 = time.perf_counter()
+        A.decode_attention(packed, g, gs, wl.q, wl.block_table, wl.seq_lens, wl.softmax_scale,
+                           wl.v_dim, batch_indices=[b])
+        t4 = time.perf_counter()
+    q_s, dq_s, dec_s = t1 - t0, t2 - t1, t4 - t3
+    # scale each leg to the whole step's bytes of that leg
+    per_page = codec_bytes(wl.geometry, 1)
+    t_step = (step_unit_bytes["quantize"] / (pages * per_page)) * q_s + \
+             (step_unit_bytes["dequantize"] / (pages * per_page)) * dq_s + \
+             (step_unit_bytes["decode"] / (int(wl.seq_lens[b]) * dec_bytes_per_token)) * dec_s
+    return {"value": round(step_bytes / t_step / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"oracle on 1 host thread: encode {pages} pages ({q_s:.2f} s), decode "
+                       f"{pages} pages ({dq_s:.2f} s), attention for sequence 0 "
+                       f"({int(wl.seq_lens[b])} tokens, all {wl.num_q_heads} q heads, "
+                       f"{dec_s:.2f} s); scaled to the step's bytes"),
+            "seconds": round(q_s + dq_s + dec_s, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not a built component.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_paged_decode_amd as K
+    from nvfp4_paged_decode_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    K.load_library()
+
+    t_gen = time.perf_counter()
+    name = args.workload
+    if name == "cold_pages":
+        cw = W.cold_pages()
+        wl = None
+    else:
+        wl = W.FULL[name]()
+    t_gen = time.perf_counter() - t_gen
+
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    if wl is not None:
+        geometry = wl.geometry
+        gs = [float(v) for v in (wl.gs_calibrated if args.gs == "calibrated" else wl.gs_unit)]
+        hot = torch.from_numpy(wl.hot_pool.view(np.int16)).to(dev)
+        pages = int(wl.used_slots.shape[0])
+        slots = torch.from_numpy(wl.used_slots.astype(np.int32)).to(dev)
+        num_slots = wl.num_slots
+    else:
+        geometry = cw.geometry
+        gs = [float(v) for v in (cw.gs_calibrated if args.gs == "calibrated" else cw.gs_unit)]
+        hot = torch.from_numpy(cw.hot_pool.view(np.int16)).to(dev)
+        pages = cw.num_pages
+        slots = torch.from_numpy(cw.src_slots).to(dev)
+        num_slots = cw.num_pages
+    pbytes = K.kvfp4_packed_page_bytes(geometry)
+    packed = torch.zeros((num_slots, pbytes), dtype=torch.uint8, device=dev)
+    hot_back = torch.empty_like(hot)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    if wl is not None:
+        q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
+        bt = torch.from_numpy(wl.block_table).to(dev)
+        sl = torch.from_numpy(wl.seq_lens).to(dev)
+        hint = int(wl.seq_lens.max())
+        ws_n = K.kvfp4_decode_workspace_bytes(geometry, wl.batch, wl.num_q_heads, wl.v_dim, hint)
+        ws = torch.empty(max(ws_n, 4), dtype=torch.uint8, device=dev)
+        out = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), dtype=torch.int16, device=dev)
+        lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+
+    def k_quant():
+        K.kvfp4_quantize_pages(geometry, hot, packed, pages, gs, slots, slots)
+
+    def k_decode():
+        K.kvfp4_paged_decode_attention(geometry, packed, gs, q, bt, sl, hint, wl.softmax_scale,
+                                       out, lse, ws, v_dim=wl.v_dim)
+
+    def k_dequant():
+        K.kvfp4_dequantize_pages(geometry, packed, hot_back, pages, gs, slots, slots)
+
+    legs = [("quantize", k_quant)]
+    if wl is not None:
+        legs.append(("decode", k_decode))
+    legs.append(("dequantize", k_dequant))
+
+    def run(n_steps, timed):
+        ev = {k: [] for k, _ in legs}
+        for _ in range(n_steps):
+            for k, fn in legs:
+                if not args.no_flush:
+                    flush.fill_(1)
+                if timed:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    ev[k].append((e0, e1))
+                else:
+                    fn()
+        return ev
+
+    run(args.warmup, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev = run(args.steps, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {k: [a.elapsed_time(b) for a, b in v] for k, v in ev.items()}
+    avg = {k: float(np.mean(v)) for k, v in ms.items()}
+    med = {k: float(np.median(v)) for k, v in ms.items()}
+    step_ms = float(sum(avg.values()))
+
+    cb = codec_bytes(geometry, pages)
+    leg_bytes = {"quantize": cb, "dequantize": cb}
+    kern = {}
+    if wl is not None:
+        db = decode_bytes(wl)
+        leg_bytes["decode"] = db["bytes"]
+    for k in leg_bytes:
+        gbs = leg_bytes[k] / (avg[k] * 1e-3) / 1e9
+        kern[k] = {"avg_us": round(avg[k] * 1e3, 2), "median_us": round(med[k] * 1e3, 2),
+                   "bytes": leg_bytes[k], "GB/s": round(gbs, 1),
+                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if wl is not None:
+        t = avg["decode"] * 1e-3
+        kern["decode"]["tokens_per_s"] = round(wl.batch / t, 1)
+        kern["decode"]["context_tokens_per_s"] = round(float(wl.seq_lens.sum()) / t, 1)
+        kern["decode"]["TFLOP/s"] = round(db["flops"] / t / 1e12, 2)
+        kern["decode"]["frac_bf16_mfma_peak"] = round(db["flops"] / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    step_bytes = sum(leg_bytes.values())
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    dom = max(avg, key=avg.get)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": None}
+
+    if wl is not None:
+        nt, T, H, D = geometry
+        wdesc = (f"{name}: batch {wl.batch}, {wl.num_q_heads} q / {H} KV heads, head_dim {D}, "
+                 f"v_dim {wl.v_dim}, context {int(wl.seq_lens.min())}-{int(wl.seq_lens.max())} "
+                 f"(sum {int(wl.seq_lens.sum())}), page {T}; step = encode {pages} pages + "
+                 f"decode attention + decode {pages} pages")
+    else:
+        wdesc = f"cold_pages: {pages} pages x {geometry}; step = encode + decode of every page"
+
+    cpu = None
+    if wl is not None and not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(wl, gs, args.cpu_sample_pages,
+                               db["bytes"] / float(wl.seq_lens.sum()), step_bytes, leg_bytes)
+        except Exception as e:  # the GPU figure stands on its own
+            cpu = {"error": repr(e)}
+
+    line = {
+        "metric": "NVFP4-KV decode attn effective HBM GB/s (% peak) + page quant/dequant GB/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16<->nvfp4 codec (integer thresholds), fp32 attention",
+        "data": "synthetic (seeded)",
+        "config": {"workload": wdesc, "global_scale": args.gs, "cache_flush_between_kernels":
+                   not args.no_flush, "global_batch": wl.batch if wl is not None else None,
+                   "seq_len": int(wl.seq_lens.max()) if wl is not None else None,
+                   "parallelism": "single GPU"},
+        "kernels": kern,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall, 3),
+        "gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * kvfp4.h -- NVFP4 paged KV cache for AMD MI355X (gfx950): page codec and
+ * single-token decode attention that dequantizes NVFP4 K/V in-kernel.
+ *
+ * Format ("Accelerating Long-Context and Agentic Inference with NVFP4 KV
+ * Cache", introduction and Figure 1; NVFP4 KV Decode Attention Kernel
+ * Implementation): E2M1 4-bit values, one E4M3 (OCP E4M3FN) scale per
+ * block of 16 values, one FP32 scale per tensor.  A block is 8 bytes of
+ * packed codes plus 1 scale byte.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Plain C ABI; pointers are device pointers unless marked HOST.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *   default stream), never synchronizes, never allocates, and keeps no
+ *   state between calls, so calls are thread-safe and re-entrant.  The
+ *   caller owns every buffer; they must stay valid until the stream work
+ *   has completed.  Input and output buffers must not overlap.
+ * - All arguments are validated on the host BEFORE anything is launched;
+ *   on error nothing is launched and a negative status is returned, with
+ *   a thread-local message in kvfp4_last_error_message().
+ * - Device-side data (slot ids, page table entries, sequence lengths) is
+ *   bounds-checked by the kernels: an out-of-range slot id makes that
+ *   page (or that page of the sequence) contribute nothing / be skipped.
+ *   NaN or Inf bf16 inputs are outside the contract (unspecified output).
+ *
+ * Page layout (one fixed-size block per page, "KV Cache Compression in
+ * TensorRT LLM", NVFP4 Cold-Page Compression / How It Works, Figure 6;
+ * the KV cache manager addresses a page as base + slot * size):
+ * - hot page slot (bf16):   [n_t][T][H][D] row-major, 2*E bytes,
+ *   E = n_t * T * H * D elements, n_t = num_kv_tensors (K then V).
+ * - packed page slot:       E/2 data bytes [n_t][T][H][D/2] followed by
+ *   E/16 scale bytes [n_t][T][H][D/16]: 9*E/16 bytes.  Byte k of a block
+ *   holds element 2k in bits 3:0 and element 2k+1 in bits 7:4; a nibble is
+ *   sign<<3 | E2M1 magnitude code.  A block is 16 consecutive elements
+ *   along D of one (tensor, token, head) row.
+ *
+ * Arithmetic (the readings the pages leave open):
+ * - global_scale[t] is the decode multiplier of tensor t:
+ *   x ~= e2m1 * e4m3 * global_scale[t].
+ * - block scale = E4M3(amax / (6 * gs)), element code = E2M1(|x| / (sb*gs)),
+ *   each rounded once from the exact quotient, to nearest, ties to the
+ *   even code, saturating (448, 6); a block whose scale rounds to 0 stores
+ *   magnitude 0 everywhere; every nibble keeps its input's sign bit.
+ * - dequantized value = bf16_RNE(+-e2m1 * e4m3 * gs), one rounding.
+ */
+#ifndef KVFP4_H_
+#define KVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KVFP4_OK 0
+#define KVFP4_ERR_INVALID_ARG (-1) /* bad pointer, size, scale or shape      */
+#define KVFP4_ERR_UNSUPPORTED (-2) /* valid geometry with no compiled kernel  */
+#define KVFP4_ERR_WORKSPACE (-3)   /* workspace smaller than required         */
+#define KVFP4_ERR_HIP (-4)         /* a HIP launch or runtime call failed     */
+
+/* Page geometry.  num_kv_tensors: 2 = separate K and V (MHA/GQA), 1 = one
+ * shared latent (MLA: the key is the whole row, the value its first v_dim
+ * elements).  head_dim must be a positive multiple of 16. */
+typedef struct kvfp4_geometry {
+  int32_t num_kv_tensors;
+  int32_t page_size;    /* tokens per page T          */
+  int32_t num_kv_heads; /* H                          */
+  int32_t head_dim;     /* D (576 = 512 + 64 for MLA) */
+} kvfp4_geometry;
+
+/* Bytes of one bf16 hot page slot (2*E) and one packed slot (9*E/16); 0 for
+ * an invalid geometry.  Storage: 0.5625 bytes per value ("KV Cache
+ * Compression in TensorRT LLM", Evaluation / Performance, Figure 10). */
+size_t kvfp4_hot_page_bytes(const kvfp4_geometry* g);
+size_t kvfp4_packed_page_bytes(const kvfp4_geometry* g);
+
+/* Encode bf16 hot pages into packed NVFP4 pages ("KV Cache Compression in
+ * TensorRT LLM", How It Works: quantize on offload, one block per page).
+ *   hot_pool    bf16 slots [hot_pool_pages][2*E bytes]           (read)
+ *   src_slots   int32 [num_pages] hot slot of page i; NULL = i
+ *   packed_pool packed slots [packed_pool_pages][9*E/16 bytes]  (written)
+ *   dst_slots   int32 [num_pages] packed slot of page i; NULL = i
+ *   global_scale HOST float [num_kv_tensors]: finite, > 0, and
+ *               2688 * gs <= FLT_MAX.
+ * Pages whose src or dst slot is out of range are skipped.  With NULL slot
+ * arrays num_pages must not exceed the pool.  num_pages == 0 is a no-op.
+ * Duplicate dst slots race (unspecified winner). */
+int32_t kvfp4_quantize_pages(const kvfp4_geometry* g, const void* hot_pool,
+                             int32_t hot_pool_pages, const int32_t* src_slots,
+                             void* packed_pool, int32_t packed_pool_pages,
+                             const int32_t* dst_slots, int32_t num_pages,
+                             const float* global_scale, void* stream);
+
+/* Decode packed pages back into bf16 hot slots (onboard), bit-exact per the
+ * arithmetic above.  Same argument rules as kvfp4_quantize_pages with the
+ * roles of the pools swapped. */
+int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
+                               int32_t packed_pool_pages, const int32_t* src_slots,
+                               void* hot_pool, int32_t hot_pool_pages,
+                               const int32_t* dst_slots, int32_t num_pages,
+                               const float* global_scale, void* stream);
+
+/* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
+ * current device (0 is a valid answer). */
+size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,
+                                    int32_t num_q_heads, int32_t v_dim,
+                                    int32_t max_seq_len_hint);
+
+/* Single-token decode attention over the packed cache ("Accelerating
+ * Long-Context and Agentic Inference with NVFP4 KV Cache", Path 3: Decode
+ * and NVFP4 KV Decode Attention Kernel Implementation / Figure 3): NVFP4
+ * K/V are dequantized in registers, the per-tensor scales enter as scalar
+ * multipliers of the two products.  For sequence b and query head h (KV
+ * head h / (num_q_heads / num_kv_heads)):
+ *   s_j = softmax_scale * q . k_j,  out = sum_j softmax(s)_j v_j,
+ *   lse = log sum_j exp(s_j),   over the seq_lens[b] cached tokens,
+ * token j living in slot block_table[b][j / T], row j % T.
+ *   packed_pool   [packed_pool_pages][9*E/16 bytes]
+ *   global_scale  HOST float [num_kv_tensors] (K, V; MLA: one)
+ *   q             bf16 [batch][num_q_heads][head_dim]
+ *   v_dim         == head_dim when num_kv_tensors == 2; <= head_dim for MLA
+ *   block_table   int32 [batch][max_pages_per_seq]
+ *   seq_lens      int32 [batch]; each <= max_seq_len_hint and
+ *                 <= max_pages_per_seq * T (longer values are clamped)
+ *   max_seq_len_hint HOST upper bound on seq_lens (sizes the split-K plan)
+ *   out           bf16 [batch][num_q_heads][v_dim]
+ *   lse           float [batch][num_q_heads] natural-log LSE, or NULL;
+ *                 seq_lens[b] == 0 gives out = 0 and lse = -inf.
+ *   workspace     >= kvfp4_decode_workspace_bytes(...) bytes (may be NULL
+ *                 when that is 0).
+ * num_q_heads must be a multiple of num_kv_heads. */
+int32_t kvfp4_paged_decode_attention(
+    const kvfp4_geometry* g, const void* packed_pool, int32_t packed_pool_pages,
+    const float* global_scale, const void* q, int32_t batch, int32_t num_q_heads,
+    int32_t v_dim, const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* seq_lens, int32_t max_seq_len_hint, float softmax_scale,
+    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* kvfp4_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* kvfp4_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFP4_H_ */

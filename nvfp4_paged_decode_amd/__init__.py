@@ -1,0 +1,186 @@
+"""NVFP4 paged KV cache for AMD MI355X (gfx950).
+
+Thin ctypes binding of ``libkvfp4.so`` (see ``include/kvfp4.h`` for the
+contract).  Functions carry the C ABI's names; they only marshal torch
+tensors into pointers and sizes, pass torch's current HIP stream, and turn
+a negative status into :class:`KvFp4Error`.  Every step of the computation
+runs in the library's HIP kernels; there is no Python or CPU fallback: if
+the library is not built, every call raises.
+
+Build the library with ``python -m nvfp4_paged_decode_amd.build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvfp4.so")
+
+KVFP4_OK = 0
+KVFP4_ERR_INVALID_ARG = -1
+KVFP4_ERR_UNSUPPORTED = -2
+KVFP4_ERR_WORKSPACE = -3
+KVFP4_ERR_HIP = -4
+
+#: Every function the header declares (checked by the CPU tests).
+EXPORTS = (
+    "kvfp4_hot_page_bytes", "kvfp4_packed_page_bytes", "kvfp4_quantize_pages",
+    "kvfp4_dequantize_pages", "kvfp4_decode_workspace_bytes",
+    "kvfp4_paged_decode_attention", "kvfp4_status_string", "kvfp4_last_error_message",
+)
+
+
+class Geometry(ctypes.Structure):
+    """``kvfp4_geometry``: (num_kv_tensors, page_size, num_kv_heads, head_dim)."""
+
+    _fields_ = [("num_kv_tensors", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, g) -> "Geometry":
+        return g if isinstance(g, cls) else cls(*[int(v) for v in g])
+
+
+class KvFp4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkvfp4.so once.  torch is imported first so that the library
+    binds to the HIP runtime torch already loaded (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run: python -m nvfp4_paged_decode_amd.build")
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    G = ctypes.POINTER(Geometry)
+    lib.kvfp4_hot_page_bytes.argtypes = [G]
+    lib.kvfp4_hot_page_bytes.restype = SZ
+    lib.kvfp4_packed_page_bytes.argtypes = [G]
+    lib.kvfp4_packed_page_bytes.restype = SZ
+    codec = [G, P, I32, P, P, I32, P, I32, P, P]
+    lib.kvfp4_quantize_pages.argtypes = codec
+    lib.kvfp4_quantize_pages.restype = I32
+    lib.kvfp4_dequantize_pages.argtypes = codec
+    lib.kvfp4_dequantize_pages.restype = I32
+    lib.kvfp4_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
+    lib.kvfp4_decode_workspace_bytes.restype = SZ
+    lib.kvfp4_paged_decode_attention.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32, P, I32,
+                                                 F, P, P, P, SZ, P]
+    lib.kvfp4_paged_decode_attention.restype = I32
+    lib.kvfp4_status_string.argtypes = [I32]
+    lib.kvfp4_status_string.restype = ctypes.c_char_p
+    lib.kvfp4_last_error_message.argtypes = []
+    lib.kvfp4_last_error_message.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> int:
+    if status != KVFP4_OK:
+        lib = load_library()
+        msg = lib.kvfp4_last_error_message().decode() or lib.kvfp4_status_string(status).decode()
+        raise KvFp4Error(status, msg)
+    return status
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _scales(global_scale: Sequence[float], n: int):
+    vals = [float(v) for v in list(global_scale)[:n]]
+    if len(vals) < n:
+        raise ValueError(f"global_scale needs {n} values")
+    return (ctypes.c_float * n)(*vals)
+
+
+def _pages(pool, page_bytes: int) -> int:
+    nbytes = pool.numel() * pool.element_size()
+    return nbytes // page_bytes if page_bytes else 0
+
+
+def kvfp4_hot_page_bytes(geometry) -> int:
+    return int(load_library().kvfp4_hot_page_bytes(ctypes.byref(Geometry.of(geometry))))
+
+
+def kvfp4_packed_page_bytes(geometry) -> int:
+    return int(load_library().kvfp4_packed_page_bytes(ctypes.byref(Geometry.of(geometry))))
+
+
+def kvfp4_quantize_pages(geometry, hot_pool, packed_pool, num_pages: int, global_scale,
+                         src_slots=None, dst_slots=None, stream=None) -> None:
+    """Encode ``num_pages`` bf16 pages of ``hot_pool`` into ``packed_pool``."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    _check(lib.kvfp4_quantize_pages(
+        ctypes.byref(g), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)), _ptr(src_slots),
+        _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)), _ptr(dst_slots),
+        int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, global_scale,
+                           src_slots=None, dst_slots=None, stream=None) -> None:
+    """Decode ``num_pages`` packed pages of ``packed_pool`` into ``hot_pool``."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    _check(lib.kvfp4_dequantize_pages(
+        ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        _ptr(src_slots), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
+        _ptr(dst_slots), int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_decode_workspace_bytes(geometry, batch: int, num_q_heads: int, v_dim: int,
+                                 max_seq_len_hint: int) -> int:
+    return int(load_library().kvfp4_decode_workspace_bytes(
+        ctypes.byref(Geometry.of(geometry)), int(batch), int(num_q_heads), int(v_dim),
+        int(max_seq_len_hint)))
+
+
+def kvfp4_paged_decode_attention(geometry, packed_pool, global_scale, q, block_table, seq_lens,
+                                 max_seq_len_hint: int, softmax_scale: float, out, lse=None,
+                                 workspace=None, v_dim: Optional[int] = None,
+                                 stream=None) -> None:
+    """Decode attention over the packed cache; writes ``out`` (bf16 bits or
+    bf16 tensor ``[B, Hq, v_dim]``) and, if given, ``lse`` (fp32 ``[B, Hq]``)."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    vd = int(v_dim if v_dim is not None else out.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.kvfp4_paged_decode_attention(
+        ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        _scales(global_scale, g.num_kv_tensors), _ptr(q), B, Hq, vd, _ptr(block_table),
+        int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len_hint), float(softmax_scale),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

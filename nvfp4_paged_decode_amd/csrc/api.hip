@@ -1,0 +1,249 @@
+// C ABI of libkvfp4: argument validation and dispatch.  Declarations and
+// the contract (layouts, ownership, errors) are in include/kvfp4.h.
+#include <float.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+
+#include "common.hpp"
+#include "kvfp4.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_msg[0] = '\0';
+  return KVFP4_OK;
+}
+
+bool geometry_valid(const kvfp4_geometry* g) {
+  if (!g) return false;
+  if (g->num_kv_tensors != 1 && g->num_kv_tensors != 2) return false;
+  if (g->page_size <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0) return false;
+  if (g->head_dim % 16 != 0) return false;
+  long long e = (long long)g->num_kv_tensors * g->page_size * g->num_kv_heads * g->head_dim;
+  return e <= (1LL << 30);
+}
+
+int32_t check_geometry(const kvfp4_geometry* g) {
+  if (!g) return fail(KVFP4_ERR_INVALID_ARG, "geometry is NULL");
+  if (!geometry_valid(g))
+    return fail(KVFP4_ERR_INVALID_ARG,
+                "invalid geometry (num_kv_tensors=%d page_size=%d num_kv_heads=%d head_dim=%d): "
+                "need num_kv_tensors in {1,2}, positive sizes, head_dim %% 16 == 0",
+                g->num_kv_tensors, g->page_size, g->num_kv_heads, g->head_dim);
+  return KVFP4_OK;
+}
+
+int32_t check_scales(const kvfp4_geometry* g, const float* gs) {
+  if (!gs) return fail(KVFP4_ERR_INVALID_ARG, "global_scale is NULL");
+  for (int t = 0; t < g->num_kv_tensors; ++t) {
+    float v = gs[t];
+    if (!(v > 0.0f) || !isfinite(v) || (double)v * 2688.0 > (double)FLT_MAX)
+      return fail(KVFP4_ERR_INVALID_ARG,
+                  "global_scale[%d] = %g: must be finite, > 0 and <= FLT_MAX / 2688", t, (double)v);
+  }
+  return KVFP4_OK;
+}
+
+kvfp4::Geom to_geom(const kvfp4_geometry* g) {
+  return kvfp4::Geom{g->num_kv_tensors, g->page_size, g->num_kv_heads, g->head_dim};
+}
+
+std::atomic<int> g_cus[64];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int c = g_cus[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int32_t check_codec(const kvfp4_geometry* g, const void* from, int32_t from_pages,
+                    const int32_t* src, const void* to, int32_t to_pages, const int32_t* dst,
+                    int32_t num_pages, const float* gs, const char* from_name,
+                    const char* to_name) {
+  int32_t st = check_geometry(g);
+  if (st) return st;
+  if (num_pages < 0) return fail(KVFP4_ERR_INVALID_ARG, "num_pages = %d < 0", num_pages);
+  if (from_pages < 0 || to_pages < 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "pool page counts must be >= 0 (%d, %d)", from_pages,
+                to_pages);
+  if (num_pages == 0) return KVFP4_OK;
+  if (!from) return fail(KVFP4_ERR_INVALID_ARG, "%s is NULL", from_name);
+  if (!to) return fail(KVFP4_ERR_INVALID_ARG, "%s is NULL", to_name);
+  if (from == to) return fail(KVFP4_ERR_INVALID_ARG, "%s and %s alias", from_name, to_name);
+  if (!src && num_pages > from_pages)
+    return fail(KVFP4_ERR_INVALID_ARG, "num_pages %d > %s pages %d with identity slots",
+                num_pages, from_name, from_pages);
+  if (!dst && num_pages > to_pages)
+    return fail(KVFP4_ERR_INVALID_ARG, "num_pages %d > %s pages %d with identity slots",
+                num_pages, to_name, to_pages);
+  return check_scales(g, gs);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvfp4_hot_page_bytes(const kvfp4_geometry* g) {
+  if (!geometry_valid(g)) return 0;
+  return (size_t)to_geom(g).hot_bytes();
+}
+
+size_t kvfp4_packed_page_bytes(const kvfp4_geometry* g) {
+  if (!geometry_valid(g)) return 0;
+  return (size_t)to_geom(g).packed_bytes();
+}
+
+int32_t kvfp4_quantize_pages(const kvfp4_geometry* g, const void* hot_pool,
+                             int32_t hot_pool_pages, const int32_t* src_slots, void* packed_pool,
+                             int32_t packed_pool_pages, const int32_t* dst_slots,
+                             int32_t num_pages, const float* global_scale, void* stream) {
+  int32_t st = check_codec(g, hot_pool, hot_pool_pages, src_slots, packed_pool,
+                           packed_pool_pages, dst_slots, num_pages, global_scale, "hot_pool",
+                           "packed_pool");
+  if (st) return st;
+  if (num_pages == 0) return ok();
+  hipError_t e = kvfp4::launch_quantize(to_geom(g), hot_pool, hot_pool_pages, src_slots,
+                                        packed_pool, packed_pool_pages, dst_slots, num_pages,
+                                        global_scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
+                               int32_t packed_pool_pages, const int32_t* src_slots,
+                               void* hot_pool, int32_t hot_pool_pages, const int32_t* dst_slots,
+                               int32_t num_pages, const float* global_scale, void* stream) {
+  int32_t st = check_codec(g, packed_pool, packed_pool_pages, src_slots, hot_pool,
+                           hot_pool_pages, dst_slots, num_pages, global_scale, "packed_pool",
+                           "hot_pool");
+  if (st) return st;
+  if (num_pages == 0) return ok();
+  hipError_t e = kvfp4::launch_dequantize(to_geom(g), packed_pool, packed_pool_pages, src_slots,
+                                          hot_pool, hot_pool_pages, dst_slots, num_pages,
+                                          global_scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "dequantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static int32_t check_decode_shape(const kvfp4_geometry* g, int32_t batch, int32_t num_q_heads,
+                                  int32_t v_dim, int32_t max_seq_len_hint) {
+  int32_t st = check_geometry(g);
+  if (st) return st;
+  if (batch < 0) return fail(KVFP4_ERR_INVALID_ARG, "batch = %d < 0", batch);
+  if (num_q_heads <= 0 || num_q_heads % g->num_kv_heads != 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "num_q_heads = %d must be a positive multiple of %d",
+                num_q_heads, g->num_kv_heads);
+  if (v_dim <= 0 || v_dim > g->head_dim)
+    return fail(KVFP4_ERR_INVALID_ARG, "v_dim = %d must be in [1, head_dim=%d]", v_dim,
+                g->head_dim);
+  if (g->num_kv_tensors == 2 && v_dim != g->head_dim)
+    return fail(KVFP4_ERR_INVALID_ARG, "v_dim = %d must equal head_dim with separate K and V",
+                v_dim);
+  if (max_seq_len_hint < 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "max_seq_len_hint = %d < 0", max_seq_len_hint);
+  if (g->head_dim > 576)
+    return fail(KVFP4_ERR_UNSUPPORTED, "head_dim %d > 576 has no decode kernel", g->head_dim);
+  return KVFP4_OK;
+}
+
+size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch, int32_t num_q_heads,
+                                    int32_t v_dim, int32_t max_seq_len_hint) {
+  if (check_decode_shape(g, batch, num_q_heads, v_dim, max_seq_len_hint)) return 0;
+  return kvfp4::plan_decode(to_geom(g), batch, num_q_heads, v_dim, max_seq_len_hint,
+                            device_cus())
+      .workspace_bytes;
+}
+
+int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed_pool,
+                                     int32_t packed_pool_pages, const float* global_scale,
+                                     const void* q, int32_t batch, int32_t num_q_heads,
+                                     int32_t v_dim, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                     int32_t max_seq_len_hint, float softmax_scale, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  int32_t st = check_decode_shape(g, batch, num_q_heads, v_dim, max_seq_len_hint);
+  if (st) return st;
+  if (batch == 0) return ok();
+  if (!packed_pool || !q || !block_table || !seq_lens || !out)
+    return fail(KVFP4_ERR_INVALID_ARG,
+                "NULL required pointer (packed_pool=%p q=%p block_table=%p seq_lens=%p out=%p)",
+                packed_pool, q, block_table, seq_lens, out);
+  if (packed_pool_pages <= 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "packed_pool_pages = %d <= 0", packed_pool_pages);
+  if (max_pages_per_seq <= 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "max_pages_per_seq = %d <= 0", max_pages_per_seq);
+  if (!isfinite(softmax_scale))
+    return fail(KVFP4_ERR_INVALID_ARG, "softmax_scale is not finite");
+  st = check_scales(g, global_scale);
+  if (st) return st;
+  kvfp4::Geom geom = to_geom(g);
+  kvfp4::DecodePlan plan =
+      kvfp4::plan_decode(geom, batch, num_q_heads, v_dim, max_seq_len_hint, device_cus());
+  if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
+    return fail(KVFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                plan.workspace_bytes);
+  kvfp4::DecodeArgs a{};
+  a.g = geom;
+  a.pool = (const uint8_t*)packed_pool;
+  a.pool_pages = packed_pool_pages;
+  a.gs_k = global_scale[0];
+  a.gs_v = g->num_kv_tensors == 2 ? global_scale[1] : global_scale[0];
+  a.q = (const uint16_t*)q;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.v_dim = v_dim;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.softmax_scale = softmax_scale;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.splits = plan.splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * plan.splits * v_dim;
+  hipError_t e = kvfp4::launch_decode(plan, a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* kvfp4_status_string(int32_t status) {
+  switch (status) {
+    case KVFP4_OK: return "ok";
+    case KVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case KVFP4_ERR_UNSUPPORTED: return "unsupported geometry";
+    case KVFP4_ERR_WORKSPACE: return "workspace too small";
+    case KVFP4_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* kvfp4_last_error_message(void) { return g_msg; }
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Shared device helpers and internal launcher declarations for libkvfp4.
+//
+// Everything here is gfx950 (CDNA4) code: wave64, 64 KiB LDS per workgroup,
+// MFMA / packed-16-bit VALU.  Host-visible entry points live in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvfp4 {
+
+constexpr int kBlock = 16;  // values per NVFP4 block (one E4M3 scale each)
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Page geometry as the kernels see it.
+struct Geom {
+  int nt;  // KV tensors per page (2: K,V; 1: MLA latent)
+  int T;   // tokens per page
+  int H;   // KV heads
+  int D;   // head dim (multiple of 16)
+  __host__ __device__ long long elems() const { return (long long)nt * T * H * D; }
+  __host__ __device__ long long hot_bytes() const { return 2 * elems(); }
+  __host__ __device__ long long data_bytes() const { return elems() / 2; }
+  __host__ __device__ long long scale_bytes() const { return elems() / kBlock; }
+  __host__ __device__ long long packed_bytes() const { return data_bytes() + scale_bytes(); }
+  __host__ __device__ int blocks_per_tensor() const { return T * H * (D / kBlock); }
+};
+
+// ---------------------------------------------------------------------------
+// Directed rounding of a non-negative fp64 value to a bf16 bit pattern.
+// Used to turn exact fp64 rounding thresholds into integer thresholds on
+// bf16 bit patterns (for non-negative floats, bit patterns order like the
+// values they encode).
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t bf16_bits_directed(double x, bool up) {
+  if (!(x > 0.0)) return 0u;
+  int E;
+  (void)frexp(x, &E);               // x = f * 2^E, f in [0.5, 1)
+  int e = E - 1;                    // floor(log2 x)
+  if (e < -126) e = -126;           // bf16 subnormals share the 2^-126 spacing base
+  if (e > 200) return up ? 0x7F80u : 0x7F7Fu;
+  double y = ldexp(x, 7 - e);       // exact: x / 2^(e-7), in [0, 256)
+  double k = up ? ceil(y) : floor(y);
+  long long bits = ((long long)(e + 126) << 7) + (long long)k;
+  if (up) return bits > 0x7F80 ? 0x7F80u : (uint32_t)bits;
+  return bits > 0x7F7F ? 0x7F7Fu : (uint32_t)bits;
+}
+
+// Threshold t on bf16 magnitude bits v such that  v > t  <=>  value > M
+// (strict) or value >= M (non-strict), for an exact fp64 M > 0.
+__device__ inline uint32_t gt_threshold(double M, bool strict) {
+  return strict ? bf16_bits_directed(M, false) : bf16_bits_directed(M, true) - 1u;
+}
+
+// OCP E4M3FN value of a scale byte (NaN for 0x7F / 0xFF), as fp32 (exact).
+__device__ inline float e4m3_to_float(uint32_t code) {
+  uint32_t e = (code >> 3) & 0xF, m = code & 7;
+  float v;
+  if (e == 0) {
+    v = (float)m * 0x1p-9f;
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  if ((code & 0x7F) == 0x7F) v = __uint_as_float(0x7FC00000u);
+  return (code & 0x80) ? -v : v;
+}
+
+// fp32 value of an E2M1 magnitude code 0..7: {0, .5, 1, 1.5, 2, 3, 4, 6}.
+__device__ inline float e2m1_mag_to_float(uint32_t m) {
+  uint32_t bits = (m << 22) + (126u << 23);
+  bits = m >= 2 ? bits : (m == 1 ? 0x3F000000u : 0u);
+  return __uint_as_float(bits);
+}
+
+// bf16 bits of a finite fp64 value, rounded to nearest even once (used by
+// the dequantizer when the tensor scale is so small that fp32 products
+// would leave the normal range).
+__device__ inline uint32_t bf16_rne_from_f64(double v) {
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  uint32_t sign = (uint32_t)(b >> 63) << 15;
+  int ex = (int)((b >> 52) & 0x7FF);
+  if (ex == 0) return sign;  // zero (fp64 subnormals cannot occur here)
+  uint64_t m53 = (b & ((1ull << 52) - 1)) | (1ull << 52);
+  int e = ex - 1023;
+  int shift = 45;                     // keep 8 significant bits
+  uint32_t base;
+  if (e >= -126) {
+    base = (uint32_t)(e + 127) << 7;  // exponent field; the kept value adds
+    // m53 >> 45 is in [128, 256): subtract the implicit bit via base
+    base -= 128;
+  } else {
+    shift += (-126 - e);              // bf16 subnormal: fewer kept bits
+    base = 0;
+  }
+  if (shift > 60) return sign;        // below half the smallest subnormal
+  uint64_t keep = m53 >> shift;
+  uint64_t rem = m53 & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  keep += (rem > half || (rem == half && (keep & 1))) ? 1 : 0;
+  uint32_t bits = base + (uint32_t)keep;
+  if (bits >= 0x7F80u) bits = 0x7F80u;  // overflow to inf
+  return sign | bits;
+}
+
+// ---------------------------------------------------------------------------
+// Internal launchers (host side).  All validate nothing: the C ABI did.
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const Geom& g, const void* hot, int hot_pages, const int32_t* src,
+                           void* packed, int packed_pages, const int32_t* dst, int num_pages,
+                           const float* gs, hipStream_t stream);
+hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages,
+                             const int32_t* src, void* hot, int hot_pages, const int32_t* dst,
+                             int num_pages, const float* gs, hipStream_t stream);
+
+struct DecodeArgs {
+  Geom g;
+  const uint8_t* pool;
+  int pool_pages;
+  float gs_k, gs_v;
+  const uint16_t* q;
+  int batch, hq, v_dim;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  float softmax_scale;
+  uint16_t* out;
+  float* lse;
+  // split-K plan
+  int splits;            // token splits per sequence
+  int pages_per_split;   // pages each split covers
+  float* ws_o;           // [batch][hq][splits][v_dim]
+  float* ws_ml;          // [batch][hq][splits][2]  (max, sum) in log2 units
+};
+
+// Which decode kernel a shape uses, and how it splits the context.
+struct DecodePlan {
+  int kernel;            // 0 = generic, 1 = GQA VALU, 2 = MLA MFMA
+  int splits;
+  int pages_per_split;
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_len_hint,
+                       int num_cus);
+hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvfp4

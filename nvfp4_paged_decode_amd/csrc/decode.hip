@@ -1,0 +1,247 @@
+// Paged NVFP4 decode attention: split-K plan, the generic kernel, and the
+// cross-workgroup merge.
+//
+// "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+// Path 3: Decode and NVFP4 KV Decode Attention Kernel Implementation /
+// Figure 3: the kernel reads packed NVFP4 K/V and their E4M3 block scales,
+// dequantizes in registers, and applies the per-tensor K and V scales as
+// scalars on the two products (here: gs_K is folded into the softmax scale,
+// gs_V multiplies the merged output).  No standalone dequantization pass.
+//
+// Split-K.  A sequence's pages are cut into `splits` contiguous ranges of
+// `pages_per_split` pages; each (sequence, split) workgroup writes an
+// unnormalized partial (o, m, l) with scores in log2 units, and
+// merge_kernel combines them: M = max m_s, L = sum l_s 2^(m_s - M),
+// out = gs_V * sum o_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.
+#include "common.hpp"
+
+namespace kvfp4 {
+
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream);
+bool gqa_supported(const Geom& g, int hq, int v_dim);
+bool mla_supported(const Geom& g, int hq, int v_dim);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kGenThreads = 256;
+constexpr int kGenHeads = 16;   // query heads per workgroup
+constexpr int kGenTile = 8;     // tokens per LDS tile
+constexpr int kMaxD = 576;
+
+// Dequantized value c * sb of element d of a packed row (exact in fp32).
+__device__ inline float packed_elem(const uint8_t* data_row, const uint8_t* scale_row, int d) {
+  uint32_t byte = data_row[d >> 1];
+  uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xF);
+  float v = e2m1_mag_to_float(nib & 7) * e4m3_to_float(scale_row[d >> 4]);
+  return (nib & 8) ? -v : v;
+}
+
+// Generic decode: one workgroup per (split, kv head x 16-query-head chunk,
+// sequence).  Thread (qh = tid / 16, r = tid % 16) keeps query head qh's
+// elements r, r+16, ... in registers and the matching accumulator slice.
+// Correct for every supported geometry (D <= 576); the shape-specialised
+// kernels are the fast paths.
+__global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs a) {
+  const Geom g = a.g;
+  const int split = blockIdx.x;
+  const int b = blockIdx.z;
+  const int G = a.hq / g.H;
+  const int nqc = (G + kGenHeads - 1) / kGenHeads;
+  const int h = blockIdx.y / nqc;
+  const int qc = blockIdx.y % nqc;
+  const int tid = threadIdx.x;
+  const int qh = tid >> 4, r = tid & 15;
+  const int head = h * G + qc * kGenHeads + qh;  // query head of this thread
+  const bool active = (qc * kGenHeads + qh) < G;
+
+  __shared__ float ks[kGenTile][kMaxD + 1];
+  __shared__ float vs[kGenTile][kMaxD + 1];
+
+  const int D = g.D, Dv = a.v_dim;
+  const int nd = (D + 15) / 16, nv = (Dv + 15) / 16;
+  float qreg[kMaxD / 16];
+  float acc[kMaxD / 16];
+  const float qscale = a.softmax_scale * a.gs_k * kLog2e;
+#pragma unroll
+  for (int i = 0; i < kMaxD / 16; ++i) {
+    int d = r + 16 * i;
+    float v = 0.f;
+    if (active && i < nd && d < D)
+      v = __uint_as_float((uint32_t)a.q[((long long)b * a.hq + head) * D + d] << 16);
+    qreg[i] = v * qscale;
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  int L = a.seq_lens[b];
+  const int cap = a.max_pages * g.T;
+  if (L > cap) L = cap;
+  if (L < 0) L = 0;
+  const int t_begin = split * a.pages_per_split * g.T;
+  int t_end = t_begin + a.pages_per_split * g.T;
+  if (t_end > L) t_end = L;
+
+  const long long page_bytes = g.packed_bytes();
+  const long long row_data = D / 2, row_scale = D / 16;
+  for (int t0 = t_begin; t0 < t_end; t0 += kGenTile) {
+    // dequantize the tile: K (tensor 0) and V (tensor 1, or the latent prefix)
+    __syncthreads();
+    for (int e = tid; e < kGenTile * D; e += kGenThreads) {
+      int tt = e / D, d = e - tt * D;
+      int tok = t0 + tt;
+      float kv = 0.f, vv = 0.f;
+      if (tok < t_end) {
+        int slot = a.block_table[(long long)b * a.max_pages + tok / g.T];
+        if (slot >= 0 && slot < a.pool_pages) {
+          int row = tok % g.T;
+          const uint8_t* page = a.pool + (long long)slot * page_bytes;
+          long long r0 = (long long)row * g.H + h;  // row index within tensor 0
+          kv = packed_elem(page + r0 * row_data, page + g.data_bytes() + r0 * row_scale, d);
+          if (g.nt == 2) {
+            long long r1 = (long long)(g.T + row) * g.H + h;  // tensor 1
+            if (d < Dv)
+              vv = packed_elem(page + r1 * row_data, page + g.data_bytes() + r1 * row_scale, d);
+          } else {
+            vv = kv;
+          }
+        }
+      }
+      ks[tt][d] = kv;
+      vs[tt][d] = vv;
+    }
+    __syncthreads();
+    float s[kGenTile];
+#pragma unroll
+    for (int tt = 0; tt < kGenTile; ++tt) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxD / 16; ++i)
+        if (i < nd && r + 16 * i < D) p += qreg[i] * ks[tt][r + 16 * i];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) p += __shfl_xor(p, off, 16);
+      s[tt] = (t0 + tt < t_end) ? p : -INFINITY;
+    }
+    float mt = m;
+#pragma unroll
+    for (int tt = 0; tt < kGenTile; ++tt) mt = fmaxf(mt, s[tt]);
+    float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mt);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < kMaxD / 16; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int tt = 0; tt < kGenTile; ++tt) {
+      float p = (s[tt] == -INFINITY) ? 0.f : exp2f(s[tt] - mt);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < kMaxD / 16; ++i)
+        if (i < nv && r + 16 * i < Dv) acc[i] += p * vs[tt][r + 16 * i];
+    }
+    m = mt;
+  }
+  if (!active) return;
+  long long base = (((long long)b * a.hq + head) * a.splits + split);
+#pragma unroll
+  for (int i = 0; i < kMaxD / 16; ++i) {
+    int d = r + 16 * i;
+    if (i < nv && d < Dv) a.ws_o[base * Dv + d] = acc[i];
+  }
+  if (r == 0) {
+    a.ws_ml[base * 2] = m;
+    a.ws_ml[base * 2 + 1] = l;
+  }
+}
+
+constexpr int kMergeThreads = 128;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y;
+  const long long base = ((long long)b * a.hq + head) * a.splits;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.ws_ml[(base + s) * 2]);
+  float Lsum = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    float ms = a.ws_ml[(base + s) * 2];
+    if (ms != -INFINITY) Lsum += a.ws_ml[(base + s) * 2 + 1] * exp2f(ms - M);
+  }
+  const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
+  for (int d = threadIdx.x; d < a.v_dim; d += kMergeThreads) {
+    float o = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      float ms = a.ws_ml[(base + s) * 2];
+      if (ms != -INFINITY) o += a.ws_o[(base + s) * a.v_dim + d] * exp2f(ms - M);
+    }
+    o *= inv;
+    uint32_t u = __float_as_uint(o);
+    uint32_t bf = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    a.out[((long long)b * a.hq + head) * a.v_dim + d] = (uint16_t)bf;
+  }
+  if (threadIdx.x == 0 && a.lse) {
+    float v = (Lsum > 0.f) ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
+    a.lse[(long long)b * a.hq + head] = v;
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_len_hint,
+                       int num_cus) {
+  DecodePlan p{};
+  int hint = max_seq_len_hint > 0 ? max_seq_len_hint : 1;
+  int pages_max = (hint + g.T - 1) / g.T;
+  long long items;
+  if (mla_supported(g, hq, v_dim)) {
+    p.kernel = 2;
+    items = batch;
+  } else if (gqa_supported(g, hq, v_dim)) {
+    p.kernel = 1;
+    items = batch;
+  } else {
+    p.kernel = 0;
+    int G = hq / g.H;
+    items = (long long)batch * g.H * ((G + kGenHeads - 1) / kGenHeads);
+  }
+  if (batch <= 0 || items <= 0) {
+    p.splits = 1;
+    p.pages_per_split = pages_max;
+    p.workspace_bytes = 0;
+    return p;
+  }
+  long long want = 2LL * (num_cus > 0 ? num_cus : 256);
+  long long s = (want + items - 1) / items;
+  if (s < 1) s = 1;
+  if (s > pages_max) s = pages_max;
+  p.pages_per_split = (int)((pages_max + s - 1) / s);
+  p.splits = (pages_max + p.pages_per_split - 1) / p.pages_per_split;
+  p.workspace_bytes = (size_t)batch * hq * p.splits * (size_t)(v_dim + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  hipError_t e;
+  if (plan.kernel == 2) {
+    e = launch_decode_mla(a, stream);
+  } else if (plan.kernel == 1) {
+    e = launch_decode_gqa(a, stream);
+  } else {
+    int G = a.hq / a.g.H;
+    int nqc = (G + kGenHeads - 1) / kGenHeads;
+    hipLaunchKernelGGL(decode_generic_kernel, dim3(a.splits, a.g.H * nqc, a.batch),
+                       dim3(kGenThreads), 0, stream, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Shape-specialised fast paths are compiled in their own files; until a
+// shape has one, it runs on the generic kernel.
+bool gqa_supported(const Geom&, int, int) { return false; }
+bool mla_supported(const Geom&, int, int) { return false; }
+hipError_t launch_decode_gqa(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_mla(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
+
+}  // namespace kvfp4

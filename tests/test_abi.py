@@ -1,0 +1,145 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/kvfp4.h declares, and rejects invalid arguments before launching
+anything (no GPU needed; no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_paged_decode_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "kvfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvfp4_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.library_path()):
+        pytest.fail("libkvfp4.so is not built (python -m nvfp4_paged_decode_amd.build)")
+    return K.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    declared = _header_functions()
+    assert declared == sorted(K.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_page_sizes(lib):
+    g = K.Geometry(2, 64, 8, 128)
+    assert lib.kvfp4_hot_page_bytes(ctypes.byref(g)) == 262144
+    assert lib.kvfp4_packed_page_bytes(ctypes.byref(g)) == 73728
+    mla = K.Geometry(1, 64, 1, 576)
+    assert lib.kvfp4_packed_page_bytes(ctypes.byref(mla)) == 64 * 576 * 9 // 16
+    for bad in [(3, 64, 8, 128), (2, 64, 8, 120), (2, 0, 8, 128), (2, 64, -1, 128)]:
+        assert lib.kvfp4_packed_page_bytes(ctypes.byref(K.Geometry(*bad))) == 0
+    assert lib.kvfp4_hot_page_bytes(None) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _q(lib, g, num_pages=4, gs=(1.0, 1.0), hot=FAKE, packed=FAKE, hot_pages=8, packed_pages=8):
+    arr = (ctypes.c_float * 2)(*gs)
+    return lib.kvfp4_quantize_pages(ctypes.byref(g) if g is not None else None, hot, hot_pages,
+                                    None, packed, packed_pages, None, num_pages, arr, None)
+
+
+@pytest.mark.parametrize("case", [
+    dict(g=None),
+    dict(g=K.Geometry(2, 64, 8, 100)),
+    dict(g=K.Geometry(0, 64, 8, 128)),
+    dict(num_pages=-1),
+    dict(hot=None),
+    dict(packed=None),
+    dict(hot=FAKE, packed=FAKE),  # aliasing pools
+    dict(num_pages=9),            # more pages than the pool with identity slots
+    dict(gs=(0.0, 1.0)),
+    dict(gs=(1.0, -2.0)),
+    dict(gs=(float("nan"), 1.0)),
+    dict(gs=(float("inf"), 1.0)),
+    dict(gs=(1e36, 1.0)),         # 2688 * gs overflows fp32
+])
+def test_codec_rejects_invalid_arguments(lib, case):
+    g = case.pop("g", K.Geometry(2, 64, 8, 128))
+    if case.get("hot") == FAKE and case.get("packed") == FAKE:
+        st = _q(lib, g, **case)
+    else:
+        case.setdefault("packed", FAKE + 0x100)
+        st = _q(lib, g, **case)
+    assert st == K.KVFP4_ERR_INVALID_ARG
+    assert lib.kvfp4_last_error_message().decode() != ""
+    # the same validation guards the dequantizer
+    arr = (ctypes.c_float * 2)(*case.get("gs", (1.0, 1.0)))
+    st2 = lib.kvfp4_dequantize_pages(ctypes.byref(g) if g is not None else None,
+                                     case.get("packed", FAKE + 0x100), 8, None,
+                                     case.get("hot", FAKE), 8, None, case.get("num_pages", 4),
+                                     arr, None)
+    assert st2 == K.KVFP4_ERR_INVALID_ARG
+
+
+def test_codec_zero_pages_is_a_noop(lib):
+    g = K.Geometry(2, 64, 8, 128)
+    arr = (ctypes.c_float * 2)(1.0, 1.0)
+    assert lib.kvfp4_quantize_pages(ctypes.byref(g), None, 0, None, None, 0, None, 0, arr,
+                                    None) == K.KVFP4_OK
+
+
+def _decode(lib, g, gs=(1.0, 1.0), batch=2, hq=32, v_dim=128, hint=1024, ws=0, wsptr=None,
+            pool=FAKE, q=FAKE, bt=FAKE, sl=FAKE, out=FAKE, scale=0.088, max_pages=16,
+            pool_pages=64):
+    arr = (ctypes.c_float * 2)(*gs)
+    return lib.kvfp4_paged_decode_attention(
+        ctypes.byref(g) if g is not None else None, pool, pool_pages, arr, q, batch, hq, v_dim,
+        bt, max_pages, sl, hint, ctypes.c_float(scale), out, None, wsptr, ws, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(g=None), K.KVFP4_ERR_INVALID_ARG),
+    (dict(hq=30), K.KVFP4_ERR_INVALID_ARG),      # not a multiple of 8 KV heads
+    (dict(v_dim=64), K.KVFP4_ERR_INVALID_ARG),   # K and V need v_dim == head_dim
+    (dict(v_dim=0), K.KVFP4_ERR_INVALID_ARG),
+    (dict(batch=-1), K.KVFP4_ERR_INVALID_ARG),
+    (dict(hint=-5), K.KVFP4_ERR_INVALID_ARG),
+    (dict(q=None), K.KVFP4_ERR_INVALID_ARG),
+    (dict(bt=None), K.KVFP4_ERR_INVALID_ARG),
+    (dict(out=None), K.KVFP4_ERR_INVALID_ARG),
+    (dict(max_pages=0), K.KVFP4_ERR_INVALID_ARG),
+    (dict(pool_pages=0), K.KVFP4_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), K.KVFP4_ERR_INVALID_ARG),
+    (dict(gs=(1.0, 0.0)), K.KVFP4_ERR_INVALID_ARG),
+    (dict(ws=0), K.KVFP4_ERR_WORKSPACE),          # workspace too small
+    (dict(g=K.Geometry(2, 64, 8, 640), v_dim=640), K.KVFP4_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_invalid_arguments(lib, case, code):
+    g = case.pop("g", K.Geometry(2, 64, 8, 128))
+    assert _decode(lib, g, **case) == code
+    assert lib.kvfp4_last_error_message().decode() != ""
+
+
+def test_decode_workspace_size(lib):
+    g = K.Geometry(2, 64, 8, 128)
+    n = lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 32, 32, 128, 8192)
+    assert n > 0 and n % (32 * 32 * 130 * 4) == 0
+    assert lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 32, 30, 128, 8192) == 0
+    assert lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 0, 32, 128, 8192) == 0
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert lib.kvfp4_status_string(s).decode()
+
+
+def test_python_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(K, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(K, "_lib", None)
+    with pytest.raises(ImportError):
+        K.load_library()

@@ -1,0 +1,133 @@
+"""GPU parity of paged NVFP4 decode attention against the fp64 oracle:
+every output within 1e-2 + 1e-2 |ref|, lse within 1e-3 + 1e-3 |ref|."""
+
+import numpy as np
+import pytest
+
+import nvfp4_paged_decode_amd as K
+from nvfp4_paged_decode_amd import workloads as W
+from oracle import nvfp4 as O
+from tests.gpu_common import (assert_attention_close, dev, host, oracle_attention,
+                              oracle_packed_pages, poison_unread, require_gpu, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_decode(wl, packed_d, gs, hint=None, seq_lens=None):
+    B, Hq = wl.batch, wl.num_q_heads
+    hint = int(wl.seq_lens.max()) if hint is None else hint
+    ws_bytes = K.kvfp4_decode_workspace_bytes(wl.geometry, B, Hq, wl.v_dim, hint)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, wl.v_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    sl = wl.seq_lens if seq_lens is None else seq_lens
+    K.kvfp4_paged_decode_attention(wl.geometry, packed_d, gs, dev(wl.q.view(np.int16)),
+                                   dev(wl.block_table), dev(sl.astype(np.int32)), hint,
+                                   wl.softmax_scale, out, lse, ws, v_dim=wl.v_dim)
+    return host(out).view(np.uint16), host(lse)
+
+
+def oracle_pool(wl, gs, poison_seed=0):
+    packed = oracle_packed_pages(wl.hot_pool, wl.geometry, gs, np.arange(wl.num_slots))
+    poison_unread(packed, wl, np.random.default_rng(poison_seed))
+    return packed
+
+
+def check(wl, gs, packed, out, lse, batch_indices=None, head_indices=None, what=""):
+    ref, ref_lse = oracle_attention(packed, wl, gs, batch_indices, head_indices)
+    bi = slice(None) if batch_indices is None else np.asarray(batch_indices)
+    o = out[bi]
+    l = lse[bi]
+    if head_indices is not None:
+        o = o[:, np.asarray(head_indices)]
+        l = l[:, np.asarray(head_indices)]
+    assert_attention_close(o, ref, what)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(l)), f"{what}: lse finiteness"
+    assert np.all(np.abs(l[fin] - ref_lse[fin]) <= 1e-3 + 1e-3 * np.abs(ref_lse[fin])), what
+
+
+SMALL = {
+    "tiny": lambda: W.tiny(),
+    "llama3_ragged": lambda: W.llama3_8b(seed=12, batch=3, context=300),
+    "qwen3_ragged": lambda: W.qwen3_8b_long(seed=13, batch=3, lo=1, hi=700),
+    "mla_ragged": lambda: W.mla(seed=15, batch=2, context=200),
+    "mla_16_heads": lambda: W.mla(seed=16, batch=3, context=130, num_q_heads=16),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("gs_kind", ["unit", "calibrated"])
+def test_decode_small_all_outputs(name, gs_kind):
+    require_gpu()
+    wl = SMALL[name]()
+    gs = wl.gs_unit if gs_kind == "unit" else wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=f"{name}/{gs_kind}")
+
+
+def test_decode_edge_lengths():
+    """Empty sequences, one token, exact page multiples and a page-table row
+    used to the last entry, in one batch."""
+    require_gpu()
+    wl = W.llama3_8b(seed=17, batch=6, context=256)
+    wl.seq_lens[:] = [0, 1, 64, 256, 63, 65]
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs, hint=256)
+    check(wl, gs, packed, out, lse, what="edge lengths")
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+
+
+def test_decode_hint_larger_than_lengths():
+    require_gpu()
+    wl = W.qwen3_8b_long(seed=18, batch=2, lo=50, hi=300)
+    gs = wl.gs_unit
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs, hint=int(wl.max_pages_per_seq * wl.page_size))
+    check(wl, gs, packed, out, lse, what="large hint")
+
+
+FULL = {
+    "llama3_8b": (lambda: W.llama3_8b(), [0, 13, 31]),
+    "qwen3_8b_long": (lambda: W.qwen3_8b_long(), None),  # longest and shortest sequence
+    "mla": (lambda: W.mla(), [0, 37, 63]),
+}
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "qwen3_8b_long", "mla"])
+def test_decode_full_size_sampled(name):
+    """Full-size workloads in the bench's launch configuration.  The pool is
+    encoded on the GPU; the sampled sequences' pages are then overwritten
+    with oracle-encoded bytes, so every compared output depends on oracle
+    inputs only."""
+    require_gpu()
+    wl = FULL[name][0]()
+    gs = wl.gs_calibrated
+    if name == "qwen3_8b_long":
+        sample = [int(np.argmax(wl.seq_lens)), int(np.argmin(wl.seq_lens))]
+    else:
+        sample = FULL[name][1]
+    g = O.Geometry(*wl.geometry)
+    hot_d = dev(wl.hot_pool.view(np.int16))
+    packed_d = torch.empty((wl.num_slots, O.packed_page_bytes(g)), dtype=torch.uint8,
+                           device="cuda")
+    K.kvfp4_quantize_pages(wl.geometry, hot_d, packed_d, wl.num_slots, gs)
+    del hot_d
+    T = wl.page_size
+    slots = sorted({int(s) for b in sample
+                    for s in wl.block_table[b, :-(-int(wl.seq_lens[b]) // T)]})
+    ref_pages = oracle_packed_pages(wl.hot_pool, wl.geometry, gs, slots)
+    host_pool = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
+    host_pool[slots] = ref_pages
+    spare = np.setdiff1d(np.arange(wl.num_slots), wl.used_slots)
+    poison_unread(host_pool, wl, np.random.default_rng(3))  # tails + spare slots
+    touched = np.union1d(np.asarray(slots), spare)
+    packed_d[torch.from_numpy(touched).cuda()] = dev(host_pool[touched])
+    out, lse = gpu_decode(wl, packed_d, gs)
+    check(wl, gs, host_pool, out, lse, batch_indices=sample,
+          head_indices=None, what=f"{name} full size")
+    # every output of the whole batch is finite and the merge produced an lse
+    allo = (out.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isfinite(allo)) and np.all(np.isfinite(lse))
