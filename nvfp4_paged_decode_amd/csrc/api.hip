@@ -226,8 +226,11 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
   a.lse = lse;
   a.splits = plan.splits;
   a.pages_per_split = plan.pages_per_split;
+  a.nwg = plan.nwg;
+  size_t partials = plan.kernel == 0 ? (size_t)batch * num_q_heads * plan.splits
+                                     : (size_t)(plan.nwg + batch) * num_q_heads;
   a.ws_o = (float*)workspace;
-  a.ws_ml = a.ws_o + (size_t)batch * num_q_heads * plan.splits * v_dim;
+  a.ws_ml = a.ws_o + partials * v_dim;
   hipError_t e = kvfp4::launch_decode(plan, a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();

@@ -127,18 +127,22 @@ struct DecodeArgs {
   float softmax_scale;
   uint16_t* out;
   float* lse;
-  // split-K plan
-  int splits;            // token splits per sequence
-  int pages_per_split;   // pages each split covers
-  float* ws_o;           // [batch][hq][splits][v_dim]
-  float* ws_ml;          // [batch][hq][splits][2]  (max, sum) in log2 units
+  // split-K plan.  Generic kernel: `splits` fixed page ranges per sequence,
+  // partials [batch][hq][splits].  Balanced kernels: `nwg` workgroups over
+  // the batch's concatenated pages, partials [nwg + batch][hq].
+  int splits;
+  int pages_per_split;
+  int nwg;
+  float* ws_o;           // partial outputs, v_dim floats each
+  float* ws_ml;          // partial (max, sum), scores in log2 units
 };
 
 // Which decode kernel a shape uses, and how it splits the context.
 struct DecodePlan {
   int kernel;            // 0 = generic, 1 = GQA VALU, 2 = MLA MFMA
-  int splits;
-  int pages_per_split;
+  int splits;            // generic kernel
+  int pages_per_split;   // generic kernel
+  int nwg;               // balanced kernels
   size_t workspace_bytes;
 };
 

@@ -14,6 +14,7 @@
 // merge_kernel combines them: M = max m_s, L = sum l_s 2^(m_s - M),
 // out = gs_V * sum o_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.
 #include "common.hpp"
+#include "decode_plan.hpp"
 
 namespace kvfp4 {
 
@@ -183,6 +184,65 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   }
 }
 
+// Merge for the balanced kernels: sequence b's partials sit in slots
+// w + b for every workgroup w whose page range overlaps b's pages.
+__global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y;
+  __shared__ long long s_tot, s_start;
+  if (threadIdx.x == 0) {
+    long long tot = 0, start = 0;
+    for (int i = 0; i < a.batch; ++i) {
+      int np = pages_of(a, i);
+      if (i < b) start += np;
+      tot += np;
+    }
+    s_tot = tot;
+    s_start = start;
+  }
+  __syncthreads();
+  const long long ptot = s_tot, first = s_start;
+  const long long last = first + pages_of(a, b);
+  const int nwg = a.nwg;
+  float M = -INFINITY, Lsum = 0.f;
+  int w_lo = 0, w_hi = -1;
+  if (last > first) {
+    // first workgroup whose range ends after `first`
+    int w = (int)(first * nwg / ptot);
+    while (w > 0 && range_begin(ptot, w, nwg) > first) --w;
+    while (range_begin(ptot, w + 1, nwg) <= first) ++w;
+    w_lo = w;
+    w_hi = w;
+    while (w_hi + 1 < nwg && range_begin(ptot, w_hi + 1, nwg) < last) ++w_hi;
+    for (int v = w_lo; v <= w_hi; ++v) {
+      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;  // empty range
+      M = fmaxf(M, a.ws_ml[(((long long)v + b) * a.hq + head) * 2]);
+    }
+    for (int v = w_lo; v <= w_hi; ++v) {
+      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
+      float ms = a.ws_ml[(((long long)v + b) * a.hq + head) * 2];
+      if (ms != -INFINITY) Lsum += a.ws_ml[(((long long)v + b) * a.hq + head) * 2 + 1] * exp2f(ms - M);
+    }
+  }
+  const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
+  for (int d = threadIdx.x; d < a.v_dim; d += kMergeThreads) {
+    float o = 0.f;
+    for (int v = w_lo; v <= w_hi; ++v) {
+      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
+      long long slot = ((long long)v + b) * a.hq + head;
+      float ms = a.ws_ml[slot * 2];
+      if (ms != -INFINITY) o += a.ws_o[slot * a.v_dim + d] * exp2f(ms - M);
+    }
+    o *= inv;
+    uint32_t u = __float_as_uint(o);
+    uint32_t bf = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    a.out[((long long)b * a.hq + head) * a.v_dim + d] = (uint16_t)bf;
+  }
+  if (threadIdx.x == 0 && a.lse) {
+    float v = (Lsum > 0.f) ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
+    a.lse[(long long)b * a.hq + head] = v;
+  }
+}
+
 }  // namespace
 
 DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_len_hint,
@@ -190,30 +250,35 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
   DecodePlan p{};
   int hint = max_seq_len_hint > 0 ? max_seq_len_hint : 1;
   int pages_max = (hint + g.T - 1) / g.T;
-  long long items;
-  if (mla_supported(g, hq, v_dim)) {
-    p.kernel = 2;
-    items = batch;
-  } else if (gqa_supported(g, hq, v_dim)) {
-    p.kernel = 1;
-    items = batch;
-  } else {
-    p.kernel = 0;
-    int G = hq / g.H;
-    items = (long long)batch * g.H * ((G + kGenHeads - 1) / kGenHeads);
-  }
-  if (batch <= 0 || items <= 0) {
+  const int cus = num_cus > 0 ? num_cus : 256;
+  if (batch <= 0) {
     p.splits = 1;
     p.pages_per_split = pages_max;
+    p.nwg = 1;
     p.workspace_bytes = 0;
     return p;
   }
-  long long want = 2LL * (num_cus > 0 ? num_cus : 256);
+  if (mla_supported(g, hq, v_dim) || gqa_supported(g, hq, v_dim)) {
+    // balanced kernels: one workgroup per CU (or per page when fewer)
+    p.kernel = mla_supported(g, hq, v_dim) ? 2 : 1;
+    long long pages_ub = (long long)batch * pages_max;
+    long long nwg = cus < pages_ub ? cus : pages_ub;
+    p.nwg = (int)(nwg > 0 ? nwg : 1);
+    p.splits = 0;
+    p.pages_per_split = 0;
+    p.workspace_bytes = (size_t)(p.nwg + batch) * hq * (size_t)(v_dim + 2) * sizeof(float);
+    return p;
+  }
+  p.kernel = 0;
+  int G = hq / g.H;
+  long long items = (long long)batch * g.H * ((G + kGenHeads - 1) / kGenHeads);
+  long long want = 2LL * cus;
   long long s = (want + items - 1) / items;
   if (s < 1) s = 1;
   if (s > pages_max) s = pages_max;
   p.pages_per_split = (int)((pages_max + s - 1) / s);
   p.splits = (pages_max + p.pages_per_split - 1) / p.pages_per_split;
+  p.nwg = 0;
   p.workspace_bytes = (size_t)batch * hq * p.splits * (size_t)(v_dim + 2) * sizeof(float);
   return p;
 }
@@ -233,15 +298,17 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
+  if (plan.kernel == 0) {
+    hipLaunchKernelGGL(merge_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(merge_balanced_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 
-// Shape-specialised fast paths are compiled in their own files; until a
-// shape has one, it runs on the generic kernel.
-bool gqa_supported(const Geom&, int, int) { return false; }
+// Shapes without a specialised kernel run on the generic one.
 bool mla_supported(const Geom&, int, int) { return false; }
-hipError_t launch_decode_gqa(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_mla(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace kvfp4

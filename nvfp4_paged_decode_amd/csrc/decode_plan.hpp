@@ -1,0 +1,85 @@
+// Balanced split-K over the pages of a whole batch (device side).
+//
+// The pages of all sequences, concatenated in batch order, form one list of
+// P pages (sequence b contributes ceil(L_b / T) of them).  Workgroup w of
+// nwg owns pages [floor(w P / nwg), floor((w+1) P / nwg)).  Every range is
+// contiguous and ranges are monotone in w, so the (workgroup, sequence)
+// pairs that overlap are indexed without collision by w + b: this is the
+// partial slot the workgroup writes for that sequence.  Kernels and the
+// merge compute the same ranges from seq_lens with the same integer
+// arithmetic.
+#pragma once
+
+#include "common.hpp"
+
+namespace kvfp4 {
+
+// Cached-token count of sequence b, clamped to what its page-table row holds.
+__device__ inline int clamped_len(const DecodeArgs& a, int b) {
+  int L = a.seq_lens[b];
+  const int cap = a.max_pages * a.g.T;
+  if (L > cap) L = cap;
+  if (L < 0) L = 0;
+  return L;
+}
+
+__device__ inline int pages_of(const DecodeArgs& a, int b) {
+  return (clamped_len(a, b) + a.g.T - 1) / a.g.T;
+}
+
+__device__ inline long long range_begin(long long ptot, int w, int nwg) {
+  return (long long)w * ptot / nwg;
+}
+
+struct BalancedRange {
+  long long ptot;         // pages in the batch
+  long long p_begin;      // this workgroup's pages [p_begin, p_end)
+  long long p_end;
+  int b_first;            // first sequence with pages in the range (batch if none)
+  long long start_first;  // index of its first page in the concatenation
+};
+
+// Wave-level inclusive prefix sum of an int over 64 lanes.
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Computed by every wave on its own (no LDS, no barrier).
+__device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, BalancedRange& r) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    int b = base + lane;
+    int np = b < a.batch ? pages_of(a, b) : 0;
+    tot += __shfl(wave_incl_scan(np), 63);
+  }
+  r.ptot = tot;
+  r.p_begin = range_begin(tot, w, nwg);
+  r.p_end = range_begin(tot, w + 1, nwg);
+  r.b_first = a.batch;
+  r.start_first = tot;
+  if (r.p_begin >= r.p_end) return;
+  long long run = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    int b = base + lane;
+    int np = b < a.batch ? pages_of(a, b) : 0;
+    int incl = wave_incl_scan(np);
+    bool hit = np > 0 && run + incl > r.p_begin;
+    unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
+    if (m) {
+      int l0 = __builtin_ctzll(m);
+      r.b_first = base + l0;
+      r.start_first = run + __shfl(incl - np, l0);
+      return;
+    }
+    run += __shfl(incl, 63);
+  }
+}
+
+}  // namespace kvfp4
