@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true", help="do not evict caches between kernels")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-pages", type=int, default=6)
+    p.add_argument("--no-copy-yardstick", action="store_true",
+                   help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
     return p.parse_args()
 
 
@@ -197,6 +199,26 @@ def main():
                     fn()
         return ev
 
+    copy = None
+    if not args.no_copy_yardstick:
+        # a plain device-to-device copy of 1 GiB: reads 1 GiB and writes 1 GiB
+        src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        times = []
+        for i in range(4):
+            flush.fill_(2)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst_c.copy_(src_c)
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms_c = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
+        copy = {"bytes": 2 << 30, "median_us": round(ms_c * 1e3, 2),
+                "GB/s": round((2 << 30) / (ms_c * 1e-3) / 1e9, 1)}
+        del src_c, dst_c
+
     run(args.warmup, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -260,6 +282,7 @@ def main():
                    "seq_len": int(wl.seq_lens.max()) if wl is not None else None,
                    "parallelism": "single GPU"},
         "kernels": kern,
+        "copy_yardstick": copy,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),

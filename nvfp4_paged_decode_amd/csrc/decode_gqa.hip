@@ -63,13 +63,21 @@ __device__ inline float scale_value(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
 }
 
-__device__ inline float dpp_sum8(float v) {
-  // sum over the 8 lanes of a stream: xor 1, xor 2 (quad_perm), then the
-  // half-row mirror pairs lane i with 7-i
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
-  return v;
+// v[i] += value of v[i] in lane (lane ^ 1), (lane ^ 2), then the half-row
+// mirror (lane i <-> 7 - i): the sum over the 8 lanes of a stream.  Each
+// step runs over all values before the next, so DPP reads never wait on
+// the VALU write just before them.
+template <int N>
+__device__ inline void dpp_sum8(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0xB1, 0xF, 0xF, true));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x4E, 0xF, 0xF, true));
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    v[i] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v[i]), 0x141, 0xF, 0xF, true));
 }
 
 // Running-max sentinel: finite, so exp2(s - m) needs no special cases
@@ -85,48 +93,56 @@ struct Pair {
 };
 
 // Where pair k of a wave's work (pages [p_lo, p_hi) of one sequence) lives.
+// Loads go through buffer resources whose size covers only the page's
+// valid rows, so rows past the sequence end read as zero and are never
+// fetched from memory.
 struct PairSource {
   const uint8_t* pool;
   const int32_t* bt_row;     // block_table row of the sequence
-  long long page_bytes;
-  int pool_pages, L, T, H, pairs_per_page, h, s, c;
+  long long page_bytes, data_bytes;
+  int pool_pages, L, T, H, pairs_per_page, s;
   long long p_lo;
   int npairs;
+  uint32_t lane_data, lane_scale;  // this lane's byte offsets for row s
 };
 
-__device__ inline void load_pair(Pair& q, const PairSource& src, int k, const Geom& g) {
-  q.ok0 = q.ok1 = false;
-  q.k0 = q.k1 = q.v0 = q.v1 = (u32x2){0u, 0u};
-  q.ks0 = q.ks1 = q.vs0 = q.vs1 = 0u;
-  if (k >= src.npairs) return;
-  const long long pg = src.p_lo + k / src.pairs_per_page;
-  const int j = k % src.pairs_per_page;
-  const int slot = src.bt_row[pg];
-  if (slot < 0 || slot >= src.pool_pages) return;
+// Loads one lane's share of pair j of page `pg` (an index into the
+// sequence's page-table row; pages at or past `pg_end` read as empty).
+// The page's slot comes from a register (readlane), never from a memory
+// load issued behind the data loads, so waiting for it never drains the
+// data loads in flight.
+// Unconditional: out-of-range rows come back as zero from the buffer
+// resource, so no branch surrounds the loads.
+__device__ inline void load_pair(Pair& q, const PairSource& src, int slot_vec, long long c0,
+                                 long long pg, long long pg_end, int j) {
+  // page-table entries of pages c0 .. c0+63 sit one per lane in slot_vec
+  int slot = -1;
+  if (pg < pg_end) slot = __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
   int n_valid = src.L - (int)pg * src.T;
   if (n_valid > src.T) n_valid = src.T;
-  const uint8_t* page = src.pool + (long long)slot * src.page_bytes;
-  const long long H = src.H;
-  const uint8_t* kdat = page;
-  const uint8_t* vdat = page + (long long)src.T * H * (kD / 2);
-  const uint8_t* ksc = page + g.data_bytes();
-  const uint8_t* vsc = ksc + (long long)src.T * H * (kD / 16);
-  const int row0 = src.s + 16 * j, row1 = row0 + 8;
-  const long long r0 = (long long)row0 * H + src.h, r1 = (long long)row1 * H + src.h;
-  if (row0 < n_valid) {
-    q.ok0 = true;
-    q.k0 = *reinterpret_cast<const u32x2*>(kdat + r0 * 64 + src.c * 8);
-    q.v0 = *reinterpret_cast<const u32x2*>(vdat + r0 * 64 + src.c * 8);
-    q.ks0 = ksc[r0 * 8 + src.c];
-    q.vs0 = vsc[r0 * 8 + src.c];
-  }
-  if (row1 < n_valid) {
-    q.ok1 = true;
-    q.k1 = *reinterpret_cast<const u32x2*>(kdat + r1 * 64 + src.c * 8);
-    q.v1 = *reinterpret_cast<const u32x2*>(vdat + r1 * 64 + src.c * 8);
-    q.ks1 = ksc[r1 * 8 + src.c];
-    q.vs1 = vsc[r1 * 8 + src.c];
-  }
+  if (slot < 0 || slot >= src.pool_pages) n_valid = 0;
+  n_valid = __builtin_amdgcn_readfirstlane(n_valid);
+  const uint8_t* page = src.pool + (long long)(n_valid > 0 ? slot : 0) * src.page_bytes;
+  const int rowbytes = src.H * (kD / 2), rowscale = src.H * (kD / 16);
+  const uint8_t* vdat = page + (long long)src.T * rowbytes;
+  const uint8_t* ksc = page + src.data_bytes;
+  const uint8_t* vsc = ksc + (long long)src.T * rowscale;
+  auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, n_valid * rowbytes, 0x00020000);
+  auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vdat, (short)0, n_valid * rowbytes, 0x00020000);
+  auto rks = __builtin_amdgcn_make_buffer_rsrc((void*)ksc, (short)0, n_valid * rowscale, 0x00020000);
+  auto rvs = __builtin_amdgcn_make_buffer_rsrc((void*)vsc, (short)0, n_valid * rowscale, 0x00020000);
+  const int so0 = 16 * j * rowbytes, so1 = so0 + 8 * rowbytes;
+  const int ss0 = 16 * j * rowscale, ss1 = ss0 + 8 * rowscale;
+  q.k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, src.lane_data, so0, 0);
+  q.k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, src.lane_data, so1, 0);
+  q.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, src.lane_data, so0, 0);
+  q.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, src.lane_data, so1, 0);
+  q.ks0 = __builtin_amdgcn_raw_buffer_load_b8(rks, src.lane_scale, ss0, 0);
+  q.ks1 = __builtin_amdgcn_raw_buffer_load_b8(rks, src.lane_scale, ss1, 0);
+  q.vs0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, src.lane_scale, ss0, 0);
+  q.vs1 = __builtin_amdgcn_raw_buffer_load_b8(rvs, src.lane_scale, ss1, 0);
+  q.ok0 = src.s + 16 * j < n_valid;
+  q.ok1 = src.s + 16 * j + 8 < n_valid;
 }
 
 template <int G>
@@ -136,48 +152,58 @@ struct Stream {
   float m[G], l[G];
 };
 
-// Score of one row for every query of the group, summed over the stream.
+// Rare path: a running maximum grew; rescale the stream's state.
 template <int G>
-__device__ inline void row_scores(const Stream<G>& st, u32x2 kw, uint32_t kscale, bool ok,
-                                  float qscale, float out[G]) {
-  uint32_t kc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) kc[j] = fp4x2_to_bf16x2(j < 4 ? kw.x : kw.y, j & 3);
-  const float ks = scale_value(kscale) * qscale;
+__device__ inline void rescale(Stream<G>& st, const float (&mt)[G]) {
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    float p = 0.f;
+    const float alpha = __builtin_amdgcn_exp2f(st.m[i] - mt[i]);
+    st.l[i] *= alpha;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(st.q[i][j]), as_bf16x2(kc[j]), p, false);
-    p = dpp_sum8(p * ks);
-    out[i] = ok ? p : -INFINITY;
+    for (int d = 0; d < 16; ++d) st.acc[i][d] *= alpha;
+    st.m[i] = mt[i];
   }
 }
 
 template <int G>
 __device__ inline void process_pair(Stream<G>& st, const Pair& pr, float qscale) {
-  float s0[G], s1[G];
-  row_scores<G>(st, pr.k0, pr.ks0, pr.ok0, qscale, s0);
-  row_scores<G>(st, pr.k1, pr.ks1, pr.ok1, qscale, s1);
+  // scores of both rows for every query of the group
+  float sc[2 * G];
+  {
+    uint32_t k0[8], k1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      k0[j] = fp4x2_to_bf16x2(j < 4 ? pr.k0.x : pr.k0.y, j & 3);
+      k1[j] = fp4x2_to_bf16x2(j < 4 ? pr.k1.x : pr.k1.y, j & 3);
+    }
+    const float ks0 = scale_value(pr.ks0) * qscale, ks1 = scale_value(pr.ks1) * qscale;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(st.q[i][j]), as_bf16x2(k0[j]), p0, false);
+        p1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(st.q[i][j]), as_bf16x2(k1[j]), p1, false);
+      }
+      sc[i] = p0 * ks0;
+      sc[G + i] = p1 * ks1;
+    }
+  }
+  dpp_sum8<2 * G>(sc);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    sc[i] = pr.ok0 ? sc[i] : -INFINITY;
+    sc[G + i] = pr.ok1 ? sc[G + i] : -INFINITY;
+  }
   // online softmax: rescale only when some running maximum grows
   float mt[G];
   bool grew = false;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    mt[i] = fmaxf(st.m[i], fmaxf(s0[i], s1[i]));
+    mt[i] = fmaxf(st.m[i], fmaxf(sc[i], sc[G + i]));
     grew |= mt[i] > st.m[i];
   }
-  if (__builtin_amdgcn_ballot_w64(grew)) {
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m[i] - mt[i]);
-      st.l[i] *= alpha;
-#pragma unroll
-      for (int d = 0; d < 16; ++d) st.acc[i][d] *= alpha;
-      st.m[i] = mt[i];
-    }
-  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(grew) != 0, 0)) rescale<G>(st, mt);
   // P.V along the token axis: (p0 sv0, p1 sv1) . (c0[d], c1[d])
   uint32_t va[8], vb[8];
 #pragma unroll
@@ -189,8 +215,8 @@ __device__ inline void process_pair(Stream<G>& st, const Pair& pr, float qscale)
   uint32_t pp[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const float p0 = __builtin_amdgcn_exp2f(s0[i] - st.m[i]);
-    const float p1 = __builtin_amdgcn_exp2f(s1[i] - st.m[i]);
+    const float p0 = __builtin_amdgcn_exp2f(sc[i] - st.m[i]);
+    const float p1 = __builtin_amdgcn_exp2f(sc[G + i] - st.m[i]);
     st.l[i] += p0 + p1;
     bf16x2 w = {(__bf16)(p0 * sv0), (__bf16)(p1 * sv1)};
     pp[i] = __builtin_bit_cast(uint32_t, w);
@@ -207,9 +233,7 @@ __device__ inline void process_pair(Stream<G>& st, const Pair& pr, float qscale)
   }
 }
 
-constexpr int kPrefetch = 4;  // row pairs in flight per lane
-
-template <int G>
+template <int G, int PPP>  // PPP: row pairs per page (page size / 16)
 __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
   const Geom g = a.g;
   const int h = threadIdx.x >> 6;  // wave = KV head
@@ -222,7 +246,7 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
   balanced_range(a, w, nwg, rng);
   long long seq_start = rng.start_first;
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
-    const int L = clamped_len(a, b);
+    const int L = uniform(clamped_len(a, b));
     const int npages = (L + g.T - 1) / g.T;
     const long long first = seq_start;
     seq_start += npages;
@@ -246,27 +270,37 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
     src.pool = a.pool;
     src.bt_row = a.block_table + (long long)b * a.max_pages;
     src.page_bytes = g.packed_bytes();
+    src.data_bytes = g.data_bytes();
     src.pool_pages = a.pool_pages;
     src.L = L;
     src.T = g.T;
     src.H = g.H;
     src.pairs_per_page = g.T / 16;
-    src.h = h;
     src.s = s;
-    src.c = c;
     src.p_lo = p_lo;
     src.npairs = (int)(p_hi - p_lo) * src.pairs_per_page;
+    src.lane_data = (uint32_t)((s * g.H + h) * (kD / 2) + c * 8);
+    src.lane_scale = (uint32_t)((s * g.H + h) * (kD / 16) + c);
 
-    Pair ring[kPrefetch];
+    // Two page buffers: while one page is processed the next one is in
+    // flight (a page is 64 rows x 144 bytes per wave for a 64-row page).
+    // Pages go in chunks of 64 whose page-table entries are read once.
+    for (long long c0 = p_lo; c0 < p_hi; c0 += 64) {
+      const long long ce = c0 + 64 < p_hi ? c0 + 64 : p_hi;
+      const int slot_vec = (c0 + lane < ce) ? src.bt_row[c0 + lane] : -1;
+      Pair A[PPP], B[PPP];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) load_pair(ring[k], src, k, g);
-    for (int k0 = 0; k0 < src.npairs; k0 += kPrefetch) {
+      for (int j = 0; j < PPP; ++j) load_pair(A[j], src, slot_vec, c0, c0, ce, j);
+      for (long long pg = c0; pg < ce; pg += 2) {
 #pragma unroll
-      for (int j = 0; j < kPrefetch; ++j) {
-        if (k0 + j < src.npairs) {
-          const Pair cur = ring[j];
-          load_pair(ring[j], src, k0 + j + kPrefetch, g);
-          process_pair<G>(st, cur, qscale);
+        for (int j = 0; j < PPP; ++j) load_pair(B[j], src, slot_vec, c0, pg + 1, ce, j);
+#pragma unroll
+        for (int j = 0; j < PPP; ++j) process_pair<G>(st, A[j], qscale);
+#pragma unroll
+        for (int j = 0; j < PPP; ++j) load_pair(A[j], src, slot_vec, c0, pg + 2, ce, j);
+        if (pg + 1 < ce) {
+#pragma unroll
+          for (int j = 0; j < PPP; ++j) process_pair<G>(st, B[j], qscale);
         }
       }
     }
@@ -310,7 +344,13 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
 
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_gqa_kernel<G>), dim3(a.nwg), dim3(64 * a.g.H), 0, stream, a);
+  const dim3 grid(a.nwg), block(64 * a.g.H);
+  switch (a.g.T) {
+    case 16: hipLaunchKernelGGL((decode_gqa_kernel<G, 1>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((decode_gqa_kernel<G, 2>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((decode_gqa_kernel<G, 4>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -31,6 +31,16 @@ __device__ inline long long range_begin(long long ptot, int w, int nwg) {
   return (long long)w * ptot / nwg;
 }
 
+// Wave-uniform copies (values every lane already agrees on), so that the
+// compiler keeps them in scalar registers and can build buffer resources
+// and branch on them without per-lane loops.
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline long long uniform(long long v) {
+  unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v & 0xFFFFFFFFu));
+  unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 struct BalancedRange {
   long long ptot;         // pages in the batch
   long long p_begin;      // this workgroup's pages [p_begin, p_end)
@@ -59,6 +69,7 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
     int np = b < a.batch ? pages_of(a, b) : 0;
     tot += __shfl(wave_incl_scan(np), 63);
   }
+  tot = uniform(tot);
   r.ptot = tot;
   r.p_begin = range_begin(tot, w, nwg);
   r.p_end = range_begin(tot, w + 1, nwg);
@@ -74,11 +85,11 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
     unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
     if (m) {
       int l0 = __builtin_ctzll(m);
-      r.b_first = base + l0;
-      r.start_first = run + __shfl(incl - np, l0);
+      r.b_first = uniform(base + l0);
+      r.start_first = uniform(run + __shfl(incl - np, l0));
       return;
     }
-    run += __shfl(incl, 63);
+    run = uniform(run + __shfl(incl, 63));
   }
 }
 
