@@ -63,7 +63,8 @@ extern "C" {
 
 /* Page geometry.  num_kv_tensors: 2 = separate K and V (MHA/GQA), 1 = one
  * shared latent (MLA: the key is the whole row, the value its first v_dim
- * elements).  head_dim must be a positive multiple of 16. */
+ * elements).  head_dim must be a positive multiple of 16, and a page holds
+ * at most 2^28 values. */
 typedef struct kvfp4_geometry {
   int32_t num_kv_tensors;
   int32_t page_size;    /* tokens per page T          */

@@ -33,7 +33,7 @@ bool geometry_valid(const kvfp4_geometry* g) {
   if (g->page_size <= 0 || g->num_kv_heads <= 0 || g->head_dim <= 0) return false;
   if (g->head_dim % 16 != 0) return false;
   long long e = (long long)g->num_kv_tensors * g->page_size * g->num_kv_heads * g->head_dim;
-  return e <= (1LL << 30);
+  return e <= (1LL << 28);  // a page's bf16 bytes stay within a 32-bit offset
 }
 
 int32_t check_geometry(const kvfp4_geometry* g) {

@@ -2,24 +2,36 @@
 //
 // "KV Cache Compression in TensorRT LLM", NVFP4 Cold-Page Compression / How
 // It Works: a batch of pages is encoded into one fixed-size block per page
-// on the way out and decoded on the way back.  Both kernels are pure
-// streaming maps (HBM-bound): one lane owns one 16-value block, so a wave
-// reads 2 KiB of bf16 contiguously and writes 512 data bytes + 64 scale
-// bytes contiguously; pages are found through the slot arrays.
+// on the way out and decoded on the way back.  Both kernels are streaming
+// maps: one lane owns half a 16-value block, so every wave instruction
+// moves one contiguous run (1 KiB of bf16, 256 packed bytes), and each lane
+// keeps several half-blocks in flight.
+// Each workgroup owns a contiguous run of pages and walks them block by
+// block; a page's slot is read once per page (scalar), and all loads and
+// stores go through per-page buffer resources, so no per-lane 64-bit
+// address arithmetic is needed.
 //
-// Exactness.  The block scale is E4M3(amax / (6 gs)) and an element code is
-// E2M1(|x| / (sb gs)), both rounded once from the exact quotient.  Instead
-// of dividing, each workgroup builds, per tensor, the exact rounding
-// thresholds of both steps in fp64 (every threshold mid * 6 gs or
-// mu * sb * gs has at most 31 significant bits, so fp64 holds it exactly)
-// and turns each into an integer threshold on bf16 magnitude bit patterns
-// with directed rounding: for a bf16 magnitude v, "v > M" equals
-// "bits(v) > bits(RD(M))" and "v >= M" equals "bits(v) > bits(RU(M)) - 1".
-// A code is then the number of thresholds its input exceeds, found by
-// binary search: 7 steps over 126 E4M3 thresholds per block, 3 steps over 7
-// E2M1 thresholds per element, two elements per packed 16-bit instruction.
-// Ties go to the even code because even-code boundaries use the strict and
-// odd-code boundaries the non-strict comparison.
+// Exactness, encoder.  The block scale is E4M3(amax / (6 gs)) and an
+// element code is E2M1(|x| / (sb gs)), each rounded once from the exact
+// quotient.  Every workgroup first builds, per tensor, the exact rounding
+// thresholds of both steps in fp64 (a threshold mid * 6 gs or mu * sb * gs
+// has at most 31 significant bits, so fp64 holds it exactly) and turns each
+// into an integer threshold on bf16 magnitude bit patterns by directed
+// rounding: for a bf16 magnitude v, "v > M" equals "bits(v) > bits(RD(M))"
+// and "v >= M" equals "bits(v) > bits(RU(M)) - 1".  A code is the number of
+// thresholds its input exceeds.  Ties go to the even code because
+// even-code boundaries use the strict and odd-code boundaries the
+// non-strict comparison.
+//  - scale: an fp64 estimate of amax / (6 gs), truncated to E4M3, is the
+//    exact code or one below it; one threshold comparison decides.
+//  - elements: a 3-step binary search over the 7 thresholds, two elements
+//    per packed 16-bit instruction; selects are multiply-adds by 0/1.
+//
+// Exactness, decoder.  For a given tensor scale the result depends only on
+// the scale code (128) and the magnitude code (8): every workgroup builds
+// that table once, each entry rounded to bf16 once from the exact fp64
+// product, stored as 8 low bytes then 8 high bytes per scale code; an
+// element is then two byte lookups (v_perm) plus its sign bit.
 #include "common.hpp"
 
 namespace kvfp4 {
@@ -27,25 +39,51 @@ namespace kvfp4 {
 namespace {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr uint32_t kPad = 0x7FFFu;  // above every finite bf16 magnitude
+constexpr int kRsrcFlags = 0x00020000;
 
-// LDS threshold tables, one set per tensor.
+__device__ inline u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ inline uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ inline uint32_t pk_sub(uint32_t a, uint32_t b) { return as_u32(as_u16x2(a) - as_u16x2(b)); }
+__device__ inline uint32_t pk_mad(uint32_t a, uint32_t b, uint32_t c) {
+  return as_u32(as_u16x2(a) * as_u16x2(b) + as_u16x2(c));
+}
+__device__ inline uint32_t pk_shr15(uint32_t a) { return as_u32(as_u16x2(a) >> (u16x2){15, 15}); }
+// 1 in each 16-bit half where the magnitude v exceeds threshold t (both < 0x8000)
+__device__ inline uint32_t gt_bit(uint32_t t, uint32_t v) { return pk_shr15(pk_sub(t, v)); }
+__device__ inline uint32_t dup16(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x01000100u); }
+
+// Pages [p0, p1) of this workgroup.
+__device__ inline void page_range(int num_pages, int& p0, int& p1) {
+  p0 = (int)((long long)blockIdx.x * num_pages / gridDim.x);
+  p1 = (int)((long long)(blockIdx.x + 1) * num_pages / gridDim.x);
+}
+
+__device__ inline int page_slot(const int32_t* slots, int i, int pool_pages) {
+  int s = slots ? __builtin_amdgcn_readfirstlane(slots[i]) : i;
+  return (s >= 0 && s < pool_pages) ? s : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Encoder
+// ---------------------------------------------------------------------------
+
 struct QuantLds {
   uint16_t e4m3[2][128];     // scale thresholds (126 used)
   uint16_t e2m1[2][128][8];  // element thresholds per scale code (7 used)
+  double inv6gs[2];          // 1 / (6 gs) per tensor, for the scale estimate
 };
 
-__device__ inline void build_tables(QuantLds& s, int nt, float gs0, float gs1) {
+__device__ inline void build_quant_tables(QuantLds& s, int nt, float gs0, float gs1) {
   const double mu[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  if (threadIdx.x < 2) s.inv6gs[threadIdx.x] = 1.0 / (6.0 * (double)(threadIdx.x ? gs1 : gs0));
   for (int i = threadIdx.x; i < nt * 128; i += blockDim.x) {
     int t = i >> 7, j = i & 127;
     double gs = t == 0 ? (double)gs0 : (double)gs1;
-    // E4M3 midpoint between codes j and j+1, times 6 gs (exact in fp64).
     uint32_t th = kPad;
-    if (j < 126) {
+    if (j < 126) {  // E4M3 midpoint between codes j and j+1, times 6 gs
       double mid = 0.5 * ((double)e4m3_to_float(j) + (double)e4m3_to_float(j + 1));
       th = gt_threshold(mid * 6.0 * gs, (j & 1) == 0);
     }
@@ -59,152 +97,229 @@ __device__ inline void build_tables(QuantLds& s, int nt, float gs0, float gs1) {
   }
 }
 
-// Number of the 128 sorted scale thresholds that amax exceeds.
-__device__ inline uint32_t scale_code(const uint16_t* th, uint32_t amax) {
-  uint32_t pos = 0;
-#pragma unroll
-  for (uint32_t step = 64; step >= 1; step >>= 1) pos += (amax > th[pos + step - 1]) ? step : 0;
-  return pos;
+// E4M3 code of amax / (6 gs): the truncation of an fp64 estimate (error
+// far below E4M3's spacing, and no overflow for any valid gs) is the exact
+// code or one below it; the exact threshold decides.
+__device__ inline uint32_t scale_code(const uint16_t* th, uint32_t amax_bits, double inv6gs) {
+  const double q = (double)__uint_as_float(amax_bits << 16) * inv6gs;
+  const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(q) >> 32);
+  const int e = (int)(hi >> 20) - 1016;  // E4M3 exponent field for normal codes
+  uint32_t cand;
+  if (e >= 1) {
+    const int c = (e << 3) | (int)((hi >> 17) & 7);
+    cand = (uint32_t)(c > 126 ? 126 : c);
+  } else {
+    const double sub = q * 512.0;  // subnormal codes: m * 2^-9
+    cand = sub >= 7.0 ? 7u : (uint32_t)sub;
+  }
+  return cand + (amax_bits > th[cand] ? 1u : 0u);
 }
-
-__device__ inline u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
-__device__ inline s16x2 as_s16x2(uint32_t x) { return __builtin_bit_cast(s16x2, x); }
-__device__ inline uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ inline uint32_t as_u32(s16x2 x) { return __builtin_bit_cast(uint32_t, x); }
-
-// 0xFFFF in each half whose magnitude v exceeds the threshold t (both < 0x8000).
-__device__ inline uint32_t gt_mask(uint32_t t, uint32_t v) {
-  return as_u32(as_s16x2(as_u32(as_u16x2(t) - as_u16x2(v))) >> (s16x2){15, 15});
-}
-__device__ inline uint32_t gt_bit(uint32_t t, uint32_t v) {
-  return as_u32(as_u16x2(as_u32(as_u16x2(t) - as_u16x2(v))) >> (u16x2){15, 15});
-}
-__device__ inline uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
 
 // Two elements (one dword of bf16) -> two nibbles in bits 3:0 and 19:16.
-__device__ inline uint32_t encode_pair(uint32_t raw, const uint32_t T[7]) {
-  uint32_t v = raw & 0x7FFF7FFFu;
-  uint32_t m1 = gt_mask(T[3], v);
-  uint32_t m2 = gt_mask(bfi(m1, T[5], T[1]), v);
-  uint32_t ta = bfi(m1, T[4], T[0]);
-  uint32_t tb = bfi(m1, T[6], T[2]);
-  uint32_t b0 = gt_bit(bfi(m2, tb, ta), v);
-  uint32_t code = (m1 & 0x00040004u) | (m2 & 0x00020002u) | b0;
-  return code | ((raw >> 12) & 0x00080008u);
+// T[k]: threshold k in both halves; D51 = T5 - T1, D40 = T4 - T0,
+// D20 = T2 - T0, DD = (T6 - T4) - (T2 - T0), all per half.
+struct Thr {
+  uint32_t T0, T1, T3, D51, D40, D20, DD;
+};
+
+// The sequence is written out instruction by instruction so that the
+// compiler keeps the 0/1 multiply-add selects (v_pk_mad_u16) instead of
+// expanding them into per-half masks.  k15 holds 15 in both halves, k8 the
+// sign-bit mask 0x00080008.
+__device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15, uint32_t k8) {
+  const uint32_t v = raw & 0x7FFF7FFFu;
+  uint32_t code, b1, b2, d, u, w;
+  asm volatile(
+      "v_pk_sub_u16 %[d], %[T3], %[v]\n\t"
+      "v_pk_lshrrev_b16 %[b1], %[k15], %[d]\n\t"           // b1 = v > T3
+      "v_pk_mad_u16 %[u], %[b1], %[D51], %[T1]\n\t"        // T5 or T1
+      "v_pk_sub_u16 %[d], %[u], %[v]\n\t"
+      "v_pk_lshrrev_b16 %[b2], %[k15], %[d]\n\t"           // b2
+      "v_pk_mad_u16 %[u], %[b1], %[D40], %[T0]\n\t"        // T4 or T0
+      "v_pk_mad_u16 %[w], %[b1], %[DD], %[D20]\n\t"        // T6-T4 or T2-T0
+      "v_pk_mad_u16 %[u], %[b2], %[w], %[u]\n\t"           // T6, T4, T2 or T0
+      "v_pk_sub_u16 %[d], %[u], %[v]\n\t"
+      "v_pk_lshrrev_b16 %[d], %[k15], %[d]\n\t"            // b3
+      "v_lshl_or_b32 %[d], %[b2], 1, %[d]\n\t"
+      "v_lshl_or_b32 %[code], %[b1], 2, %[d]\n\t"
+      "v_lshrrev_b32 %[w], 12, %[raw]\n\t"
+      "v_and_or_b32 %[code], %[w], %[k8], %[code]"         // sign bits
+      : [code] "=&v"(code), [b1] "=&v"(b1), [b2] "=&v"(b2), [d] "=&v"(d), [u] "=&v"(u),
+        [w] "=&v"(w)
+      : [v] "v"(v), [raw] "v"(raw), [T0] "v"(t.T0), [T1] "v"(t.T1), [T3] "v"(t.T3),
+        [D51] "v"(t.D51), [D40] "v"(t.D40), [D20] "v"(t.D20), [DD] "v"(t.DD), [k15] "v"(k15),
+        [k8] "v"(k8));
+  return code;
 }
+
+constexpr int kQuantUnroll = 4;    // half-blocks in flight per lane
+constexpr int kDequantUnroll = 8;
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     Geom g, const uint8_t* __restrict__ hot, int hot_pages, const int32_t* __restrict__ src,
     uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ dst,
-    long long total_blocks, float gs0, float gs1) {
+    int num_pages, float gs0, float gs1) {
   __shared__ QuantLds s;
-  build_tables(s, g.nt, gs0, gs1);
+  build_quant_tables(s, g.nt, gs0, gs1);
   __syncthreads();
-
-  const long long bpp = (long long)g.elems() / kBlock;  // blocks per page
+  const uint32_t k15 = 0x000F000Fu, k8 = 0x00080008u;
+  // A lane owns half a block (8 values): 16 contiguous input bytes, 4
+  // output bytes; the two halves of a block sit in adjacent lanes.
+  const int hpp = (int)(g.elems() / 8);  // half-blocks per page
   const int bpt = g.blocks_per_tensor();
-  const long long stride = (long long)gridDim.x * kThreads;
-  for (long long blk = (long long)blockIdx.x * kThreads + threadIdx.x; blk < total_blocks;
-       blk += stride) {
-    long long page = blk / bpp;
-    int bip = (int)(blk - page * bpp);
-    int ss = src ? src[page] : (int)page;
-    int ds = dst ? dst[page] : (int)page;
-    if (ss < 0 || ss >= hot_pages || ds < 0 || ds >= packed_pages) continue;
-    int t = bip >= bpt ? 1 : 0;
-    const u32x4* in = reinterpret_cast<const u32x4*>(hot + (long long)ss * g.hot_bytes() +
-                                                     (long long)bip * 32);
-    u32x4 a = __builtin_nontemporal_load(in);
-    u32x4 b = __builtin_nontemporal_load(in + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    // block amax over 16 magnitudes, two per packed max
-    u16x2 mx = as_u16x2(w[0] & 0x7FFF7FFFu);
+  const int data_bytes = (int)g.data_bytes();
+  int p0, p1;
+  page_range(num_pages, p0, p1);
+  for (int p = p0; p < p1; ++p) {
+    const int ss = page_slot(src, p, hot_pages);
+    const int ds = page_slot(dst, p, packed_pages);
+    if (ss < 0 || ds < 0) continue;
+    const uint8_t* in = hot + (long long)ss * g.hot_bytes();
+    uint8_t* out = packed + (long long)ds * g.packed_bytes();
+    auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)in, (short)0, (int)g.hot_bytes(), kRsrcFlags);
+    auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)g.packed_bytes(), kRsrcFlags);
+    for (int h0 = 0; h0 < hpp; h0 += kThreads * kQuantUnroll) {
+      u32x4 a[kQuantUnroll];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = __builtin_elementwise_max(mx, as_u16x2(w[i] & 0x7FFF7FFFu));
-    uint32_t amax = mx.x > mx.y ? mx.x : mx.y;
-    uint32_t sc = scale_code(s.e4m3[t], amax);
-    const u32x4 trow = *reinterpret_cast<const u32x4*>(s.e2m1[t][sc]);
-    uint32_t th16[8] = {trow.x & 0xFFFF, trow.x >> 16, trow.y & 0xFFFF, trow.y >> 16,
-                        trow.z & 0xFFFF, trow.z >> 16, trow.w & 0xFFFF, trow.w >> 16};
-    uint32_t T[7];
+      for (int u = 0; u < kQuantUnroll; ++u) {
+        // out-of-range half-blocks read zero (buffer bounds) and store nothing
+        a[u] = __builtin_amdgcn_raw_buffer_load_b128(rin, (h0 + u * kThreads + (int)threadIdx.x) * 16, 0, 0);
+      }
 #pragma unroll
-    for (int k = 0; k < 7; ++k) T[k] = th16[k] | (th16[k] << 16);
-    uint32_t by[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t n = encode_pair(w[i], T);
-      by[i] = (n | (n >> 12)) & 0xFFu;
-    }
-    u32x2 o;
-    o.x = by[0] | (by[1] << 8) | (by[2] << 16) | (by[3] << 24);
-    o.y = by[4] | (by[5] << 8) | (by[6] << 16) | (by[7] << 24);
-    uint8_t* pp = packed + (long long)ds * g.packed_bytes();
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(pp + (long long)bip * 8));
-    pp[g.data_bytes() + bip] = (uint8_t)sc;
-  }
-}
-
-// bf16 bits of (+-) cs * gs, rounded once, for |cs * gs| in fp32's normal
-// range and an exactly representable product error (gs >= 2^-96): the fp32
-// product is taken to round-to-odd (sticky last bit) and then rounded to
-// bf16, which equals rounding the exact product once.
-__device__ inline uint32_t bf16_of_product(float cs, float gs) {
-  float p = __fmul_rn(cs, gs);
-  float err = __fmaf_rn(cs, gs, -p);
-  uint32_t pb = __float_as_uint(p);
-  bool inexact = err != 0.0f;
-  bool away = inexact && ((err < 0.0f) != (p < 0.0f));  // |p| > |exact|
-  pb = pb - (away ? 1u : 0u);
-  pb = pb | (inexact ? 1u : 0u);
-  return (pb + 0x7FFFu + ((pb >> 16) & 1u)) >> 16;
-}
-
-template <bool kTinyScale>
-__global__ __launch_bounds__(kThreads) void dequantize_kernel(
-    Geom g, const uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ src,
-    uint8_t* __restrict__ hot, int hot_pages, const int32_t* __restrict__ dst,
-    long long total_blocks, float gs0, float gs1) {
-  const long long bpp = (long long)g.elems() / kBlock;
-  const int bpt = g.blocks_per_tensor();
-  const long long stride = (long long)gridDim.x * kThreads;
-  for (long long blk = (long long)blockIdx.x * kThreads + threadIdx.x; blk < total_blocks;
-       blk += stride) {
-    long long page = blk / bpp;
-    int bip = (int)(blk - page * bpp);
-    int ss = src ? src[page] : (int)page;
-    int ds = dst ? dst[page] : (int)page;
-    if (ss < 0 || ss >= packed_pages || ds < 0 || ds >= hot_pages) continue;
-    float gs = bip >= bpt ? gs1 : gs0;
-    const uint8_t* pp = packed + (long long)ss * g.packed_bytes();
-    u32x2 d = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(pp + (long long)bip * 8));
-    float sb = e4m3_to_float(pp[g.data_bytes() + bip]);
-    uint32_t h[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t word = i < 8 ? d.x : d.y;
-      uint32_t nib = (word >> (4 * (i & 7))) & 0xF;
-      float cs = e2m1_mag_to_float(nib & 7) * sb;  // exact: <= 6 significant bits
-      uint32_t sign = (nib & 8) << 12;
-      if (kTinyScale) {
-        h[i] = bf16_rne_from_f64((double)cs * (double)gs) ^ sign;
-      } else {
-        h[i] = bf16_of_product(cs, gs) ^ sign;
+      for (int u = 0; u < kQuantUnroll; ++u) {
+        const int hb = h0 + u * kThreads + (int)threadIdx.x;
+        const int blk = hb >> 1;
+        const uint32_t w[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+        u16x2 mx = __builtin_elementwise_max(as_u16x2(w[0] & 0x7FFF7FFFu), as_u16x2(w[1] & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, as_u16x2(w[2] & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, as_u16x2(w[3] & 0x7FFF7FFFu));
+        uint32_t amax = mx.x > mx.y ? mx.x : mx.y;
+        // the partner lane holds the other half of the block
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true);
+        amax = amax > other ? amax : other;
+        const int t = blk >= bpt ? 1 : 0;
+        const uint32_t sc = scale_code(s.e4m3[t], amax, s.inv6gs[t]);
+        const u32x4 row = *reinterpret_cast<const u32x4*>(s.e2m1[t][sc]);
+        Thr th;
+        th.T0 = dup16(row.x);
+        th.T1 = dup16(row.x >> 16);
+        const uint32_t T2 = dup16(row.y), T4 = dup16(row.z), T5 = dup16(row.z >> 16);
+        const uint32_t T6 = dup16(row.w);
+        th.T3 = dup16(row.y >> 16);
+        th.D51 = pk_sub(T5, th.T1);
+        th.D40 = pk_sub(T4, th.T0);
+        th.D20 = pk_sub(T2, th.T0);
+        th.DD = pk_sub(pk_sub(T6, T4), th.D20);
+        // pairs (0,1),(2,3) -> nibbles e0..e3; pairs (4,5),(6,7) -> e4..e7
+        const uint32_t n0 = encode_pair(w[0], th, k15, k8) | (encode_pair(w[1], th, k15, k8) << 8);
+        const uint32_t n1 = encode_pair(w[2], th, k15, k8) | (encode_pair(w[3], th, k15, k8) << 8);
+        const uint32_t h0w = n0 | (n0 >> 12), h1w = n1 | (n1 >> 12);
+        if (hb < hpp) {
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(h1w, h0w, 0x05040100u), rout,
+                                                hb * 4, 0, 0);
+          if ((hb & 1) == 0)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + blk, 0, 0);
+        }
       }
     }
-    u32x4 o0 = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    u32x4 o1 = {h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16),
-                h[14] | (h[15] << 16)};
-    u32x4* out = reinterpret_cast<u32x4*>(hot + (long long)ds * g.hot_bytes() + (long long)bip * 32);
-    __builtin_nontemporal_store(o0, out);
-    __builtin_nontemporal_store(o1, out + 1);
   }
 }
 
-int grid_for(long long total_blocks) {
-  long long wgs = (total_blocks + kThreads - 1) / kThreads;
-  // enough workgroups to cover 256 CUs several times; each then loops
-  long long cap = 256LL * 16;
-  return (int)(wgs < cap ? wgs : cap);
+// ---------------------------------------------------------------------------
+// Decoder
+// ---------------------------------------------------------------------------
+
+struct DequantLds {
+  // per tensor and scale code: 8 low bytes then 8 high bytes of the bf16
+  // results for magnitude codes 0..7
+  uint32_t row[2][128][4];
+};
+
+__device__ inline void build_dequant_table(DequantLds& s, int nt, float gs0, float gs1) {
+  uint8_t* bytes = reinterpret_cast<uint8_t*>(&s.row[0][0][0]);
+  for (int i = threadIdx.x; i < nt * 128 * 8; i += blockDim.x) {
+    const int t = i >> 10, j = (i >> 3) & 127, c = i & 7;
+    const double gs = t == 0 ? (double)gs0 : (double)gs1;
+    // exact: <= 2 + 4 + 24 significant bits
+    const double v = (double)e2m1_mag_to_float(c) * (double)e4m3_to_float(j) * gs;
+    uint32_t b16 = (j == 127) ? 0x7FC0u : bf16_rne_from_f64(v);
+    uint8_t* r = bytes + ((t * 128 + j) * 16);
+    r[c] = (uint8_t)(b16 & 0xFF);
+    r[8 + c] = (uint8_t)(b16 >> 8);
+  }
+}
+
+// Four elements (selector bytes: bit 3 sign, bits 2:0 magnitude code) ->
+// bf16 pairs (e0, e1), (e2, e3).
+__device__ inline void lookup4(uint32_t sel, const u32x4& row, uint32_t& o0, uint32_t& o1) {
+  const uint32_t m = sel & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(row.y, row.x, m);
+  uint32_t hi = __builtin_amdgcn_perm(row.w, row.z, m);
+  hi |= (sel & 0x08080808u) << 4;  // sign into bit 7 of the high byte
+  o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// Eight nibbles of one data word -> four bf16 pairs in element order.
+__device__ inline void decode8(uint32_t w, const u32x4& row, uint32_t sign_flip, uint32_t* o) {
+  const uint32_t x = w & 0x0F0F0F0Fu;         // elements 0 2 4 6
+  const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;  // elements 1 3 5 7
+  const uint32_t s0 = __builtin_amdgcn_perm(y, x, 0x05010400u) ^ sign_flip;  // 0 1 2 3
+  const uint32_t s1 = __builtin_amdgcn_perm(y, x, 0x07030602u) ^ sign_flip;  // 4 5 6 7
+  lookup4(s0, row, o[0], o[1]);
+  lookup4(s1, row, o[2], o[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+    Geom g, const uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ src,
+    uint8_t* __restrict__ hot, int hot_pages, const int32_t* __restrict__ dst, int num_pages,
+    float gs0, float gs1) {
+  __shared__ DequantLds s;
+  build_dequant_table(s, g.nt, gs0, gs1);
+  __syncthreads();
+  // A lane owns half a block: 4 data bytes + the block's scale byte in,
+  // 16 contiguous output bytes.
+  const int hpp = (int)(g.elems() / 8);
+  const int bpt = g.blocks_per_tensor();
+  const int data_bytes = (int)g.data_bytes();
+  int p0, p1;
+  page_range(num_pages, p0, p1);
+  for (int p = p0; p < p1; ++p) {
+    const int ss = page_slot(src, p, packed_pages);
+    const int ds = page_slot(dst, p, hot_pages);
+    if (ss < 0 || ds < 0) continue;
+    const uint8_t* in = packed + (long long)ss * g.packed_bytes();
+    uint8_t* out = hot + (long long)ds * g.hot_bytes();
+    auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)in, (short)0, (int)g.packed_bytes(), kRsrcFlags);
+    auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)g.hot_bytes(), kRsrcFlags);
+    for (int h0 = 0; h0 < hpp; h0 += kThreads * kDequantUnroll) {
+      uint32_t dw[kDequantUnroll], code[kDequantUnroll];
+#pragma unroll
+      for (int u = 0; u < kDequantUnroll; ++u) {
+        const int hb = h0 + u * kThreads + (int)threadIdx.x;
+        dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, 0);
+        code[u] = hb < hpp ? __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0, 0) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kDequantUnroll; ++u) {
+        const int hb = h0 + u * kThreads + (int)threadIdx.x;
+        const int t = (hb >> 1) >= bpt ? 1 : 0;
+        const u32x4 row = *reinterpret_cast<const u32x4*>(s.row[t][code[u] & 127]);
+        const uint32_t flip = (code[u] & 0x80u) ? 0x08080808u : 0u;  // negative E4M3 scale
+        uint32_t o[4];
+        decode8(dw[u], row, flip, o);
+        if (hb < hpp)
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rout, hb * 16, 0, 0);
+      }
+    }
+  }
+}
+
+int grid_for(int num_pages) {
+  // one workgroup per page up to 8 per CU of a 256-CU part; each walks its
+  // contiguous run of pages
+  const int cap = 2048;
+  return num_pages < cap ? num_pages : cap;
 }
 
 }  // namespace
@@ -212,31 +327,22 @@ int grid_for(long long total_blocks) {
 hipError_t launch_quantize(const Geom& g, const void* hot, int hot_pages, const int32_t* src,
                            void* packed, int packed_pages, const int32_t* dst, int num_pages,
                            const float* gs, hipStream_t stream) {
-  long long total = (long long)num_pages * (g.elems() / kBlock);
-  if (total == 0) return hipSuccess;
+  if (num_pages == 0) return hipSuccess;
   float gs1 = g.nt > 1 ? gs[1] : gs[0];
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream, g,
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)hot, hot_pages, src, (uint8_t*)packed, packed_pages, dst,
-                     total, gs[0], gs1);
+                     num_pages, gs[0], gs1);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages,
                              const int32_t* src, void* hot, int hot_pages, const int32_t* dst,
                              int num_pages, const float* gs, hipStream_t stream) {
-  long long total = (long long)num_pages * (g.elems() / kBlock);
-  if (total == 0) return hipSuccess;
+  if (num_pages == 0) return hipSuccess;
   float gs1 = g.nt > 1 ? gs[1] : gs[0];
-  bool tiny = gs[0] < 0x1p-96f || gs1 < 0x1p-96f;
-  if (tiny) {
-    hipLaunchKernelGGL(dequantize_kernel<true>, dim3(grid_for(total)), dim3(kThreads), 0, stream,
-                       g, (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
-                       total, gs[0], gs1);
-  } else {
-    hipLaunchKernelGGL(dequantize_kernel<false>, dim3(grid_for(total)), dim3(kThreads), 0, stream,
-                       g, (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
-                       total, gs[0], gs1);
-  }
+  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
+                     (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
+                     num_pages, gs[0], gs1);
   return hipGetLastError();
 }
 
