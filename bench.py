@@ -10,8 +10,9 @@ Llama-3-8B-shaped layer (batch 32, 32 q / 8 KV heads, head_dim 128, 8192
 tokens, 64-token pages in a seeded permutation; 4096 pages).
 
 Timing: HIP events on the stream the kernels run on, around each kernel;
-between kernels an untimed 1 GiB write evicts the 256 MiB Infinity Cache so
-that bytes come from HBM.  `value` is the step's algorithmic bytes divided
+between kernels an untimed 1 GiB read evicts the 256 MiB Infinity Cache so
+that bytes come from HBM (a read, so that no dirty lines are left to be
+written back inside the next timed kernel).  `value` is the step's algorithmic bytes divided
 by its kernel time.  Prints one JSON line.
 """
 
@@ -41,6 +42,9 @@ def parse():
                    choices=["tiny", "llama3_8b", "qwen3_8b_long", "mla", "cold_pages"])
     p.add_argument("--gs", default="calibrated", choices=["calibrated", "unit"])
     p.add_argument("--no-flush", action="store_true", help="do not evict caches between kernels")
+    p.add_argument("--flush-mode", default="read", choices=["read", "write"],
+                   help="evict caches by reading (default; leaves no dirty lines to be "
+                        "written back inside the next timed kernel) or writing 1 GiB")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-pages", type=int, default=6)
     p.add_argument("--no-copy-yardstick", action="store_true",
@@ -155,7 +159,15 @@ def main():
     pbytes = K.kvfp4_packed_page_bytes(geometry)
     packed = torch.zeros((num_slots, pbytes), dtype=torch.uint8, device=dev)
     hot_back = torch.empty_like(hot)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def evict():
+        # touch 1 GiB (4x the 256 MiB Infinity Cache) between timed kernels
+        if args.flush_mode == "read":
+            torch.sum(flush, dim=0, out=flush_sink)
+        else:
+            flush.fill_(1)
 
     if wl is not None:
         q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
@@ -187,7 +199,7 @@ def main():
         for _ in range(n_steps):
             for k, fn in legs:
                 if not args.no_flush:
-                    flush.fill_(1)
+                    evict()
                 if timed:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
@@ -206,7 +218,7 @@ def main():
         dst_c = torch.empty_like(src_c)
         times = []
         for i in range(4):
-            flush.fill_(2)
+            evict()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -278,7 +290,7 @@ def main():
         "dtype": "bf16<->nvfp4 codec (integer thresholds), fp32 attention",
         "data": "synthetic (seeded)",
         "config": {"workload": wdesc, "global_scale": args.gs, "cache_flush_between_kernels":
-                   not args.no_flush, "global_batch": wl.batch if wl is not None else None,
+                   "none" if args.no_flush else args.flush_mode + " 1 GiB", "global_batch": wl.batch if wl is not None else None,
                    "seq_len": int(wl.seq_lens.max()) if wl is not None else None,
                    "parallelism": "single GPU"},
         "kernels": kern,

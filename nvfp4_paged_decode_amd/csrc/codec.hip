@@ -152,8 +152,17 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
   return code;
 }
 
-constexpr int kQuantUnroll = 4;    // half-blocks in flight per lane
-constexpr int kDequantUnroll = 8;
+#ifndef KVFP4_QUANT_UNROLL
+#define KVFP4_QUANT_UNROLL 4
+#endif
+#ifndef KVFP4_DEQUANT_UNROLL
+#define KVFP4_DEQUANT_UNROLL 8
+#endif
+#ifndef KVFP4_CODEC_GRID
+#define KVFP4_CODEC_GRID 2048
+#endif
+constexpr int kQuantUnroll = KVFP4_QUANT_UNROLL;    // half-blocks in flight per lane
+constexpr int kDequantUnroll = KVFP4_DEQUANT_UNROLL;
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     Geom g, const uint8_t* __restrict__ hot, int hot_pages, const int32_t* __restrict__ src,
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 int grid_for(int num_pages) {
   // one workgroup per page up to 8 per CU of a 256-CU part; each walks its
   // contiguous run of pages
-  const int cap = 2048;
+  const int cap = KVFP4_CODEC_GRID;
   return num_pages < cap ? num_pages : cap;
 }
 
