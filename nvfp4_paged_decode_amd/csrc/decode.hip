@@ -259,10 +259,13 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
     return p;
   }
   if (mla_supported(g, hq, v_dim) || gqa_supported(g, hq, v_dim)) {
-    // balanced kernels: one workgroup per CU (or per page when fewer)
+    // balanced kernels: one workgroup per CU (or per page when fewer); the
+    // MLA kernel runs two per CU and splits 128 heads over two workgroups
     p.kernel = mla_supported(g, hq, v_dim) ? 2 : 1;
+    long long target = cus;
+    if (p.kernel == 2) target = 2LL * cus / (hq > 64 ? hq / 64 : 1);
     long long pages_ub = (long long)batch * pages_max;
-    long long nwg = cus < pages_ub ? cus : pages_ub;
+    long long nwg = target < pages_ub ? target : pages_ub;
     p.nwg = (int)(nwg > 0 ? nwg : 1);
     p.splits = 0;
     p.pages_per_split = 0;
@@ -308,7 +311,5 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
 }
 
 // Shapes without a specialised kernel run on the generic one.
-bool mla_supported(const Geom&, int, int) { return false; }
-hipError_t launch_decode_mla(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace kvfp4
