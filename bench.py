@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+COPY_CALLS = 4          # 1 GiB device copies timed as the practical ceiling
+COPY_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -46,7 +49,8 @@ def parse():
                    help="evict caches by reading (default; leaves no dirty lines to be "
                         "written back inside the next timed kernel) or writing 1 GiB")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-pages", type=int, default=6)
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="approximate host time budget of the oracle sample")
     p.add_argument("--no-copy-yardstick", action="store_true",
                    help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
     return p.parse_args()
@@ -71,47 +75,59 @@ def codec_bytes(geometry, pages: int) -> int:
     return pages * (2 * e + e * 9 // 16)
 
 
-def cpu_baseline(wl, gs, pages: int, dec_bytes_per_token: float, step_bytes: float,
-                 step_unit_bytes: dict) -> dict:
+def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
+                 step_bytes: float) -> dict:
     """The oracle as it stands, on one host thread, over a bounded sample of
-    the same workload: `pages` pages encoded and decoded, and decode
-    attention for one sequence (all its query heads).  Reported in GB/s of
-    algorithmic bytes over the same byte accounting as the GPU figure."""
+    the same workload: pages encoded, then decoded, in chunks of 16 until
+    each direction has used about a quarter of `budget_s`, then decode
+    attention for whole sequences (all query heads) until about half of it
+    is used.  Each leg's rate is scaled to that leg's bytes in one step, and
+    the figure is the step's algorithmic bytes over the summed time."""
     from threadpoolctl import threadpool_limits
     from oracle import nvfp4 as O
     from oracle import attention as A
     g = O.Geometry(*wl.geometry)
-    slots = wl.used_slots[:pages]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        packed = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
-        O.quantize_pages(wl.hot_pool, g, pages, gs, packed, slots, slots)
-        t1 = time.perf_counter()
-        back = np.zeros((pages, *g.row_shape), np.uint16)
-        O.dequantize_pages(packed, g, pages, gs, back, slots, None)
-        t2 = time.perf_counter()
-        # decode over the first sequence: its pages are the first ones used
-        b = 0
-        need = -(-int(wl.seq_lens[b]) // wl.page_size)
-        bslots = wl.block_table[b, :need]
-        O.quantize_pages(wl.hot_pool, g, need, gs, packed, bslots, bslots)
-        t3 = time.perf_counter()
-        A.decode_attention(packed, g, gs, wl.q, wl.block_table, wl.seq_lens, wl.softmax_scale,
-                           wl.v_dim, batch_indices=[b])
-        t4 = time.perf_counter()
-    q_s, dq_s, dec_s = t1 - t0, t2 - t1, t4 - t3
-    # scale each leg to the whole step's bytes of that leg
     per_page = codec_bytes(wl.geometry, 1)
-    t_step = (step_unit_bytes["quantize"] / (pages * per_page)) * q_s + \
-             (step_unit_bytes["dequantize"] / (pages * per_page)) * dq_s + \
-             (step_unit_bytes["decode"] / (int(wl.seq_lens[b]) * dec_bytes_per_token)) * dec_s
+    packed = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
+    chunk = 16
+    with threadpool_limits(limits=1):
+        n_q = 0
+        t0 = time.perf_counter()
+        while n_q + chunk <= wl.used_slots.shape[0] and time.perf_counter() - t0 < budget_s / 4:
+            sl = wl.used_slots[n_q:n_q + chunk]
+            O.quantize_pages(wl.hot_pool, g, chunk, gs, packed, sl, sl)
+            n_q += chunk
+        q_s = time.perf_counter() - t0
+        back = np.zeros((chunk, *g.row_shape), np.uint16)
+        n_d = 0
+        t0 = time.perf_counter()
+        while n_d + chunk <= n_q and time.perf_counter() - t0 < budget_s / 4:
+            O.dequantize_pages(packed, g, chunk, gs, back, wl.used_slots[n_d:n_d + chunk], None)
+            n_d += chunk
+        dq_s = time.perf_counter() - t0
+        # attention reads the pages of each sampled sequence, encoded first
+        # (untimed: that is the encode leg's work)
+        tokens, seqs, dec_s = 0, 0, 0.0
+        while seqs < wl.batch and dec_s < budget_s / 2:
+            need = -(-int(wl.seq_lens[seqs]) // wl.page_size)
+            bslots = wl.block_table[seqs, :need]
+            O.quantize_pages(wl.hot_pool, g, need, gs, packed, bslots, bslots)
+            t0 = time.perf_counter()
+            A.decode_attention(packed, g, gs, wl.q, wl.block_table, wl.seq_lens,
+                               wl.softmax_scale, wl.v_dim, batch_indices=[seqs])
+            dec_s += time.perf_counter() - t0
+            tokens += int(wl.seq_lens[seqs])
+            seqs += 1
+    t_step = (step_unit_bytes["quantize"] / (n_q * per_page)) * q_s + \
+             (step_unit_bytes["dequantize"] / (n_d * per_page)) * dq_s + \
+             (step_unit_bytes["decode"] / (tokens * dec_bytes_per_token)) * dec_s
     return {"value": round(step_bytes / t_step / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": (f"oracle on 1 host thread: encode {pages} pages ({q_s:.2f} s), decode "
-                       f"{pages} pages ({dq_s:.2f} s), attention for sequence 0 "
-                       f"({int(wl.seq_lens[b])} tokens, all {wl.num_q_heads} q heads, "
-                       f"{dec_s:.2f} s); scaled to the step's bytes"),
-            "seconds": round(q_s + dq_s + dec_s, 3)}
+            "sample": (f"oracle (NumPy fp64) on 1 host thread: encode {n_q} pages ({q_s:.1f} s), "
+                       f"decode {n_d} pages ({dq_s:.1f} s), attention for {seqs} sequence(s) "
+                       f"({tokens} tokens, all {wl.num_q_heads} q heads, {dec_s:.1f} s); each leg "
+                       f"scaled to the step's bytes of that leg"),
+            "seconds": round(q_s + dq_s + dec_s, 2)}
 
 
 def main():
@@ -159,8 +175,10 @@ def main():
     pbytes = K.kvfp4_packed_page_bytes(geometry)
     packed = torch.zeros((num_slots, pbytes), dtype=torch.uint8, device=dev)
     hot_back = torch.empty_like(hot)
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
-    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
+    # fp32 in and out, so that the sum is one read-only reduction (an int32
+    # sum would first widen the whole buffer to int64 in a 2 GiB write)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def evict():
         # touch 1 GiB (4x the 256 MiB Infinity Cache) between timed kernels
@@ -214,10 +232,10 @@ def main():
     copy = None
     if not args.no_copy_yardstick:
         # a plain device-to-device copy of 1 GiB: reads 1 GiB and writes 1 GiB
-        src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src_c = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst_c = torch.empty_like(src_c)
         times = []
-        for i in range(4):
+        for i in range(COPY_CALLS):
             evict()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -227,8 +245,8 @@ def main():
             times.append((e0, e1))
         torch.cuda.synchronize()
         ms_c = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
-        copy = {"bytes": 2 << 30, "median_us": round(ms_c * 1e3, 2),
-                "GB/s": round((2 << 30) / (ms_c * 1e-3) / 1e9, 1)}
+        copy = {"bytes": 2 * COPY_BYTES, "median_us": round(ms_c * 1e3, 2),
+                "GB/s": round(2 * COPY_BYTES / (ms_c * 1e-3) / 1e9, 1)}
         del src_c, dst_c
 
     run(args.warmup, False)
@@ -262,8 +280,18 @@ def main():
     step_bytes = sum(leg_bytes.values())
     value = step_bytes / (step_ms * 1e-3) / 1e9
     dom = max(avg, key=avg.get)
-    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": None}
+    from nvfp4_paged_decode_amd.profiling import read_traffic
+    traffic = read_traffic(os.path.join(PROFILES, f"counters_{name}.txt"), name, dom)
+    if dom == "decode" and name == "mla":
+        # 128 query heads over one latent: a dense bf16 contraction (about
+        # 820 flop per cache byte), bound by MFMA throughput, not HBM
+        roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["TFLOP/s"],
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": kern[dom]["frac_bf16_mfma_peak"], "traffic": traffic}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB/s"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
+                "traffic": traffic}
 
     if wl is not None:
         nt, T, H, D = geometry
@@ -277,8 +305,8 @@ def main():
     cpu = None
     if wl is not None and not args.no_cpu_baseline:
         try:
-            cpu = cpu_baseline(wl, gs, args.cpu_sample_pages,
-                               db["bytes"] / float(wl.seq_lens.sum()), step_bytes, leg_bytes)
+            cpu = cpu_baseline(wl, gs, args.cpu_seconds, leg_bytes,
+                               db["bytes"] / float(wl.seq_lens.sum()), step_bytes)
         except Exception as e:  # the GPU figure stands on its own
             cpu = {"error": repr(e)}
 

@@ -1,0 +1,165 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Two commands, each printing a short text summary (to stdout or --out):
+
+  python -m nvfp4_paged_decode_amd.profiling stats DIR [--command TEXT]
+      per-kernel dispatch count and average/min/max duration from a
+      `rocprofv3 --kernel-trace --stats --output-format csv -d DIR` run.
+
+  python -m nvfp4_paged_decode_amd.profiling counters --fetch DIR --write DIR
+          --workload NAME --copy-bytes N [--command TEXT]
+      HBM traffic per dispatch from two `rocprofv3 --pmc` runs (FETCH_SIZE,
+      then WRITE_SIZE; both counters report KiB per dispatch).  Each counter
+      is scaled by what it reads for the plain device-to-device copies the
+      benchmark runs (`--copy-bytes` bytes read and as many written, summed
+      over every copy dispatch), so the result is in true bytes.  The
+      summary ends with one `traffic` line per benchmark leg, which bench.py
+      reads back together with the digest of the kernel sources the counters
+      were taken on (a figure for other sources is not reported).
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    n = re.sub(r"kvfp4::\(anonymous namespace\)::", "", name)
+    n = n.replace("void ", "")
+    if "copyBuffer" in n:
+        return "copyBuffer"
+    if "reduce_kernel" in n:
+        return "torch_reduce"
+    if "FillFunctor" in n:
+        return "torch_fill"
+    return n.split("(")[0].strip()
+
+
+def leg_of(kernel: str) -> str | None:
+    """Benchmark leg a kernel belongs to."""
+    if kernel.startswith("quantize_kernel"):
+        return "quantize"
+    if kernel.startswith("dequantize_kernel"):
+        return "dequantize"
+    if kernel.startswith(("decode_", "merge_")):
+        return "decode"
+    return None
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def stats(d: str) -> list[str]:
+    rows = list(csv.DictReader(open(_find(d, "kernel_stats.csv"))))
+    out = [f"{'kernel':<52} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'share%':>7}"]
+    for r in rows:
+        out.append(f"{short_name(r['Name'])[:52]:<52} {int(r['Calls']):>6} "
+                   f"{float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                   f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>7.2f}")
+    return out
+
+
+def _counter(d: str, counter: str) -> dict[str, list[float]]:
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return per
+
+
+def counters(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> list[str]:
+    fetch = _counter(fetch_dir, "FETCH_SIZE")
+    write = _counter(write_dir, "WRITE_SIZE")
+    if "copyBuffer" not in fetch or "copyBuffer" not in write:
+        raise SystemExit("no copy dispatches to calibrate against")
+    f_cal = copy_bytes / (1024.0 * sum(fetch["copyBuffer"]))
+    w_cal = copy_bytes / (1024.0 * sum(write["copyBuffer"]))
+    out = [f"calibration: {len(fetch['copyBuffer'])} copy dispatches moving {copy_bytes} B read "
+           f"+ {copy_bytes} B written read FETCH_SIZE {sum(fetch['copyBuffer']):.0f} KiB, "
+           f"WRITE_SIZE {sum(write['copyBuffer']):.0f} KiB",
+           f"scale: fetch x{f_cal:.4f}, write x{w_cal:.4f} (bytes per counter KiB / 1024)",
+           "",
+           f"{'kernel':<44} {'disp':>5} {'FETCH_KiB':>12} {'WRITE_KiB':>12} {'read_B':>14} {'written_B':>14}"]
+    legs = collections.defaultdict(lambda: [0.0, 0.0])
+    for k in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(k, [0.0]), write.get(k, [0.0])
+        fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
+        rb, wb = fa * 1024 * f_cal, wa * 1024 * w_cal
+        out.append(f"{k[:44]:<44} {len(fv):>5} {fa:>12.0f} {wa:>12.0f} {rb:>14.0f} {wb:>14.0f}")
+        leg = leg_of(k)
+        if leg:
+            legs[leg][0] += rb
+            legs[leg][1] += wb
+    out.append("")
+    digest = source_digest()
+    for leg, (rb, wb) in sorted(legs.items()):
+        out.append(f"traffic workload={workload} leg={leg} read_bytes={rb:.0f} "
+                   f"written_bytes={wb:.0f} total_bytes={rb + wb:.0f} sources={digest}")
+    return out
+
+
+def read_traffic(path: str, workload: str, leg: str) -> int | None:
+    """Total HBM bytes per call of `leg`, if `path` holds a figure taken on
+    the current kernel sources for this workload; else None."""
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    for line in open(path):
+        if not line.startswith("traffic "):
+            continue
+        kv = dict(p.split("=", 1) for p in line.split()[1:])
+        if kv.get("workload") == workload and kv.get("leg") == leg and kv.get("sources") == digest:
+            return int(kv["total_bytes"])
+    return None
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("--fetch", required=True)
+    c.add_argument("--write", required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--workload", required=True)
+    for q in (s, c):
+        q.add_argument("--command", default="", help="the command(s) that produced DIR")
+        q.add_argument("--out")
+    a = p.parse_args(argv)
+    lines = stats(a.dir) if a.cmd == "stats" else counters(a.fetch, a.write, a.copy_bytes, a.workload)
+    head = [f"# {l}" for l in a.command.splitlines() if l.strip()]
+    text = "\n".join(head + [""] + lines if head else lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
