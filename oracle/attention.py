@@ -15,7 +15,7 @@ definition
 for every (sequence, query head), with query head h reading KV head
 ``h // (num_q_heads // num_kv_heads)``.
 
-Readings (listed in the design doc): the query attends to exactly ``seq_lens[b]``
+Readings of what the pages leave open: the query attends to exactly ``seq_lens[b]``
 cached tokens, found through ``block_table[b][j // page_size]`` at row
 ``j % page_size``; with one KV tensor (MLA) the latent row is the key and its
 first ``v_dim`` elements are the value; ``seq_lens[b] == 0`` gives ``o = 0``

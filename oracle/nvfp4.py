@@ -8,7 +8,7 @@ packed codes plus one scale byte (same page, kernel section), i.e. 0.5625
 bytes per value ("KV Cache Compression in TensorRT LLM", Evaluation /
 Performance, Figure 10).
 
-Readings of what the pages leave open (each listed in the design doc):
+Readings of what the pages leave open:
 
 * E2M1 is the OCP 4-bit float: 1 sign, 2 exponent bits (bias 1), 1 mantissa
   bit, no inf/NaN; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Code bits are
