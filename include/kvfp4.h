@@ -130,8 +130,9 @@ size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,
  *   out           bf16 [batch][num_q_heads][v_dim]
  *   lse           float [batch][num_q_heads] natural-log LSE, or NULL;
  *                 seq_lens[b] == 0 gives out = 0 and lse = -inf.
- *   workspace     >= kvfp4_decode_workspace_bytes(...) bytes (may be NULL
- *                 when that is 0).
+ *   workspace     >= kvfp4_decode_workspace_bytes(...) bytes, 16-byte
+ *                 aligned (may be NULL when that is 0); its contents need no
+ *                 initialization and are scratch after the call.
  * num_q_heads must be a multiple of num_kv_heads. */
 int32_t kvfp4_paged_decode_attention(
     const kvfp4_geometry* g, const void* packed_pool, int32_t packed_pool_pages,

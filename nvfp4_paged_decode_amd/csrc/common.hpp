@@ -13,6 +13,7 @@ constexpr int kBlock = 16;  // values per NVFP4 block (one E4M3 scale each)
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Page geometry as the kernels see it.
 struct Geom {

@@ -184,23 +184,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   }
 }
 
+__device__ inline long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ inline uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Merge for the balanced kernels: sequence b's partials sit in slots
-// w + b for every workgroup w whose page range overlaps b's pages.
+// w + b for every workgroup w whose page range overlaps b's pages.  One
+// workgroup per (head, sequence); the page prefix over the batch is a
+// workgroup-wide sum, the output is read and written 4 columns per thread
+// when VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte aligned out).
+template <bool VEC>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
   const int head = blockIdx.x, b = blockIdx.y;
-  __shared__ long long s_tot, s_start;
-  if (threadIdx.x == 0) {
-    long long tot = 0, start = 0;
-    for (int i = 0; i < a.batch; ++i) {
-      int np = pages_of(a, i);
-      if (i < b) start += np;
-      tot += np;
-    }
-    s_tot = tot;
-    s_start = start;
+  __shared__ long long s_red[2][kMergeThreads / 64];
+  long long tot = 0, start = 0;
+  for (int i = threadIdx.x; i < a.batch; i += kMergeThreads) {
+    const long long np = pages_of(a, i);
+    tot += np;
+    if (i < b) start += np;
+  }
+  tot = wave_sum_ll(tot);
+  start = wave_sum_ll(start);
+  if ((threadIdx.x & 63) == 0) {
+    s_red[0][threadIdx.x >> 6] = tot;
+    s_red[1][threadIdx.x >> 6] = start;
   }
   __syncthreads();
-  const long long ptot = s_tot, first = s_start;
+  long long ptot = 0, first = 0;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) {
+    ptot += s_red[0][w];
+    first += s_red[1][w];
+  }
   const long long last = first + pages_of(a, b);
   const int nwg = a.nwg;
   float M = -INFINITY, Lsum = 0.f;
@@ -224,18 +246,34 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
     }
   }
   const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
-  for (int d = threadIdx.x; d < a.v_dim; d += kMergeThreads) {
-    float o = 0.f;
-    for (int v = w_lo; v <= w_hi; ++v) {
-      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
-      long long slot = ((long long)v + b) * a.hq + head;
-      float ms = a.ws_ml[slot * 2];
-      if (ms != -INFINITY) o += a.ws_o[slot * a.v_dim + d] * exp2f(ms - M);
+  const long long orow = ((long long)b * a.hq + head) * a.v_dim;
+  if (VEC) {
+    for (int d4 = threadIdx.x; d4 < a.v_dim / 4; d4 += kMergeThreads) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      for (int v = w_lo; v <= w_hi; ++v) {
+        if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
+        const long long slot = ((long long)v + b) * a.hq + head;
+        const float ms = a.ws_ml[slot * 2];
+        if (ms != -INFINITY)
+          o += *reinterpret_cast<const f32x4*>(a.ws_o + slot * a.v_dim + 4 * d4) * exp2f(ms - M);
+      }
+      o *= inv;
+      u32x2 w2;
+      w2.x = bf16_rne_bits(o.x) | (bf16_rne_bits(o.y) << 16);
+      w2.y = bf16_rne_bits(o.z) | (bf16_rne_bits(o.w) << 16);
+      *reinterpret_cast<u32x2*>(a.out + orow + 4 * d4) = w2;
     }
-    o *= inv;
-    uint32_t u = __float_as_uint(o);
-    uint32_t bf = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    a.out[((long long)b * a.hq + head) * a.v_dim + d] = (uint16_t)bf;
+  } else {
+    for (int d = threadIdx.x; d < a.v_dim; d += kMergeThreads) {
+      float o = 0.f;
+      for (int v = w_lo; v <= w_hi; ++v) {
+        if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
+        const long long slot = ((long long)v + b) * a.hq + head;
+        const float ms = a.ws_ml[slot * 2];
+        if (ms != -INFINITY) o += a.ws_o[slot * a.v_dim + d] * exp2f(ms - M);
+      }
+      a.out[orow + d] = (uint16_t)bf16_rne_bits(o * inv);
+    }
   }
   if (threadIdx.x == 0 && a.lse) {
     float v = (Lsum > 0.f) ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
@@ -304,8 +342,14 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   if (plan.kernel == 0) {
     hipLaunchKernelGGL(merge_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(merge_balanced_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0,
-                       stream, a);
+    const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_o & 15) == 0 &&
+                     ((uintptr_t)a.out & 7) == 0;
+    if (vec)
+      hipLaunchKernelGGL(merge_balanced_kernel<true>, dim3(a.hq, a.batch), dim3(kMergeThreads),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_balanced_kernel<false>, dim3(a.hq, a.batch), dim3(kMergeThreads),
+                         0, stream, a);
   }
   return hipGetLastError();
 }
