@@ -121,7 +121,7 @@ size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,
  * token j living in slot block_table[b][j / T], row j % T.
  *   packed_pool   [packed_pool_pages][9*E/16 bytes]
  *   global_scale  HOST float [num_kv_tensors] (K, V; MLA: one)
- *   q             bf16 [batch][num_q_heads][head_dim]
+ *   q             bf16 [batch][num_q_heads][head_dim], 16-byte aligned
  *   v_dim         == head_dim when num_kv_tensors == 2; <= head_dim for MLA
  *   block_table   int32 [batch][max_pages_per_seq]
  *   seq_lens      int32 [batch]; each <= max_seq_len_hint and

@@ -210,6 +210,8 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
                 plan.workspace_bytes);
   if (plan.workspace_bytes > 0 && ((uintptr_t)workspace & 15) != 0)
     return fail(KVFP4_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (((uintptr_t)q & 15) != 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "q must be 16-byte aligned");
   kvfp4::DecodeArgs a{};
   a.g = geom;
   a.pool = (const uint8_t*)packed_pool;

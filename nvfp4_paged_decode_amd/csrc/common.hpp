@@ -140,7 +140,7 @@ struct DecodeArgs {
 
 // Which decode kernel a shape uses, and how it splits the context.
 struct DecodePlan {
-  int kernel;            // 0 = generic, 1 = GQA VALU, 2 = MLA MFMA
+  int kernel;            // 0 = generic, 1 = GQA VALU, 2 = MLA MFMA, 3 = GQA MFMA
   int splits;            // generic kernel
   int pages_per_split;   // generic kernel
   int nwg;               // balanced kernels

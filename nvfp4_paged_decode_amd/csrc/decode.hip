@@ -20,7 +20,9 @@ namespace kvfp4 {
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream);
 bool gqa_supported(const Geom& g, int hq, int v_dim);
+bool gqa_mfma_supported(const Geom& g, int hq, int v_dim);
 bool mla_supported(const Geom& g, int hq, int v_dim);
 
 namespace {
@@ -195,26 +197,59 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ inline float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kMergeChunk = 512;  // partial weights staged in LDS per pass
+
 // Merge for the balanced kernels: sequence b's partials sit in slots
 // w + b for every workgroup w whose page range overlaps b's pages.  One
-// workgroup per (head, sequence); the page prefix over the batch is a
-// workgroup-wide sum, the output is read and written 4 columns per thread
-// when VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte aligned out).
+// workgroup per (head, sequence).  The page prefix over the batch, the
+// running maximum and the weight sum are workgroup-wide reductions over
+// the slots; the weights of up to kMergeChunk slots at a time sit in LDS.
+// Output: with VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte
+// aligned out) a thread owns 4 columns of one group of slots (slot index
+// mod G, G = threads / (v_dim / 4) groups when v_dim is small), the groups
+// are summed through LDS; otherwise one column per thread.
 template <bool VEC>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
-  const int head = blockIdx.x, b = blockIdx.y;
+  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ long long s_red[2][kMergeThreads / 64];
+  __shared__ float s_f[kMergeThreads / 64];
+  __shared__ float s_wt[kMergeChunk];
+  __shared__ f32x4 s_acc[kMergeThreads];
   long long tot = 0, start = 0;
-  for (int i = threadIdx.x; i < a.batch; i += kMergeThreads) {
+  for (int i = tid; i < a.batch; i += kMergeThreads) {
     const long long np = pages_of(a, i);
     tot += np;
     if (i < b) start += np;
   }
   tot = wave_sum_ll(tot);
   start = wave_sum_ll(start);
-  if ((threadIdx.x & 63) == 0) {
-    s_red[0][threadIdx.x >> 6] = tot;
-    s_red[1][threadIdx.x >> 6] = start;
+  if ((tid & 63) == 0) {
+    s_red[0][tid >> 6] = tot;
+    s_red[1][tid >> 6] = start;
   }
   __syncthreads();
   long long ptot = 0, first = 0;
@@ -225,59 +260,114 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
   }
   const long long last = first + pages_of(a, b);
   const int nwg = a.nwg;
-  float M = -INFINITY, Lsum = 0.f;
   int w_lo = 0, w_hi = -1;
   if (last > first) {
-    // first workgroup whose range ends after `first`
+    // first workgroup whose range ends after `first`, last one starting before `last`
     int w = (int)(first * nwg / ptot);
     while (w > 0 && range_begin(ptot, w, nwg) > first) --w;
     while (range_begin(ptot, w + 1, nwg) <= first) ++w;
     w_lo = w;
-    w_hi = w;
-    while (w_hi + 1 < nwg && range_begin(ptot, w_hi + 1, nwg) < last) ++w_hi;
-    for (int v = w_lo; v <= w_hi; ++v) {
-      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;  // empty range
-      M = fmaxf(M, a.ws_ml[(((long long)v + b) * a.hq + head) * 2]);
-    }
-    for (int v = w_lo; v <= w_hi; ++v) {
-      if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
-      float ms = a.ws_ml[(((long long)v + b) * a.hq + head) * 2];
-      if (ms != -INFINITY) Lsum += a.ws_ml[(((long long)v + b) * a.hq + head) * 2 + 1] * exp2f(ms - M);
-    }
+    int hi = (int)(last * nwg / ptot);
+    if (hi < w_lo) hi = w_lo;
+    if (hi > nwg - 1) hi = nwg - 1;
+    while (hi > w_lo && range_begin(ptot, hi, nwg) >= last) --hi;
+    while (hi + 1 < nwg && range_begin(ptot, hi + 1, nwg) < last) ++hi;
+    w_hi = hi;
   }
-  const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
-  const long long orow = ((long long)b * a.hq + head) * a.v_dim;
-  if (VEC) {
-    for (int d4 = threadIdx.x; d4 < a.v_dim / 4; d4 += kMergeThreads) {
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-      for (int v = w_lo; v <= w_hi; ++v) {
-        if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
-        const long long slot = ((long long)v + b) * a.hq + head;
-        const float ms = a.ws_ml[slot * 2];
-        if (ms != -INFINITY)
-          o += *reinterpret_cast<const f32x4*>(a.ws_o + slot * a.v_dim + 4 * d4) * exp2f(ms - M);
+  const long long row = (long long)b * a.hq + head;
+  // a slot holds a partial only if its workgroup's range is not empty
+  auto ms_of = [&](int v) -> float {
+    if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) return -INFINITY;
+    return a.ws_ml[(((long long)v + b) * a.hq + head) * 2];
+  };
+  float M = -INFINITY;
+  for (int v = w_lo + tid; v <= w_hi; v += kMergeThreads) M = fmaxf(M, ms_of(v));
+  M = block_max(M, s_f);
+
+  const int D4 = a.v_dim / 4;
+  const int G = VEC ? (D4 >= kMergeThreads ? 1 : kMergeThreads / D4) : 1;
+  const int grp = VEC ? tid / (D4 >= kMergeThreads ? kMergeThreads : D4) : 0;
+  const int d4 = VEC ? (D4 >= kMergeThreads ? tid : tid % D4) : tid;
+  f32x4 o4[(kMaxD / 4 + kMergeThreads - 1) / kMergeThreads];  // VEC: columns d4 + k*threads
+  float o1[(kMaxD + kMergeThreads - 1) / kMergeThreads];      // scalar: columns tid + k*threads
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) o4[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) o1[k] = 0.f;
+  float Lpart = 0.f;
+  for (int c0 = w_lo; c0 <= w_hi; c0 += kMergeChunk) {
+    const int cn = (w_hi - c0 + 1) < kMergeChunk ? (w_hi - c0 + 1) : kMergeChunk;
+    for (int i = tid; i < cn; i += kMergeThreads) {
+      const float ms = ms_of(c0 + i);
+      float wt = 0.f;
+      if (ms != -INFINITY) {
+        wt = exp2f(ms - M);
+        Lpart += wt * a.ws_ml[(((long long)c0 + i + b) * a.hq + head) * 2 + 1];
       }
-      o *= inv;
-      u32x2 w2;
-      w2.x = bf16_rne_bits(o.x) | (bf16_rne_bits(o.y) << 16);
-      w2.y = bf16_rne_bits(o.z) | (bf16_rne_bits(o.w) << 16);
-      *reinterpret_cast<u32x2*>(a.out + orow + 4 * d4) = w2;
+      s_wt[i] = wt;
+    }
+    __syncthreads();
+    if (VEC) {
+      if (grp < G) {
+        for (int i = grp; i < cn; i += G) {
+          const float wt = s_wt[i];
+          if (wt == 0.f) continue;
+          const float* src = a.ws_o + (((long long)c0 + i + b) * a.hq + head) * a.v_dim;
+#pragma unroll
+          for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) {
+            const int c = d4 + k * kMergeThreads;
+            if (c < D4) o4[k] += *reinterpret_cast<const f32x4*>(src + 4 * c) * wt;
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < cn; ++i) {
+        const float wt = s_wt[i];
+        if (wt == 0.f) continue;
+        const float* src = a.ws_o + (((long long)c0 + i + b) * a.hq + head) * a.v_dim;
+#pragma unroll
+        for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) {
+          const int c = tid + k * kMergeThreads;
+          if (c < a.v_dim) o1[k] += src[c] * wt;
+        }
+      }
+    }
+    __syncthreads();  // s_wt is rewritten by the next chunk
+  }
+  const float Lsum = block_sum(Lpart, s_f);
+  const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
+  if (VEC) {
+    if (G > 1) {
+      // sum the G slot groups of each column block (D4 < threads: one k)
+      s_acc[tid] = o4[0];
+      __syncthreads();
+      if (tid < D4) {
+        f32x4 t = s_acc[tid];
+        for (int gg = 1; gg < G; ++gg) t += s_acc[gg * D4 + tid];
+        o4[0] = t;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) {
+      const int c = d4 + k * kMergeThreads;
+      if (grp == 0 && c < D4) {
+        const f32x4 o = o4[k] * inv;
+        u32x2 w2;
+        w2.x = bf16_rne_bits(o.x) | (bf16_rne_bits(o.y) << 16);
+        w2.y = bf16_rne_bits(o.z) | (bf16_rne_bits(o.w) << 16);
+        *reinterpret_cast<u32x2*>(a.out + row * a.v_dim + 4 * c) = w2;
+      }
     }
   } else {
-    for (int d = threadIdx.x; d < a.v_dim; d += kMergeThreads) {
-      float o = 0.f;
-      for (int v = w_lo; v <= w_hi; ++v) {
-        if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) continue;
-        const long long slot = ((long long)v + b) * a.hq + head;
-        const float ms = a.ws_ml[slot * 2];
-        if (ms != -INFINITY) o += a.ws_o[slot * a.v_dim + d] * exp2f(ms - M);
-      }
-      a.out[orow + d] = (uint16_t)bf16_rne_bits(o * inv);
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) {
+      const int c = tid + k * kMergeThreads;
+      if (c < a.v_dim) a.out[row * a.v_dim + c] = (uint16_t)bf16_rne_bits(o1[k] * inv);
     }
   }
-  if (threadIdx.x == 0 && a.lse) {
+  if (tid == 0 && a.lse) {
     float v = (Lsum > 0.f) ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
-    a.lse[(long long)b * a.hq + head] = v;
+    a.lse[row] = v;
   }
 }
 
@@ -296,10 +386,11 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
     p.workspace_bytes = 0;
     return p;
   }
-  if (mla_supported(g, hq, v_dim) || gqa_supported(g, hq, v_dim)) {
+  if (mla_supported(g, hq, v_dim) || gqa_mfma_supported(g, hq, v_dim) ||
+      gqa_supported(g, hq, v_dim)) {
     // balanced kernels: one workgroup per CU (or per page when fewer); the
     // MLA kernel runs two per CU and splits 128 heads over two workgroups
-    p.kernel = mla_supported(g, hq, v_dim) ? 2 : 1;
+    p.kernel = mla_supported(g, hq, v_dim) ? 2 : gqa_mfma_supported(g, hq, v_dim) ? 3 : 1;
     long long target = cus;
     if (p.kernel == 2) target = 2LL * cus / (hq > 64 ? hq / 64 : 1);
     long long pages_ub = (long long)batch * pages_max;
@@ -327,7 +418,9 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   hipError_t e;
-  if (plan.kernel == 2) {
+  if (plan.kernel == 3) {
+    e = launch_decode_gqa_mfma(a, stream);
+  } else if (plan.kernel == 2) {
     e = launch_decode_mla(a, stream);
   } else if (plan.kernel == 1) {
     e = launch_decode_gqa(a, stream);

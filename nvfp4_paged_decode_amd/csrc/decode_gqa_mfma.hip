@@ -1,0 +1,466 @@
+// Paged NVFP4 decode attention for query groups of 4 (head_dim 128, 4 to 32
+// KV heads, pages a multiple of 16 tokens) on MFMA.
+//
+// "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+// NVFP4 KV Decode Attention Kernel Implementation / Figure 3: packed K/V
+// tiles and their E4M3 block scales are read from the cache, unpacked and
+// scaled in registers, both attention products run as 16-bit matrix
+// products with fp32 accumulation, and the tensor scales act as scalars.
+// Decode is memory-read-bound (same page, Path 3: Decode): the kernel is
+// built so that its per-value instruction count stays well under what
+// streaming the cache at full HBM rate leaves.
+//
+// Why MFMA with 4 query heads.  On VALU every cached value costs one FMA
+// per query head (4 per value) on top of its dequantization, which keeps
+// the VALU busy for longer than HBM takes to deliver the bytes.  Here a
+// wave takes 4 KV heads at once and places them block-diagonally in one
+// v_mfma_f32_16x16x32_f16: the 32-long contraction is 4 KV heads x 8
+// values, and the 16 output columns are those 4 KV heads x their 4 query
+// heads, so every output column is a real query head.
+//
+// 16-bit format.  E2M1 x E4M3 has at most 6 significant bits and lies in
+// [2^-10, 2688]: exact in fp16 (normal range), so the dequantized values
+// are exact; gfx950 converts E2M1 codes exactly to fp16 pairs
+// (v_cvt_scalef32_pk_f16_fp4 with scale 1.0) and one v_pk_mul_f16 applies
+// the block scale to two values.  Queries (bf16) are scaled per head by a
+// power of two so that their largest magnitude sits just under 2^15, then
+// converted to fp16: bf16's 8-bit significands fit fp16's 11, so the only
+// loss is for elements 2^-39 of the head's largest or smaller.  The power
+// of two is undone on the fp32 scores.  Probabilities are rounded to fp16
+// (11 significant bits) for the P.V product.
+//
+// Per 16-token tile of a wave (4 KV heads):
+//   scores   S^T = K Q^T: A = K, lane (token t, KV head g) dequantizes its
+//            own 64-byte row, 8 values per k-step; B = Q^T block-diagonal
+//            (lane (column c, group g) holds query c's 8 values when g is
+//            c's KV head, else 0), kept in registers per sequence.  Lane
+//            (c, g) receives rows 4g..4g+3 of column c.
+//   softmax  online per column, running max shared by the column's 4
+//            lanes, lazy rescale of the accumulators only when it grows.
+//   P.V      O^T = V^T P^T.  V rows are dequantized by the same lanes and
+//            staged in LDS in their natural [KV head][token][dim] order;
+//            ds_read_b64_tr_b16 reads them transposed (4 tokens of one dim
+//            per lane).  Two products per 16 dims: the k-group of KV head
+//            g takes tokens 4x..4x+3 and 4y..4y+3 (x, y = g + 2m, g + 2m
+//            + 1, mod 4, m = 0, 1), whose probabilities sit in lanes
+//            (c, x), (c, y) and are fetched with ds_bpermute.
+//
+// Workgroup: 8 waves = (H/4 groups of 4 KV heads) x (8/(H/4) token
+// streams); stream s takes tiles s, s + NS, ... of each sequence segment.
+// The balanced split of decode_plan.hpp gives each workgroup a contiguous
+// range of the batch's pages; at the end of each sequence segment the
+// streams are merged through LDS and the partial goes to workspace slot
+// (workgroup + sequence) for merge_balanced_kernel.
+#include "common.hpp"
+#include "decode_plan.hpp"
+
+namespace kvfp4 {
+
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;       // head dim
+constexpr int kTile = 16;     // tokens per tile
+constexpr int kWaves = 8;     // waves per workgroup
+constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords, so the
+                                 // transposed reads of a 32-lane half hit 64
+                                 // distinct banks
+constexpr float kNoMax = -1e30f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct StageLds {
+  _Float16 v[kWaves][4][kTile][kPitch];  // per wave: 4 KV heads x 16 tokens
+};
+struct MergeLds {
+  float o[kWaves][16][kD];   // per wave: 16 query heads x 128 dims
+  float ml[kWaves][16][2];   // running max and sum per query head
+};
+constexpr size_t kLdsBytes = sizeof(StageLds) > sizeof(MergeLds) ? sizeof(StageLds)
+                                                                  : sizeof(MergeLds);
+
+// One lane's packed share of a tile: its 64-byte K row and V row and
+// their 8 scale bytes each.
+struct Packed {
+  u32x4 k[4], v[4];
+  u32x2 ks, vs;
+};
+
+__device__ inline f16x2 fp4x2(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+// The 8 block scales of a row (E4M3 bytes) as fp16 pairs (exact).
+__device__ inline void scales8(u32x2 s, f16x2 (&o)[4]) {
+  o[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.x, 1.0f, false);
+  o[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.x, 1.0f, true);
+  o[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.y, 1.0f, false);
+  o[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.y, 1.0f, true);
+}
+
+// 8 values of dword w (dims 8i..8i+7 of a row) times their block scale.
+__device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
+  const f16x2 s2 = {sb, sb};
+  const f16x2 a = fp4x2(w, 0) * s2, b = fp4x2(w, 1) * s2;
+  const f16x2 c = fp4x2(w, 2) * s2, d = fp4x2(w, 3) * s2;
+  return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ inline _Float16 block_scale(const f16x2 (&s)[4], int blk) {
+  return (blk & 1) ? s[blk >> 1].y : s[blk >> 1].x;
+}
+
+__device__ inline uint32_t bperm(uint32_t v, int src_lane) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+__device__ inline uint32_t pack_f16(float a, float b) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ inline f16x4 lds_read_tr(const _Float16* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, r);
+}
+
+// 8 bf16 of a query row (rows are 16-byte aligned: checked at launch).
+__device__ inline u32x4 load_q8(const uint16_t* row, int i) {
+  return *reinterpret_cast<const u32x4*>(row + 8 * i);
+}
+
+// Issues the loads of one lane's share of tile `ti` of a sequence; rows
+// past the sequence end (or a whole tile of a bad page) come back as zero
+// from the buffer resources' bounds, and are never fetched.
+struct TileGeom {
+  const uint8_t* pool;
+  long long page_bytes;
+  int pool_pages, T, H, L, tiles_per_page;
+  uint32_t off_data, off_scale;  // this lane's row offsets in a tile
+};
+
+__device__ inline int tile_rows(const TileGeom& tg, int slot, long long ti) {
+  int n = tg.L - (int)(ti * kTile);
+  n = n > kTile ? kTile : n;
+  if (slot < 0 || slot >= tg.pool_pages) n = 0;
+  return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
+}
+
+__device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long long ti, int n) {
+  const int row0 = (int)(ti % tg.tiles_per_page) * kTile;
+  const int rowb = tg.H * (kD / 2), rows = tg.H * (kD / 16);
+  const uint8_t* page = tg.pool + (long long)(n > 0 ? slot : 0) * tg.page_bytes;
+  const uint8_t* kd = page + (long long)row0 * rowb;
+  const uint8_t* vd = page + (long long)tg.T * rowb + (long long)row0 * rowb;
+  const uint8_t* kss = page + 2LL * tg.T * rowb + (long long)row0 * rows;
+  const uint8_t* vss = kss + (long long)tg.T * rows;
+  auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)kd, (short)0, n * rowb, 0x00020000);
+  auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vd, (short)0, n * rowb, 0x00020000);
+  auto rks = __builtin_amdgcn_make_buffer_rsrc((void*)kss, (short)0, n * rows, 0x00020000);
+  auto rvs = __builtin_amdgcn_make_buffer_rsrc((void*)vss, (short)0, n * rows, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tg.off_data + 16 * j, 0, 0));
+    p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tg.off_data + 16 * j, 0, 0));
+  }
+  p.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, 0));
+  p.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, 0));
+}
+
+template <int NKG>
+__global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  constexpr int NS = kWaves / NKG;  // token streams per KV-head group
+  extern __shared__ __align__(16) unsigned char smem[];
+  StageLds& st = *reinterpret_cast<StageLds*>(smem);
+  MergeLds& mg = *reinterpret_cast<MergeLds*>(smem);
+  const Geom g = a.g;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int kg = wave / NS, s = wave % NS;
+  const int lr = lane & 15, lg = lane >> 4;   // MFMA row/column, k-group
+  const bool diag = (lr >> 2) == lg;          // column lr's KV head is group lg
+  const int w = blockIdx.x, nwg = gridDim.x;
+  const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
+
+  TileGeom tg;
+  tg.pool = a.pool;
+  tg.page_bytes = g.packed_bytes();
+  tg.pool_pages = a.pool_pages;
+  tg.T = g.T;
+  tg.H = g.H;
+  tg.tiles_per_page = g.T / kTile;
+  tg.off_data = (uint32_t)((lr * g.H + 4 * kg + lg) * (kD / 2));
+  tg.off_scale = (uint32_t)((lr * g.H + 4 * kg + lg) * (kD / 16));
+
+  // transposed-read addresses: lane (q = (lane&15)>>2, j = lane&3) of
+  // k-group lg points at row 4x + q, dims 4j.. of KV head lg
+  _Float16* vw = &st.v[wave][lg][0][0];
+  const int q4 = (lr >> 2), j4 = lr & 3;
+  const _Float16* tr_base[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int x = (lg + 2 * m) & 3, y = (lg + 2 * m + 1) & 3;
+    tr_base[m][0] = vw + (4 * x + q4) * kPitch + 4 * j4;
+    tr_base[m][1] = vw + (4 * y + q4) * kPitch + 4 * j4;
+  }
+  const int src_x1 = lr + 16 * ((lg + 1) & 3);
+  const int src_x2 = lr + 16 * ((lg + 2) & 3);
+  const int src_x3 = lr + 16 * ((lg + 3) & 3);
+
+  BalancedRange rng;
+  balanced_range(a, w, nwg, rng);
+  long long seq_start = rng.start_first;
+  for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
+    const int L = uniform(clamped_len(a, b));
+    const int npages = (L + g.T - 1) / g.T;
+    const long long first = seq_start;
+    seq_start += npages;
+    const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
+    const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
+    if (p_lo >= p_hi) continue;
+    tg.L = L;
+    const long long t_lo = p_lo * tg.tiles_per_page;
+    long long t_hi = p_hi * tg.tiles_per_page;
+    const long long t_end = (L + kTile - 1) / kTile;
+    if (t_hi > t_end) t_hi = t_end;
+
+    // queries of this wave's 16 heads as the block-diagonal B operand
+    const int head = 16 * kg + lr;
+    f16x8 qb[16];
+    int sh = 0;
+    {
+      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * kD;
+      if (diag) {
+        // largest magnitude from the bf16 bit patterns, then a power of two
+        // that puts it in [2^14, 2^15)
+        uint32_t mb = 0;
+        for (int i = 0; i < kD / 8; ++i) {
+          const u32x4 raw = load_q8(qrow, i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mb = max(mb, raw[e] & 0x7FFFu);
+            mb = max(mb, (raw[e] >> 16) & 0x7FFFu);
+          }
+        }
+        if (mb != 0) {
+          int e;
+          frexpf(__uint_as_float(mb << 16), &e);  // amax < 2^e
+          sh = 15 - e;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (diag) raw = load_q8(qrow, i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[e] << 16), sh);
+          qb[i][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[e] & 0xFFFF0000u), sh);
+        }
+      }
+    }
+    // score scale of column lr: the shift lives in lane (lr, lr / 4)
+    const int sh_c = __shfl(sh, lr + 16 * (lr >> 2));
+    const float qs = ldexpf(base_scale, -sh_c);
+
+    f32x4 acc[kD / 16];
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = kNoMax, l = 0.f;
+
+    // page-table entries of pages c0 .. c0+63, one per lane
+    const int32_t* bt_row = a.block_table + (long long)b * a.max_pages;
+    long long c0 = -(1LL << 40);  // no window loaded yet
+    int slot_vec = -1;
+    auto slot_of = [&](long long ti) -> int {
+      const long long pg = ti / tg.tiles_per_page;
+      if (pg < c0 || pg >= c0 + 64) {
+        c0 = pg;
+        slot_vec = (c0 + lane < p_hi) ? bt_row[c0 + lane] : -1;
+      }
+      return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
+    };
+
+    long long ti = t_lo + s;
+    Packed cur, nxt;
+    int n_cur = 0, n_nxt = 0;
+    if (ti < t_hi) {
+      const int sl = slot_of(ti);
+      n_cur = tile_rows(tg, sl, ti);
+      load_tile(cur, tg, sl, ti, n_cur);
+    }
+    for (; ti < t_hi; ti += NS) {
+      const long long tn = ti + NS;
+      if (tn < t_hi) {
+        const int sl = slot_of(tn);
+        n_nxt = tile_rows(tg, sl, tn);
+        load_tile(nxt, tg, sl, tn, n_nxt);
+      }
+
+      // V rows -> LDS (natural layout), dequantized once
+      {
+        f16x2 vsc[4];
+        scales8(cur.vs, vsc);
+        _Float16* dst = vw + lr * kPitch;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<f16x8*>(dst + 32 * j + 8 * e) =
+                dequant8(cur.v[j][e], block_scale(vsc, (4 * j + e) >> 1));
+      }
+
+      // scores S^T[token][column]
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      {
+        f16x2 ksc[4];
+        scales8(cur.ks, ksc);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const f16x8 ka = dequant8(cur.k[ks >> 2][ks & 3], block_scale(ksc, ks >> 1));
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sc, 0, 0, 0);
+        }
+      }
+
+      // online softmax of column lr over rows 4 lg + r
+      float sv[4];
+      float mx = kNoMax;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = (4 * lg + r < n_cur) ? sc[r] * qs : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m) != 0, 0)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 16; ++dt) acc[dt] *= alpha;
+        m = mn;
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+        l += p[r];
+      }
+      const uint32_t pw0 = pack_f16(p[0], p[1]), pw1 = pack_f16(p[2], p[3]);
+
+      // P^T operands: m = 0 takes groups (lg, lg+1), m = 1 (lg+2, lg+3)
+      const uint32_t a1 = bperm(pw0, src_x1), b1 = bperm(pw1, src_x1);
+      const uint32_t a2 = bperm(pw0, src_x2), b2 = bperm(pw1, src_x2);
+      const uint32_t a3 = bperm(pw0, src_x3), b3 = bperm(pw1, src_x3);
+      const u32x4 pb0 = diag ? (u32x4){pw0, pw1, a1, b1} : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 pb1 = diag ? (u32x4){a2, b2, a3, b3} : (u32x4){0u, 0u, 0u, 0u};
+      const f16x8 pbm[2] = {__builtin_bit_cast(f16x8, pb0), __builtin_bit_cast(f16x8, pb1)};
+
+      // the V rows written above are read back by other lanes of this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      // O^T[dim][column] += V^T P^T
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int dt = 0; dt < kD / 16; ++dt) {
+          const f16x4 lo = lds_read_tr(tr_base[mm][0] + 16 * dt);
+          const f16x4 hi = lds_read_tr(tr_base[mm][1] + 16 * dt);
+          const f16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pbm[mm], acc[dt], 0, 0, 0);
+        }
+      // the next tile's V rows overwrite these only after every lane's reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+      cur = nxt;
+      n_cur = n_nxt;
+    }
+
+    // merge the NS streams of each KV-head group, then write the partial
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    __syncthreads();  // every wave is done with its staged V rows
+#pragma unroll
+    for (int dt = 0; dt < kD / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mg.o[wave][lr][16 * dt + 4 * lg + r] = acc[dt][r];
+    if (lg == 0) {
+      mg.ml[wave][lr][0] = m;
+      mg.ml[wave][lr][1] = l;
+    }
+    __syncthreads();
+    {
+      // wave (kg, s) finishes dims [s * 128/NS, (s+1) * 128/NS) of its group
+      constexpr int DW = kD / NS, DL = DW / 4;  // dims per wave, per lane
+      float M = kNoMax;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) M = fmaxf(M, mg.ml[kg * NS + u][lr][0]);
+      float wt[NS], Ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        wt[u] = __builtin_amdgcn_exp2f(mg.ml[kg * NS + u][lr][0] - M);
+        Ls += wt[u] * mg.ml[kg * NS + u][lr][1];
+      }
+      const long long slotp = ((long long)w + b) * a.hq + head;
+      const int d0 = s * DW + lg * DL;
+#pragma unroll
+      for (int i = 0; i < DL; i += 4) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NS; ++u)
+          o += *reinterpret_cast<const f32x4*>(&mg.o[kg * NS + u][lr][d0 + i]) * wt[u];
+        *reinterpret_cast<f32x4*>(a.ws_o + slotp * kD + d0 + i) = o;
+      }
+      if (s == 0 && lg == 0) {
+        a.ws_ml[slotp * 2] = M;
+        a.ws_ml[slotp * 2 + 1] = Ls;
+      }
+    }
+    __syncthreads();  // the merge area is staged V rows again next segment
+  }
+}
+
+template <int NKG>
+hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_mfma_kernel<NKG>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_gqa_mfma_kernel<NKG>), dim3(a.nwg), dim3(64 * kWaves), kLdsBytes,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
+  if (g.nt != 2 || g.D != kD || v_dim != kD) return false;
+  if (g.T % kTile != 0 || g.T > 4096) return false;
+  if (!(g.H == 4 || g.H == 8 || g.H == 16 || g.H == 32)) return false;
+  return hq == 4 * g.H;
+}
+
+hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
+  if (!gqa_mfma_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
+  if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
+  switch (a.g.H) {
+    case 4: return launch_nkg<1>(a, stream);
+    case 8: return launch_nkg<2>(a, stream);
+    case 16: return launch_nkg<4>(a, stream);
+    default: return launch_nkg<8>(a, stream);
+  }
+}
+
+}  // namespace kvfp4

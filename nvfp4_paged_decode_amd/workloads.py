@@ -145,6 +145,24 @@ def _decode_workload(name, seed, *, nt, T, H, D, B, Hq, v_dim, lens_fn, kv_fn,
                           used, poison_slot)
 
 
+def geometry_case(seed: int, *, nt: int, T: int, H: int, D: int, Hq: int, v_dim: int,
+                  lens) -> DecodeWorkload:
+    """A small decode workload of any page geometry: N(0, 1) K/V (or latent)
+    and queries, the given sequence lengths, pages in a seeded permutation.
+    For covering every kernel a shape can be routed to."""
+    lens = np.asarray(lens, dtype=np.int64)
+
+    def lens_fn(rng):
+        return int(lens.max()) if rng is None else lens
+
+    def kv(rng, slots):
+        return _normal_bf16(rng, (slots, nt, T, H, D))
+
+    return _decode_workload(f"geom_nt{nt}_T{T}_H{H}_D{D}_Hq{Hq}", seed, nt=nt, T=T, H=H, D=D,
+                            B=len(lens), Hq=Hq, v_dim=v_dim, lens_fn=lens_fn, kv_fn=kv,
+                            softmax_scale=1.0 / np.sqrt(float(D)))
+
+
 def tiny(seed: int = 1) -> DecodeWorkload:
     """1 sequence, 1 KV head, 4 query heads, head_dim 128, 256 tokens, page 16."""
     def lens(rng):

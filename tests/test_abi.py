@@ -118,6 +118,7 @@ def _decode(lib, g, gs=(1.0, 1.0), batch=2, hq=32, v_dim=128, hint=1024, ws=0, w
     (dict(gs=(1.0, 0.0)), K.KVFP4_ERR_INVALID_ARG),
     (dict(ws=0), K.KVFP4_ERR_WORKSPACE),          # workspace too small
     (dict(ws=1 << 30, wsptr=FAKE + 4), K.KVFP4_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(ws=1 << 30, wsptr=FAKE, q=FAKE + 2), K.KVFP4_ERR_INVALID_ARG),  # misaligned q
     (dict(g=K.Geometry(2, 64, 8, 640), v_dim=640), K.KVFP4_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_invalid_arguments(lib, case, code):

@@ -89,6 +89,56 @@ def test_decode_hint_larger_than_lengths():
     check(wl, gs, packed, out, lse, what="large hint")
 
 
+# (nt, T, H, D, Hq, v_dim): every decode kernel and its template variants
+GEOMETRIES = {
+    "mfma_gqa_T16_H4": (2, 16, 4, 128, 16, 128),
+    "mfma_gqa_T32_H16": (2, 32, 16, 128, 64, 128),
+    "mfma_gqa_T128_H32": (2, 128, 32, 128, 128, 128),
+    "valu_gqa_G1_H8": (2, 64, 8, 128, 8, 128),
+    "valu_gqa_G2_H2": (2, 32, 2, 128, 4, 128),
+    "valu_gqa_G4_H2": (2, 16, 2, 128, 8, 128),
+    "generic_G3_D64_T8": (2, 8, 2, 64, 6, 64),
+    "generic_D256": (2, 64, 1, 256, 4, 256),
+    "generic_mla_v448": (1, 32, 1, 576, 8, 448),
+    "mla_32_heads_T64": (1, 64, 1, 576, 32, 512),
+    "mla_64_heads_T256": (1, 256, 1, 576, 64, 512),
+}
+
+
+@pytest.mark.parametrize("name", list(GEOMETRIES))
+def test_decode_geometries(name):
+    """Ragged lengths (one token, a partial first tile, page multiples and
+    a partial last page) for each kernel the shape routes to."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = GEOMETRIES[name]
+    lens = [1, 17, 2 * T, 3 * T + 5, 300]
+    wl = W.geometry_case(40 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=name)
+
+
+def test_decode_unaligned_output():
+    """An output buffer that is only 2-byte aligned takes the merge's
+    one-column-per-thread path; results are the same."""
+    require_gpu()
+    wl = W.llama3_8b(seed=19, batch=3, context=200)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    B, Hq = wl.batch, wl.num_q_heads
+    hint = int(wl.seq_lens.max())
+    ws_bytes = K.kvfp4_decode_workspace_bytes(wl.geometry, B, Hq, wl.v_dim, hint)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    flat = torch.empty(B * Hq * wl.v_dim + 1, dtype=torch.int16, device="cuda")
+    out = flat[1:].view(B, Hq, wl.v_dim)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    K.kvfp4_paged_decode_attention(wl.geometry, dev(packed), gs, dev(wl.q.view(np.int16)),
+                                   dev(wl.block_table), dev(wl.seq_lens), hint,
+                                   wl.softmax_scale, out, lse, ws, v_dim=wl.v_dim)
+    check(wl, gs, packed, host(out).view(np.uint16), host(lse), what="unaligned out")
+
+
 FULL = {
     "llama3_8b": (lambda: W.llama3_8b(), [0, 13, 31]),
     "qwen3_8b_long": (lambda: W.qwen3_8b_long(), None),  # longest and shortest sequence
