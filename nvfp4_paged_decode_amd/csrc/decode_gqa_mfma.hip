@@ -72,6 +72,22 @@ constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords, so the
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Tuning knobs (defaults are the measured best): tiles in flight per
+// stream (2 or 3), XOR swizzle of staged V chunks, and two independent
+// accumulation chains for the scores.
+#ifndef KVFP4_GQA_DEPTH
+#define KVFP4_GQA_DEPTH 2
+#endif
+#ifndef KVFP4_GQA_SWZ
+#define KVFP4_GQA_SWZ 1
+#endif
+#ifndef KVFP4_GQA_SPLIT
+#define KVFP4_GQA_SPLIT 1
+#endif
+#ifndef KVFP4_GQA_AUX  // cache-policy bits of the K/V loads
+#define KVFP4_GQA_AUX 0
+#endif
+
 struct StageLds {
   _Float16 v[kWaves][4][kTile][kPitch];  // per wave: 4 KV heads x 16 tokens
 };
@@ -169,11 +185,11 @@ __device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long l
   auto rvs = __builtin_amdgcn_make_buffer_rsrc((void*)vss, (short)0, n * rows, 0x00020000);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tg.off_data + 16 * j, 0, 0));
-    p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tg.off_data + 16 * j, 0, 0));
+    p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
+    p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
   }
-  p.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, 0));
-  p.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, 0));
+  p.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, KVFP4_GQA_AUX));
+  p.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, KVFP4_GQA_AUX));
 }
 
 template <int NKG>
@@ -209,8 +225,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int x = (lg + 2 * m) & 3, y = (lg + 2 * m + 1) & 3;
-    tr_base[m][0] = vw + (4 * x + q4) * kPitch + 4 * j4;
-    tr_base[m][1] = vw + (4 * y + q4) * kPitch + 4 * j4;
+    tr_base[m][0] = vw + (4 * x + q4) * kPitch;
+    tr_base[m][1] = vw + (4 * y + q4) * kPitch;
+  }
+  // The 16-byte chunk c of staged row r sits at chunk c ^ ((r >> 3) & 1),
+  // so that the row-wise writes of rows r and r + 8 use different banks.  A
+  // transposed read of dims 16dt + 4j.. of rows 4x..4x+3 (chunk 2dt + j/2)
+  // therefore starts at fp16 16dt + 8((j/2) ^ (x/2)) + 4(j%2).
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int x = (lg + 2 * m) & 3, y = (lg + 2 * m + 1) & 3;
+    const int sx = KVFP4_GQA_SWZ ? x >> 1 : 0, sy = KVFP4_GQA_SWZ ? y >> 1 : 0;
+    tr_base[m][0] += 8 * ((j4 >> 1) ^ sx) + 4 * (j4 & 1);
+    tr_base[m][1] += 8 * ((j4 >> 1) ^ sy) + 4 * (j4 & 1);
   }
   const int src_x1 = lr + 16 * ((lg + 1) & 3);
   const int src_x2 = lr + 16 * ((lg + 2) & 3);
@@ -233,44 +260,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     const long long t_end = (L + kTile - 1) / kTile;
     if (t_hi > t_end) t_hi = t_end;
 
-    // queries of this wave's 16 heads as the block-diagonal B operand
     const int head = 16 * kg + lr;
-    f16x8 qb[16];
-    int sh = 0;
-    {
-      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * kD;
-      if (diag) {
-        // largest magnitude from the bf16 bit patterns, then a power of two
-        // that puts it in [2^14, 2^15)
-        uint32_t mb = 0;
-        for (int i = 0; i < kD / 8; ++i) {
-          const u32x4 raw = load_q8(qrow, i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            mb = max(mb, raw[e] & 0x7FFFu);
-            mb = max(mb, (raw[e] >> 16) & 0x7FFFu);
-          }
-        }
-        if (mb != 0) {
-          int e;
-          frexpf(__uint_as_float(mb << 16), &e);  // amax < 2^e
-          sh = 15 - e;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kD / 8; ++i) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (diag) raw = load_q8(qrow, i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[e] << 16), sh);
-          qb[i][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[e] & 0xFFFF0000u), sh);
-        }
-      }
-    }
-    // score scale of column lr: the shift lives in lane (lr, lr / 4)
-    const int sh_c = __shfl(sh, lr + 16 * (lr >> 2));
-    const float qs = ldexpf(base_scale, -sh_c);
+    f16x8 qb[16];   // queries: filled once the first tile is requested
+    float qs = 0.f;
 
     f32x4 acc[kD / 16];
 #pragma unroll
@@ -290,46 +282,39 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
     };
 
-    long long ti = t_lo + s;
-    Packed cur, nxt;
-    int n_cur = 0, n_nxt = 0;
-    if (ti < t_hi) {
-      const int sl = slot_of(ti);
-      n_cur = tile_rows(tg, sl, ti);
-      load_tile(cur, tg, sl, ti, n_cur);
-    }
-    for (; ti < t_hi; ti += NS) {
-      const long long tn = ti + NS;
-      if (tn < t_hi) {
-        const int sl = slot_of(tn);
-        n_nxt = tile_rows(tg, sl, tn);
-        load_tile(nxt, tg, sl, tn, n_nxt);
-      }
-
-      // V rows -> LDS (natural layout), dequantized once
+    // One tile of the stream: V rows to LDS, scores, softmax, P.V.
+    auto compute = [&](const Packed& cur, int n_cur) {
+      // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 3)
       {
         f16x2 vsc[4];
         scales8(cur.vs, vsc);
         _Float16* dst = vw + lr * kPitch;
+        const int sw = KVFP4_GQA_SWZ ? (lr >> 3) & 1 : 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<f16x8*>(dst + 32 * j + 8 * e) =
+            *reinterpret_cast<f16x8*>(dst + 8 * ((4 * j + e) ^ sw)) =
                 dequant8(cur.v[j][e], block_scale(vsc, (4 * j + e) >> 1));
       }
 
-      // scores S^T[token][column]
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      // scores S^T[token][column], two independent accumulation chains
+      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
       {
         f16x2 ksc[4];
         scales8(cur.ks, ksc);
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const f16x8 ka = dequant8(cur.k[ks >> 2][ks & 3], block_scale(ksc, ks >> 1));
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sc, 0, 0, 0);
+        for (int ks = 0; ks < 16; ks += 2) {
+          const f16x8 ka0 = dequant8(cur.k[ks >> 2][ks & 3], block_scale(ksc, ks >> 1));
+          sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka0, qb[ks], sc0, 0, 0, 0);
+          const f16x8 ka1 = dequant8(cur.k[ks >> 2][(ks & 3) + 1], block_scale(ksc, ks >> 1));
+          if (KVFP4_GQA_SPLIT)
+            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka1, qb[ks + 1], sc1, 0, 0, 0);
+          else
+            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka1, qb[ks + 1], sc0, 0, 0, 0);
         }
       }
+      const f32x4 sc = sc0 + sc1;
 
       // online softmax of column lr over rows 4 lg + r
       float sv[4];
@@ -384,10 +369,84 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
 
+    // Depth 3: tile k+2 is requested before tile k is computed, into the
+    // buffer tile k-1 used (no register copies of loads still in flight).
+    auto issue = [&](Packed& p, int& n, long long t) {
+      if (t < t_hi) {
+        const int sl = slot_of(t);
+        n = tile_rows(tg, sl, t);
+        load_tile(p, tg, sl, t, n);
+      }
+    };
+    // queries of this wave's 16 heads as the block-diagonal B operand, one
+    // pass: the largest magnitude (from the bf16 bit patterns) sets a power
+    // of two that puts it in [2^14, 2^15); lanes off the diagonal scale by
+    // 2^-200, which makes their operand exactly 0
+    auto load_queries = [&]() {
+      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * kD;
+      u32x4 raw[kD / 8];
+      uint32_t mb = 0;
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i) raw[i] = load_q8(qrow, i);
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mb = max(mb, raw[i][e] & 0x7FFFu);
+          mb = max(mb, (raw[i][e] >> 16) & 0x7FFFu);
+        }
+      int sh = 0;
+      if (mb != 0) {
+        int e;
+        frexpf(__uint_as_float(mb << 16), &e);  // amax < 2^e
+        sh = 15 - e;
+      }
+      const int shq = diag ? sh : -200;
+#pragma unroll
+      for (int i = 0; i < kD / 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[i][e] << 16), shq);
+          qb[i][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[i][e] & 0xFFFF0000u), shq);
+        }
+      // score scale of column lr: its shift lives in lane (lr, lr / 4)
+      const int sh_c = __shfl(sh, lr + 16 * (lr >> 2));
+      qs = ldexpf(base_scale, -sh_c);
+    };
+
+#if KVFP4_GQA_DEPTH == 3
+    Packed B0, B1, B2;
+    int n0 = 0, n1 = 0, n2 = 0;
+    long long ti = t_lo + s;
+    issue(B0, n0, ti);
+    issue(B1, n1, ti + NS);
+    load_queries();
+    for (; ti < t_hi; ti += 3 * NS) {
+      issue(B2, n2, ti + 2 * NS);
+      compute(B0, n0);
+      if (ti + NS >= t_hi) break;
+      issue(B0, n0, ti + 3 * NS);
+      compute(B1, n1);
+      if (ti + 2 * NS >= t_hi) break;
+      issue(B1, n1, ti + 4 * NS);
+      compute(B2, n2);
+    }
+#else
+    // two tiles in flight: tile k+1 is requested before tile k is computed
+    Packed cur, nxt;
+    int n_cur = 0, n_nxt = 0;
+    long long ti = t_lo + s;
+    issue(cur, n_cur, ti);  // requested before the queries are prepared
+    load_queries();
+    for (; ti < t_hi; ti += NS) {
+      issue(nxt, n_nxt, ti + NS);
+      compute(cur, n_cur);
       cur = nxt;
       n_cur = n_nxt;
     }
+#endif
 
     // merge the NS streams of each KV-head group, then write the partial
     l += __shfl_xor(l, 16);
