@@ -388,11 +388,9 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
   }
   if (mla_supported(g, hq, v_dim) || gqa_mfma_supported(g, hq, v_dim) ||
       gqa_supported(g, hq, v_dim)) {
-    // balanced kernels: one workgroup per CU (or per page when fewer); the
-    // MLA kernel runs two per CU and splits 128 heads over two workgroups
+    // balanced kernels: one workgroup per CU (or per page when fewer)
     p.kernel = mla_supported(g, hq, v_dim) ? 2 : gqa_mfma_supported(g, hq, v_dim) ? 3 : 1;
     long long target = cus;
-    if (p.kernel == 2) target = 2LL * cus / (hq > 64 ? hq / 64 : 1);
     long long pages_ub = (long long)batch * pages_max;
     long long nwg = target < pages_ub ? target : pages_ub;
     p.nwg = (int)(nwg > 0 ? nwg : 1);

@@ -1,31 +1,46 @@
 // Paged NVFP4 decode attention, MLA path on MFMA: one 576-value latent per
 // token (512 + 64 rope, all NVFP4), values = the first 512 dims of the same
-// latent, 16 to 128 query heads, pages of 32 or 64 tokens.
+// latent, up to 128 query heads, pages a multiple of 32 tokens.
 //
 // "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
 // NVFP4 KV Decode Attention Kernel Implementation / Figure 3: packed tiles
 // and their E4M3 scales are staged, unpacked and scaled, and both attention
-// products run in bf16 with the tensor scale applied as a scalar.  With 128
-// query heads over one latent the products are real dense contractions
-// (about 860 flop per cache byte), so here they run on MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// products run as 16-bit matrix products with the tensor scale applied as a
+// scalar.  With up to 128 query heads over one latent the products are real
+// dense contractions (about 820 flop per cache byte at 128 heads), so they
+// run on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
 //
-// Per workgroup (up to 4 waves, two workgroups per CU): a contiguous page
-// range of the batch (the balanced split of decode_plan.hpp) and a group of
-// up to 64 query heads (blockIdx.y); wave w owns 16 heads of the group.
-// For each 32-token tile:
-//  1. every thread dequantizes part of the tile once: E2M1 codes decoded
-//     exactly by the converter (scale 1.0) to fp32, times the E4M3 block
-//     scale (exact: at most 6 significant bits), packed to bf16 (exact),
-//     written to LDS twice: natural [token][576] for the scores and
-//     transposed [512][token] for P.V;
-//  2. scores as S^T = K Q^T (A = latent rows from LDS, B = the wave's
-//     queries, held in registers for the whole kernel), so that each lane
-//     ends up holding, for its head column, exactly the 8 tokens it feeds
-//     to the P.V MFMA as A operand: no transpose of P;
-//  3. online softmax per head (running max, lazy rescale of the output
-//     accumulators only when a maximum grows);
-//  4. O += P V with V from the transposed LDS copy.
+// 16-bit format: E2M1 x E4M3 has at most 6 significant bits in [2^-10,
+// 2688], exact in fp16; the converter decodes E2M1 codes exactly (scale
+// 1.0) and one v_pk_mul_f16 applies the block scale to two values.  Queries
+// are scaled per head by a power of two that puts their largest magnitude
+// in [2^14, 2^15) before the fp16 conversion (bf16 significands fit fp16's),
+// and the power of two is undone on the fp32 scores.  Probabilities are
+// rounded to fp16 for P.V.
+//
+// Workgroup: NW = ceil(heads / 16) waves (two per SIMD at 128 heads), one
+// CU, all query heads of a page range (the balanced split of
+// decode_plan.hpp); wave w owns heads [16w, 16w + 16), so its output
+// accumulators (16 heads x 512 dims) fit the accumulation registers.
+// Per 32-token tile:
+//  1. the workgroup dequantizes the tile once into LDS in its natural
+//     [token][576] layout (16-byte chunks XOR-swizzled by token bits 2 and
+//     3, which keeps the row reads, the transposed reads and the staging
+//     writes free of bank conflicts); tiles are double-buffered, the next
+//     tile's bytes are requested before the current tile's products and
+//     staged after them;
+//  2. scores S^T = K Q^T per 16 tokens: A = latent rows read from LDS (16
+//     bytes per lane), B = the wave's queries, held in registers per
+//     sequence; lane (column c, group g) receives rows 4g..4g+3 of head c;
+//  3. online softmax per head (a lane's accumulators all belong to its own
+//     head column, so rescaling needs no exchange; the running maximum is
+//     only raised when a tile's maximum exceeds it by more than 2^8 in
+//     exp2 units, which keeps rescales rare and probabilities below 2^8);
+//  4. O^T += V^T P^T over all 32 tokens at once: the B operand is exactly
+//     the lane's own 8 probabilities (rows 4g..4g+3 of both 16-token
+//     halves), and the A operand (V^T) comes from the same natural tile
+//     through ds_read_b64_tr_b16 (4 tokens of one dim per lane), so no
+//     transposed copy is made.
 // The wave's unnormalized partial (O, max, sum) goes to workspace slot
 // (workgroup + sequence); merge_balanced_kernel combines them.
 #include "common.hpp"
@@ -35,52 +50,104 @@ namespace kvfp4 {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kD = 576;       // latent dims per token (keys)
-constexpr int kDv = 512;      // value dims (latent prefix)
-constexpr int kTile = 32;     // tokens per tile
-constexpr int kKs = kD / 32;  // k-steps of the score MFMA
-constexpr int kVt = kDv / 16; // 16-column tiles of the output
-constexpr int kKnPitch = kD + 8;   // bf16 per natural row (292 dwords: conflict-free reads)
-constexpr int kVtPitch = 40;       // bf16 per transposed row (20 dwords)
+constexpr int kD = 576;            // latent dims per token (keys)
+constexpr int kDv = 512;           // value dims (latent prefix)
+constexpr int kTile = 32;          // tokens per tile
+constexpr int kKs = kD / 32;       // 18 k-steps of the score product
+constexpr int kDt = kDv / 16;      // 32 value-dim tiles of the output
+constexpr int kBlocks = kD / 16;   // NVFP4 blocks per latent row
+constexpr int kPitch = 608;        // fp16 per staged row (304 dwords)
+constexpr int kRowData = kD / 2, kRowScale = kD / 16;  // packed bytes per row
 constexpr float kNoMax = -1e30f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;      // lazy-rescale threshold (log2 units)
 
 struct MlaLds {
-  __bf16 kn[kTile][kKnPitch];  // natural latent rows
-  __bf16 vt[kDv][kVtPitch];    // transposed value rows, tokens in k-group order
+  _Float16 k[2][kTile][kPitch];  // double-buffered natural latent tiles
 };
 
-// Position of token t (0..31) in a transposed row: k-group g of the P.V
-// MFMA holds tokens 4g..4g+3 and 16+4g..16+4g+3 (the tokens that lane group
-// g holds in the score output), contiguously at [8g, 8g+8).
-__device__ inline int vt_pos(int t) { return ((t & 15) >> 2) * 8 + (t >> 4) * 4 + (t & 3); }
+// Swizzle of staged row `row`: 16-byte chunk c sits at chunk c ^ swz(row).
+__device__ inline int swz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
 
-__device__ inline bf16x8 lds_read8(const __bf16* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+// Physical fp16 index of chunk `chunk` (8 fp16) of staged row `row`.
+__device__ inline int chunk_at(int row, int chunk) {
+  return row * kPitch + ((chunk ^ swz(row)) << 3);
 }
 
-// Two workgroups per CU (2 x 78 KB of LDS, 256 registers per lane) so that
-// one workgroup's dequantization overlaps the other's MFMA work.
-#ifndef KVFP4_MLA_OCC
-#define KVFP4_MLA_OCC __attribute__((amdgpu_waves_per_eu(2)))
-#endif
+__device__ inline f16x2 fp4x2(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
 
-template <int NW, int NHT>
-__global__ __launch_bounds__(64 * NW) KVFP4_MLA_OCC void decode_mla_kernel(DecodeArgs a) {
-  constexpr int HG = 16 * NHT * NW;  // query heads of this workgroup
+// 8 values of dword w times their block scale (exact in fp16).
+__device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
+  const f16x2 s2 = {sb, sb};
+  const f16x2 a = fp4x2(w, 0) * s2, b = fp4x2(w, 1) * s2;
+  const f16x2 c = fp4x2(w, 2) * s2, d = fp4x2(w, 3) * s2;
+  return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+__device__ inline f16x4 lds_read_tr(const _Float16* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, r);
+}
+
+template <int NW>
+struct Prefetch {
+  static constexpr int kPer = (kTile * kBlocks + 64 * NW - 1) / (64 * NW);  // blocks per thread
+  u32x2 d[kPer];
+  uint32_t s[kPer];
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   constexpr int NT = 64 * NW;
-  const int HQ = a.hq, hg0 = blockIdx.y * HG;
+  constexpr int kPer = Prefetch<NW>::kPer;
   extern __shared__ __align__(16) unsigned char smem[];
-  MlaLds& s = *reinterpret_cast<MlaLds*>(smem);
+  MlaLds& st = *reinterpret_cast<MlaLds*>(smem);
   const Geom g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;  // head column (or token row), k-group
+  const int head = 16 * wave + col;
+  const bool head_ok = head < a.hq;
   const int w = blockIdx.x, nwg = gridDim.x;
-  const float qscale = a.softmax_scale * a.gs_k * kLog2e;
-  const int row_data = kD / 2, row_scale = kD / 16;  // bytes per token row (H = 1)
+  const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
+  const long long page_bytes = g.packed_bytes(), data_bytes = g.data_bytes();
+  const int tiles_per_page = g.T / kTile;
+
+  // score A operand of token half tt: lane (row = token 16 tt + col,
+  // k-group grp) reads chunk 4 ks + grp of its row (ks adds 32 fp16)
+  int nat_off[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int row = 16 * tt + col;
+    nat_off[tt] = row * kPitch + 8 * (grp ^ swz(row));
+  }
+  // transposed reads: in 16-lane subgroup grp, source lane 4q + j reads row
+  // 16 h + 4 grp + q, dims 16 dt + 4 j; the row swizzle (constant per
+  // subgroup) moves dim tile dt to dt ^ (grp & 1): offsets for even and odd dt
+  const int q4 = (lane & 15) >> 2, j4 = lane & 3;
+  const int sw = swz(4 * grp);
+  int tr_off[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const int row = 16 * h + 4 * grp + q4;
+      const int chunk = (2 * odd + (j4 >> 1)) ^ sw;   // of the dim-tile pair (2 dt, 2 dt + 1)
+      tr_off[h][odd] = row * kPitch + 8 * chunk + 4 * (j4 & 1) - 16 * odd;
+    }
 
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
@@ -93,182 +160,201 @@ __global__ __launch_bounds__(64 * NW) KVFP4_MLA_OCC void decode_mla_kernel(Decod
     const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;
+    const long long t_lo = p_lo * tiles_per_page;
+    long long t_hi = p_hi * tiles_per_page;
+    const long long t_end = (L + kTile - 1) / kTile;
+    if (t_hi > t_end) t_hi = t_end;
 
-    // queries of this wave as the B operand of S^T = K Q^T: lane (head
-    // column lr, k-group lg) holds q[head][32 ks + 8 lg .. + 8]
-    bf16x8 qb[NHT][kKs];
+    // page-table entries of pages c0 .. c0+63, one per lane
+    const int32_t* bt_row = a.block_table + (long long)b * a.max_pages;
+    long long c0 = -(1LL << 40);
+    int slot_vec = -1;
+    auto slot_of = [&](long long ti) -> int {
+      const long long pg = ti / tiles_per_page;
+      if (pg < c0 || pg >= c0 + 64) {
+        c0 = pg;
+        slot_vec = (c0 + lane < p_hi) ? bt_row[c0 + lane] : -1;
+      }
+      return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
+    };
+    auto rows_of = [&](int slot, long long ti) -> int {
+      int n = L - (int)(ti * kTile);
+      n = n > kTile ? kTile : n;
+      if (slot < 0 || slot >= a.pool_pages) n = 0;
+      return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
+    };
+
+    // this thread's blocks of a tile: block bi = tid + NT u is row bi % 32,
+    // block bi / 32 of the row; rows past the sequence end read as zero
+    Prefetch<NW> pre;
+    auto issue = [&](long long ti) -> int {
+      const int slot = slot_of(ti);
+      const int n = rows_of(slot, ti);
+      const int row0 = (int)(ti % tiles_per_page) * kTile;
+      const uint8_t* page = a.pool + (long long)(n > 0 ? slot : 0) * page_bytes;
+      auto rd = __builtin_amdgcn_make_buffer_rsrc((void*)(page + (long long)row0 * kRowData),
+                                                  (short)0, n * kRowData, 0x00020000);
+      auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(page + data_bytes + (long long)row0 * kRowScale), (short)0, n * kRowScale,
+          0x00020000);
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int head = hg0 + (wave * NHT + ht) * 16 + lr;
-      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * kD;
+      for (int u = 0; u < kPer; ++u) {
+        const int bi = tid + NT * u;
+        if (bi < kTile * kBlocks) {
+          const int t = bi & (kTile - 1), blk = bi >> 5;
+          pre.d[u] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rd, t * kRowData + 8 * blk, 0, 0));
+          pre.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, t * kRowScale + blk, 0, 0);
+        }
+      }
+      return n;
+    };
+    auto stage = [&](int buf) {
+      _Float16* base = &st.k[buf][0][0];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int bi = tid + NT * u;
+        if (bi < kTile * kBlocks) {
+          const int t = bi & (kTile - 1), blk = bi >> 5;
+          const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pre.s[u], 1.0f, false);
+          const _Float16 sb = sp.x;
+          *reinterpret_cast<f16x8*>(base + chunk_at(t, 2 * blk)) = dequant8(pre.d[u].x, sb);
+          *reinterpret_cast<f16x8*>(base + chunk_at(t, 2 * blk + 1)) = dequant8(pre.d[u].y, sb);
+        }
+      }
+    };
+
+    int n_cur = issue(t_lo);
+
+    // queries of this wave's 16 heads (B operand of the scores): lane
+    // (column c, group g) holds dims 32 ks + 8 g .. +8 of head c
+    f16x8 qb[kKs];
+    float qs;
+    {
+      const uint16_t* qrow = a.q + ((long long)b * a.hq + (head_ok ? head : 0)) * kD + 8 * grp;
+      u32x4 raw[kKs];
+      uint32_t mb = 0;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks)
-        qb[ht][ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * lg);
-    }
-    f32x4 acc[NHT][kVt];
-    float m[NHT], l[NHT];
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      m[ht] = kNoMax;
-      l[ht] = 0.f;
-#pragma unroll
-      for (int vt = 0; vt < kVt; ++vt) acc[ht][vt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int tiles_per_page = g.T / kTile;
-    const long long tile_lo = p_lo * tiles_per_page, tile_hi = p_hi * tiles_per_page;
-    for (long long tile = tile_lo; tile < tile_hi; ++tile) {
-      const long long pg = tile / tiles_per_page;
-      const int row0 = (int)(tile % tiles_per_page) * kTile;  // first row in the page
-      const int slot = __builtin_amdgcn_readfirstlane(a.block_table[(long long)b * a.max_pages + pg]);
-      int n_valid = L - (int)(pg * g.T) - row0;  // valid tokens of this tile
-      if (n_valid > kTile) n_valid = kTile;
-      if (slot < 0 || slot >= a.pool_pages) n_valid = 0;
-      n_valid = uniform(n_valid);
-      const uint8_t* page = a.pool + (long long)(slot < 0 ? 0 : slot) * g.packed_bytes();
-      const uint8_t* tdat = page + (long long)row0 * row_data;
-      const uint8_t* tsc = page + g.data_bytes() + (long long)row0 * row_scale;
-
-      // 1. dequantize the tile into LDS: chunk = 8 values of one token
-      __syncthreads();  // the previous tile's readers are done
-      for (int c = tid; c < kTile * (kD / 8); c += NT) {
-        const int t = c & (kTile - 1), d8 = c >> 5;  // 32 tokens per d8 column
-        f32x2 v[4];
-        if (t < n_valid) {
-          const uint32_t wd = *reinterpret_cast<const uint32_t*>(tdat + t * row_data + d8 * 4);
-          const float sb = __builtin_amdgcn_cvt_f32_fp8((int)tsc[t * row_scale + (d8 >> 1)], 0);
-          v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 0);
-          v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 1);
-          v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 2);
-          v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 3);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] *= sb;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (f32x2){0.f, 0.f};
+        for (int e = 0; e < 4; ++e) {
+          mb = max(mb, raw[ks][e] & 0x7FFFu);
+          mb = max(mb, (raw[ks][e] >> 16) & 0x7FFFu);
         }
-        bf16x8 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = (__bf16)v[i].x;
-          o[2 * i + 1] = (__bf16)v[i].y;
-        }
-        *reinterpret_cast<bf16x8*>(&s.kn[t][d8 * 8]) = o;
-        if (d8 < kDv / 8) {
-          const int pos = vt_pos(t);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s.vt[d8 * 8 + e][pos] = o[e];
-        }
+      mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+      mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+      int sh = 0;
+      if (mb != 0) {
+        int e;
+        frexpf(__uint_as_float(mb << 16), &e);  // amax < 2^e
+        sh = 15 - e;
       }
-      __syncthreads();
-
-      // 2. scores S^T[token][head]: lane (head lr, k-group lg) gets tokens
-      //    16 tt + 4 lg + r
-      f32x4 sc[NHT][2];
+      const int shq = head_ok ? sh : -200;  // padding columns: exactly 0
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) sc[ht][0] = sc[ht][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qb[ks][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] << 16), shq);
+          qb[ks][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] & 0xFFFF0000u), shq);
+        }
+      qs = ldexpf(base_scale, -sh);
+    }
+
+    f32x4 acc[kDt];
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m = kNoMax, l = 0.f;
+
+    stage(0);
+    __syncthreads();
+    int buf = 0;
+    for (long long ti = t_lo; ti < t_hi; ++ti) {
+      const bool more = ti + 1 < t_hi;
+      int n_nxt = 0;
+      if (more) n_nxt = issue(ti + 1);
+      const _Float16* kb = &st.k[buf][0][0];
+
+      // 2. scores S^T[token][head], 16 tokens per half
+      f32x4 sc[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
+        sc[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-          const bf16x8 ka = lds_read8(&s.kn[16 * tt + lr][32 * ks + 8 * lg]);
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht)
-            sc[ht][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[ht][ks], sc[ht][tt], 0, 0, 0);
+          const f16x8 ka = *reinterpret_cast<const f16x8*>(kb + nat_off[tt] + 32 * ks);
+          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sc[tt], 0, 0, 0);
         }
       }
 
-      // 3. online softmax per head column (log2 units)
-      bf16x8 pa[NHT];
-      bool grew = false;
-      float mnew[NHT];
+      // 3. online softmax of head `col` over rows 16 tt + 4 grp + r
+      float sv[8];
+      float mx = kNoMax;
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        float mx = kNoMax;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = 16 * tt + 4 * lg + r;
-            float v = sc[ht][tt][r] * qscale;
-            v = tok < n_valid ? v : -INFINITY;
-            sc[ht][tt][r] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mnew[ht] = fmaxf(m[ht], mx);
-        grew |= mnew[ht] > m[ht];
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
+        sv[e] = tok < n_cur ? sc[e >> 2][e & 3] * qs : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
       }
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grew) != 0, 0)) {
-        // output rows are heads 4 lg + r of the tile: fetch their factors
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0, 0)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          const float alpha = __builtin_amdgcn_exp2f(m[ht] - mnew[ht]);
-          l[ht] *= alpha;
-          float ar[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * lg + r);
-#pragma unroll
-          for (int vt = 0; vt < kVt; ++vt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[ht][vt][r] *= ar[r];
-          m[ht] = mnew[ht];
-        }
+        for (int dt = 0; dt < kDt; ++dt) acc[dt] *= alpha;
+        m = mn;
       }
+      f16x8 pb;
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        float sum = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sc[ht][tt][r] - m[ht]);
-            sum += p;
-            pa[ht][4 * tt + r] = (__bf16)p;
-          }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        l[ht] += sum;
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sv[e] - m);
+        l += p;
+        pb[e] = (_Float16)p;
       }
 
-      // 4. O[head][v] += P[head][token] V[token][v]
+      // 4. O^T[dim][head] += V^T P^T over the 32 tokens
 #pragma unroll
-      for (int vt = 0; vt < kVt; ++vt) {
-        const bf16x8 vb = lds_read8(&s.vt[16 * vt + lr][8 * lg]);
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-          acc[ht][vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ht], vb, acc[ht][vt], 0, 0, 0);
+      for (int dt = 0; dt < kDt; ++dt) {
+        const f16x4 lo = lds_read_tr(kb + tr_off[0][dt & 1] + 16 * dt);
+        const f16x4 hi = lds_read_tr(kb + tr_off[1][dt & 1] + 16 * dt);
+        const f16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[dt], 0, 0, 0);
       }
+
+      // 1. (next tile) staged into the other buffer
+      if (more) stage(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      n_cur = n_nxt;
     }
 
-    // partial for slot (workgroup + sequence): lane holds heads 4 lg + r of
-    // each tile, value column 16 vt + lr
-    const long long slotp = (long long)w + b;
+    // partial for slot (workgroup + sequence): lane holds head `col`,
+    // dims 16 dt + 4 grp + 0..3 in acc[dt]
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (head_ok) {
+      const long long slotp = ((long long)w + b) * a.hq + head;
+      float* dst = a.ws_o + slotp * kDv;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int hbase = hg0 + (wave * NHT + ht) * 16;
-#pragma unroll
-      for (int vt = 0; vt < kVt; ++vt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          a.ws_o[(slotp * HQ + hbase + 4 * lg + r) * kDv + 16 * vt + lr] = acc[ht][vt][r];
-      if (lg == 0) {
-        a.ws_ml[(slotp * HQ + hbase + lr) * 2] = m[ht];
-        a.ws_ml[(slotp * HQ + hbase + lr) * 2 + 1] = l[ht];
+      for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * grp) = acc[dt];
+      if (grp == 0) {
+        a.ws_ml[slotp * 2] = m;
+        a.ws_ml[slotp * 2 + 1] = l;
       }
     }
   }
 }
 
-template <int NW, int NHT>
+template <int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = sizeof(MlaLds);  // above the 64 KiB default: opt in
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mla_kernel<NW, NHT>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mla_kernel<NW>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int groups = a.hq / (16 * NHT * NW);
-  hipLaunchKernelGGL((decode_mla_kernel<NW, NHT>), dim3(a.nwg, groups), dim3(64 * NW), lds, stream, a);
+  hipLaunchKernelGGL((decode_mla_kernel<NW>), dim3(a.nwg), dim3(64 * NW), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -276,17 +362,22 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 
 bool mla_supported(const Geom& g, int hq, int v_dim) {
   if (g.nt != 1 || g.H != 1 || g.D != kD || v_dim != kDv) return false;
-  if (g.T % kTile != 0 || g.T > 256) return false;
-  return hq == 16 || hq == 32 || hq == 64 || hq == 128;
+  if (g.T % kTile != 0 || g.T > 4096) return false;
+  return hq >= 1 && hq <= 128;
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.hq) {
-    case 128: return launch_nw<4, 1>(a, stream);
-    case 64: return launch_nw<4, 1>(a, stream);
-    case 32: return launch_nw<2, 1>(a, stream);
-    case 16: return launch_nw<1, 1>(a, stream);
-    default: return hipErrorInvalidValue;
+  if (!mla_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
+  if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
+  switch ((a.hq + 15) / 16) {
+    case 1: return launch_nw<1>(a, stream);
+    case 2: return launch_nw<2>(a, stream);
+    case 3: return launch_nw<3>(a, stream);
+    case 4: return launch_nw<4>(a, stream);
+    case 5: return launch_nw<5>(a, stream);
+    case 6: return launch_nw<6>(a, stream);
+    case 7: return launch_nw<7>(a, stream);
+    default: return launch_nw<8>(a, stream);
   }
 }
 
