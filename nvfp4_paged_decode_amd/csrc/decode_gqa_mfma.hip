@@ -66,9 +66,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;       // head dim
 constexpr int kTile = 16;     // tokens per tile
 constexpr int kWaves = 8;     // waves per workgroup
-constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords, so the
-                                 // transposed reads of a 32-lane half hit 64
-                                 // distinct banks
+constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords (8 banks
+                                 // mod 32), so the 16 lanes of a transposed
+                                 // read hit distinct banks
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -228,14 +228,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     tr_base[m][0] = vw + (4 * x + q4) * kPitch;
     tr_base[m][1] = vw + (4 * y + q4) * kPitch;
   }
-  // The 16-byte chunk c of staged row r sits at chunk c ^ ((r >> 3) & 1),
-  // so that the row-wise writes of rows r and r + 8 use different banks.  A
+  // The 16-byte chunk c of staged row r sits at chunk c ^ ((r >> 2) & 1):
+  // LDS has 32 banks of 4 bytes and the pitch is 8 banks mod 32, so rows r
+  // and r + 4 would collide for the 16-byte writes of 8 lanes.  A
   // transposed read of dims 16dt + 4j.. of rows 4x..4x+3 (chunk 2dt + j/2)
-  // therefore starts at fp16 16dt + 8((j/2) ^ (x/2)) + 4(j%2).
+  // therefore starts at fp16 16dt + 8((j/2) ^ (x & 1)) + 4(j%2).
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int x = (lg + 2 * m) & 3, y = (lg + 2 * m + 1) & 3;
-    const int sx = KVFP4_GQA_SWZ ? x >> 1 : 0, sy = KVFP4_GQA_SWZ ? y >> 1 : 0;
+    const int sx = KVFP4_GQA_SWZ ? x & 1 : 0, sy = KVFP4_GQA_SWZ ? y & 1 : 0;
     tr_base[m][0] += 8 * ((j4 >> 1) ^ sx) + 4 * (j4 & 1);
     tr_base[m][1] += 8 * ((j4 >> 1) ^ sy) + 4 * (j4 & 1);
   }
@@ -284,12 +285,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 
     // One tile of the stream: V rows to LDS, scores, softmax, P.V.
     auto compute = [&](const Packed& cur, int n_cur) {
-      // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 3)
+      // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 2)
       {
         f16x2 vsc[4];
         scales8(cur.vs, vsc);
         _Float16* dst = vw + lr * kPitch;
-        const int sw = KVFP4_GQA_SWZ ? (lr >> 3) & 1 : 0;
+        const int sw = KVFP4_GQA_SWZ ? (lr >> 2) & 1 : 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll

@@ -24,8 +24,8 @@
 // accumulators (16 heads x 512 dims) fit the accumulation registers.
 // Per 32-token tile:
 //  1. the workgroup dequantizes the tile once into LDS in its natural
-//     [token][576] layout (16-byte chunks XOR-swizzled by token bits 2 and
-//     3, which keeps the row reads, the transposed reads and the staging
+//     [token][576] layout (16-byte chunks XOR-swizzled by token bit 2,
+//     which keeps the row reads, the transposed reads and the staging
 //     writes free of bank conflicts); tiles are double-buffered, the next
 //     tile's bytes are requested before the current tile's products and
 //     staged after them;
@@ -61,7 +61,7 @@ constexpr int kTile = 32;          // tokens per tile
 constexpr int kKs = kD / 32;       // 18 k-steps of the score product
 constexpr int kDt = kDv / 16;      // 32 value-dim tiles of the output
 constexpr int kBlocks = kD / 16;   // NVFP4 blocks per latent row
-constexpr int kPitch = 608;        // fp16 per staged row (304 dwords)
+constexpr int kPitch = 592;        // fp16 per staged row (296 dwords = 8 mod 32 banks)
 constexpr int kRowData = kD / 2, kRowScale = kD / 16;  // packed bytes per row
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -72,7 +72,10 @@ struct MlaLds {
 };
 
 // Swizzle of staged row `row`: 16-byte chunk c sits at chunk c ^ swz(row).
-__device__ inline int swz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
+// LDS has 32 banks of 4 bytes; with the pitch at 8 banks mod 32, rows r
+// and r + 4 would collide for 16-byte accesses of 8 lanes, which the flip
+// of chunk bit 0 on rows 4..7 (mod 8) separates.
+__device__ inline int swz(int row) { return (row >> 2) & 1; }
 
 // Physical fp16 index of chunk `chunk` (8 fp16) of staged row `row`.
 __device__ inline int chunk_at(int row, int chunk) {
@@ -135,19 +138,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     nat_off[tt] = row * kPitch + 8 * (grp ^ swz(row));
   }
   // transposed reads: in 16-lane subgroup grp, source lane 4q + j reads row
-  // 16 h + 4 grp + q, dims 16 dt + 4 j; the row swizzle (constant per
-  // subgroup) moves dim tile dt to dt ^ (grp & 1): offsets for even and odd dt
+  // 16 h + 4 grp + q, dims 16 dt + 4 j (the row swizzle is constant within
+  // the subgroup and only swaps the two chunks of a dim tile)
   const int q4 = (lane & 15) >> 2, j4 = lane & 3;
   const int sw = swz(4 * grp);
-  int tr_off[2][2];
+  int tr_off[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int odd = 0; odd < 2; ++odd) {
-      const int row = 16 * h + 4 * grp + q4;
-      const int chunk = (2 * odd + (j4 >> 1)) ^ sw;   // of the dim-tile pair (2 dt, 2 dt + 1)
-      tr_off[h][odd] = row * kPitch + 8 * chunk + 4 * (j4 & 1) - 16 * odd;
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int row = 16 * h + 4 * grp + q4;
+    tr_off[h] = row * kPitch + 8 * ((j4 >> 1) ^ sw) + 4 * (j4 & 1);
+  }
 
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
@@ -318,8 +318,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
       // 4. O^T[dim][head] += V^T P^T over the 32 tokens
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        const f16x4 lo = lds_read_tr(kb + tr_off[0][dt & 1] + 16 * dt);
-        const f16x4 hi = lds_read_tr(kb + tr_off[1][dt & 1] + 16 * dt);
+        const f16x4 lo = lds_read_tr(kb + tr_off[0] + 16 * dt);
+        const f16x4 hi = lds_read_tr(kb + tr_off[1] + 16 * dt);
         const f16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[dt], 0, 0, 0);
       }
