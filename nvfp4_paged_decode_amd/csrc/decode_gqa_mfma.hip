@@ -36,7 +36,8 @@
 //            c's KV head, else 0), kept in registers per sequence.  Lane
 //            (c, g) receives rows 4g..4g+3 of column c.
 //   softmax  online per column, running max shared by the column's 4
-//            lanes, lazy rescale of the accumulators only when it grows.
+//            lanes; the accumulators are rescaled only when a tile's
+//            maximum exceeds the running one by more than 2^8.
 //   P.V      O^T = V^T P^T.  V rows are dequantized by the same lanes and
 //            staged in LDS in their natural [KV head][token][dim] order;
 //            ds_read_b64_tr_b16 reads them transposed (4 tokens of one dim
@@ -71,6 +72,9 @@ constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords (8 banks
                                  // read hit distinct banks
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
+                               // maximum exceeds it by more than this (log2
+                               // units): rescales stay rare, p stays < 2^8
 
 // Tuning knobs (defaults are the measured best): tiles in flight per
 // stream (2 or 3), XOR swizzle of staged V chunks, and two independent
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m) != 0, 0)) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0, 0)) {
         const float mn = fmaxf(m, mx);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         l *= alpha;
