@@ -152,14 +152,23 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
   return code;
 }
 
+// Cache-policy bits of the codec's streaming loads and stores.  Every input
+// byte is read by exactly one load instruction and never again, so loads are
+// non-temporal (nt); non-temporal stores measured slower and stay default.
+#ifndef KVFP4_CODEC_LOAD_AUX
+#define KVFP4_CODEC_LOAD_AUX 2
+#endif
+#ifndef KVFP4_CODEC_STORE_AUX
+#define KVFP4_CODEC_STORE_AUX 0
+#endif
 #ifndef KVFP4_QUANT_UNROLL
-#define KVFP4_QUANT_UNROLL 4
+#define KVFP4_QUANT_UNROLL 8
 #endif
 #ifndef KVFP4_DEQUANT_UNROLL
 #define KVFP4_DEQUANT_UNROLL 8
 #endif
 #ifndef KVFP4_CODEC_GRID
-#define KVFP4_CODEC_GRID 2048
+#define KVFP4_CODEC_GRID 4096
 #endif
 constexpr int kQuantUnroll = KVFP4_QUANT_UNROLL;    // half-blocks in flight per lane
 constexpr int kDequantUnroll = KVFP4_DEQUANT_UNROLL;
@@ -192,7 +201,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
       for (int u = 0; u < kQuantUnroll; ++u) {
         // out-of-range half-blocks read zero (buffer bounds) and store nothing
-        a[u] = __builtin_amdgcn_raw_buffer_load_b128(rin, (h0 + u * kThreads + (int)threadIdx.x) * 16, 0, 0);
+        a[u] = __builtin_amdgcn_raw_buffer_load_b128(rin, (h0 + u * kThreads + (int)threadIdx.x) * 16, 0,
+                                                     KVFP4_CODEC_LOAD_AUX);
       }
 #pragma unroll
       for (int u = 0; u < kQuantUnroll; ++u) {
@@ -225,9 +235,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         const uint32_t h0w = n0 | (n0 >> 12), h1w = n1 | (n1 >> 12);
         if (hb < hpp) {
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(h1w, h0w, 0x05040100u), rout,
-                                                hb * 4, 0, 0);
+                                                hb * 4, 0, KVFP4_CODEC_STORE_AUX);
           if ((hb & 1) == 0)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + blk, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + blk, 0,
+                                                 KVFP4_CODEC_STORE_AUX);
         }
       }
     }
@@ -306,8 +317,10 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
 #pragma unroll
       for (int u = 0; u < kDequantUnroll; ++u) {
         const int hb = h0 + u * kThreads + (int)threadIdx.x;
-        dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, 0);
-        code[u] = hb < hpp ? __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0, 0) : 0u;
+        dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, KVFP4_CODEC_LOAD_AUX);
+        code[u] = hb < hpp ? __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0,
+                                                                 KVFP4_CODEC_LOAD_AUX)
+                           : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kDequantUnroll; ++u) {
@@ -318,14 +331,15 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
         uint32_t o[4];
         decode8(dw[u], row, flip, o);
         if (hb < hpp)
-          __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rout, hb * 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rout, hb * 16, 0,
+                                                 KVFP4_CODEC_STORE_AUX);
       }
     }
   }
 }
 
 int grid_for(int num_pages) {
-  // one workgroup per page up to 8 per CU of a 256-CU part; each walks its
+  // one workgroup per page up to 16 per CU of a 256-CU part; each walks its
   // contiguous run of pages
   const int cap = KVFP4_CODEC_GRID;
   return num_pages < cap ? num_pages : cap;
