@@ -43,6 +43,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr uint32_t kPad = 0x7FFFu;  // above every finite bf16 magnitude
 constexpr int kRsrcFlags = 0x00020000;
+constexpr int kNoStore = 0x7FFFFFF0;  // buffer offset past every page: store dropped
 
 __device__ inline u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
 __device__ inline uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
@@ -53,7 +54,6 @@ __device__ inline uint32_t pk_mad(uint32_t a, uint32_t b, uint32_t c) {
 __device__ inline uint32_t pk_shr15(uint32_t a) { return as_u32(as_u16x2(a) >> (u16x2){15, 15}); }
 // 1 in each 16-bit half where the magnitude v exceeds threshold t (both < 0x8000)
 __device__ inline uint32_t gt_bit(uint32_t t, uint32_t v) { return pk_shr15(pk_sub(t, v)); }
-__device__ inline uint32_t dup16(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x01000100u); }
 
 // Pages [p0, p1) of this workgroup.
 __device__ inline void page_range(int num_pages, int& p0, int& p1) {
@@ -71,10 +71,15 @@ __device__ inline int page_slot(const int32_t* slots, int i, int pool_pages) {
 // ---------------------------------------------------------------------------
 
 struct QuantLds {
-  uint16_t e4m3[2][128];     // scale thresholds (126 used)
-  uint16_t e2m1[2][128][8];  // element thresholds per scale code (7 used)
-  double inv6gs[2];          // 1 / (6 gs) per tensor, for the scale estimate
+  uint16_t e4m3[2][128];  // scale thresholds (126 used)
+  // per tensor and scale code, the element thresholds T0..T6 in the form
+  // the encoder consumes, each in both 16-bit halves: {T0, T1, T3, T5 - T1},
+  // {T4 - T0, T2 - T0, (T6 - T4) - (T2 - T0), 0} (differences mod 2^16)
+  u32x4 thr[2][128][2];
+  double inv6gs[2];       // 1 / (6 gs) per tensor, for the scale estimate
 };
+
+__device__ inline uint32_t dup_half(uint32_t x) { return (x & 0xFFFFu) | (x << 16); }
 
 __device__ inline void build_quant_tables(QuantLds& s, int nt, float gs0, float gs1) {
   const double mu[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
@@ -89,29 +94,32 @@ __device__ inline void build_quant_tables(QuantLds& s, int nt, float gs0, float 
     }
     s.e4m3[t][j] = (uint16_t)th;
     double sb = (double)e4m3_to_float(j);
-    for (int k = 0; k < 8; ++k) {
+    uint32_t T[7];
+    for (int k = 0; k < 7; ++k) {
       uint32_t v = kPad;
-      if (k < 7 && j >= 1 && j <= 126) v = gt_threshold(mu[k] * sb * gs, (k & 1) == 0);
-      s.e2m1[t][j][k] = (uint16_t)v;
+      if (j >= 1 && j <= 126) v = gt_threshold(mu[k] * sb * gs, (k & 1) == 0);
+      T[k] = v;
     }
+    const uint32_t d51 = (T[5] - T[1]) & 0xFFFFu, d40 = (T[4] - T[0]) & 0xFFFFu;
+    const uint32_t d20 = (T[2] - T[0]) & 0xFFFFu;
+    const uint32_t dd = (((T[6] - T[4]) & 0xFFFFu) - d20) & 0xFFFFu;
+    s.thr[t][j][0] = (u32x4){dup_half(T[0]), dup_half(T[1]), dup_half(T[3]), dup_half(d51)};
+    s.thr[t][j][1] = (u32x4){dup_half(d40), dup_half(d20), dup_half(dd), 0u};
   }
 }
 
 // E4M3 code of amax / (6 gs): the truncation of an fp64 estimate (error
 // far below E4M3's spacing, and no overflow for any valid gs) is the exact
-// code or one below it; the exact threshold decides.
+// code or one below it; the exact threshold decides.  Both the normal and
+// the subnormal candidate are computed and one is selected (no branch).
 __device__ inline uint32_t scale_code(const uint16_t* th, uint32_t amax_bits, double inv6gs) {
   const double q = (double)__uint_as_float(amax_bits << 16) * inv6gs;
   const uint32_t hi = (uint32_t)((uint64_t)__double_as_longlong(q) >> 32);
   const int e = (int)(hi >> 20) - 1016;  // E4M3 exponent field for normal codes
-  uint32_t cand;
-  if (e >= 1) {
-    const int c = (e << 3) | (int)((hi >> 17) & 7);
-    cand = (uint32_t)(c > 126 ? 126 : c);
-  } else {
-    const double sub = q * 512.0;  // subnormal codes: m * 2^-9
-    cand = sub >= 7.0 ? 7u : (uint32_t)sub;
-  }
+  const int cn = (e << 3) | (int)((hi >> 17) & 7);
+  const uint32_t c_norm = (uint32_t)(cn > 126 ? 126 : cn);
+  const uint32_t c_sub = (uint32_t)fmin(q * 512.0, 7.0);  // subnormal codes: m * 2^-9
+  const uint32_t cand = e >= 1 ? c_norm : c_sub;
   return cand + (amax_bits > th[cand] ? 1u : 0u);
 }
 
@@ -218,28 +226,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         amax = amax > other ? amax : other;
         const int t = blk >= bpt ? 1 : 0;
         const uint32_t sc = scale_code(s.e4m3[t], amax, s.inv6gs[t]);
-        const u32x4 row = *reinterpret_cast<const u32x4*>(s.e2m1[t][sc]);
+        const u32x4 ra = s.thr[t][sc][0], rb = s.thr[t][sc][1];
         Thr th;
-        th.T0 = dup16(row.x);
-        th.T1 = dup16(row.x >> 16);
-        const uint32_t T2 = dup16(row.y), T4 = dup16(row.z), T5 = dup16(row.z >> 16);
-        const uint32_t T6 = dup16(row.w);
-        th.T3 = dup16(row.y >> 16);
-        th.D51 = pk_sub(T5, th.T1);
-        th.D40 = pk_sub(T4, th.T0);
-        th.D20 = pk_sub(T2, th.T0);
-        th.DD = pk_sub(pk_sub(T6, T4), th.D20);
+        th.T0 = ra.x;
+        th.T1 = ra.y;
+        th.T3 = ra.z;
+        th.D51 = ra.w;
+        th.D40 = rb.x;
+        th.D20 = rb.y;
+        th.DD = rb.z;
         // pairs (0,1),(2,3) -> nibbles e0..e3; pairs (4,5),(6,7) -> e4..e7
         const uint32_t n0 = encode_pair(w[0], th, k15, k8) | (encode_pair(w[1], th, k15, k8) << 8);
         const uint32_t n1 = encode_pair(w[2], th, k15, k8) | (encode_pair(w[3], th, k15, k8) << 8);
         const uint32_t h0w = n0 | (n0 >> 12), h1w = n1 | (n1 >> 12);
-        if (hb < hpp) {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(h1w, h0w, 0x05040100u), rout,
-                                                hb * 4, 0, KVFP4_CODEC_STORE_AUX);
-          if ((hb & 1) == 0)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + blk, 0,
-                                                 KVFP4_CODEC_STORE_AUX);
-        }
+        // half-blocks past the page and the odd lane's copy of the scale
+        // byte are given an offset past the buffer: the store is dropped
+        const bool in = hb < hpp;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(h1w, h0w, 0x05040100u), rout,
+                                              in ? hb * 4 : kNoStore, 0, KVFP4_CODEC_STORE_AUX);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout,
+                                             in && (hb & 1) == 0 ? data_bytes + blk : kNoStore, 0,
+                                             KVFP4_CODEC_STORE_AUX);
       }
     }
   }
