@@ -104,6 +104,26 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
                                const int32_t* dst_slots, int32_t num_pages,
                                const float* global_scale, void* stream);
 
+/* Quantize newly computed tokens straight into packed pages ("Accelerating
+ * Long-Context and Agentic Inference with NVFP4 KV Cache", Path 1: Prefill
+ * and Path 3: Decode: new K/V rows are written to the cache in NVFP4).
+ *   rows        bf16 [num_tokens][n_t][H][D], 16-byte aligned      (read)
+ *               (token i's K rows of every head, then its V rows)
+ *   token_slots int32 [num_tokens] packed slot of token i
+ *   token_rows  int32 [num_tokens] row (token position) within that page
+ *   packed_pool packed slots [packed_pool_pages][9*E/16 bytes]  (written)
+ *   global_scale HOST float [num_kv_tensors], as for kvfp4_quantize_pages.
+ * Row r of tensor t of the slot gets exactly the data and scale bytes that
+ * kvfp4_quantize_pages writes for that row; every other byte of the pool is
+ * left untouched.  Tokens whose slot is outside [0, packed_pool_pages) or
+ * whose row is outside [0, T) are skipped.  Two tokens naming the same
+ * (slot, row) race (unspecified winner).  num_tokens == 0 is a no-op;
+ * num_tokens * n_t * H * D must stay below 2^34. */
+int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t num_tokens,
+                              const int32_t* token_slots, const int32_t* token_rows,
+                              void* packed_pool, int32_t packed_pool_pages,
+                              const float* global_scale, void* stream);
+
 /* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
  * current device (0 is a valid answer). */
 size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,

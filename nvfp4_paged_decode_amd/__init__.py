@@ -27,7 +27,7 @@ KVFP4_ERR_HIP = -4
 #: Every function the header declares (checked by the CPU tests).
 EXPORTS = (
     "kvfp4_hot_page_bytes", "kvfp4_packed_page_bytes", "kvfp4_quantize_pages",
-    "kvfp4_dequantize_pages", "kvfp4_decode_workspace_bytes",
+    "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_decode_workspace_bytes",
     "kvfp4_paged_decode_attention", "kvfp4_status_string", "kvfp4_last_error_message",
 )
 
@@ -80,6 +80,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_quantize_pages.restype = I32
     lib.kvfp4_dequantize_pages.argtypes = codec
     lib.kvfp4_dequantize_pages.restype = I32
+    lib.kvfp4_append_quantize.argtypes = [G, P, I32, P, P, P, I32, P, P]
+    lib.kvfp4_append_quantize.restype = I32
     lib.kvfp4_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
     lib.kvfp4_decode_workspace_bytes.restype = SZ
     lib.kvfp4_paged_decode_attention.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32, P, I32,
@@ -159,6 +161,24 @@ def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, glob
         ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
         _ptr(src_slots), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
         _ptr(dst_slots), int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_append_quantize(geometry, rows, token_slots, token_rows, packed_pool, global_scale,
+                          stream=None) -> None:
+    """Quantize ``rows`` (bf16 ``[num_tokens, n_t, H, D]``) into row
+    ``token_rows[i]`` of packed slot ``token_slots[i]`` of ``packed_pool``."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    n = int(token_slots.shape[0])
+    if int(token_rows.shape[0]) != n:
+        raise ValueError("token_slots and token_rows differ in length")
+    per_token = g.num_kv_tensors * g.num_kv_heads * g.head_dim
+    if rows.numel() != n * per_token:
+        raise ValueError(f"rows holds {rows.numel()} values, expected {n} x {per_token}")
+    _check(lib.kvfp4_append_quantize(
+        ctypes.byref(g), _ptr(rows), n, _ptr(token_slots), _ptr(token_rows), _ptr(packed_pool),
+        _pages(packed_pool, kvfp4_packed_page_bytes(g)), _scales(global_scale, g.num_kv_tensors),
+        _stream(stream)))
 
 
 def kvfp4_decode_workspace_bytes(geometry, batch: int, num_q_heads: int, v_dim: int,

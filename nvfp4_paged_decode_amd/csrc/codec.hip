@@ -169,6 +169,37 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
 #ifndef KVFP4_CODEC_STORE_AUX
 #define KVFP4_CODEC_STORE_AUX 0
 #endif
+// One lane's half block (8 bf16 values in `a`) of tensor t -> the block's
+// E4M3 scale code (identical in both lanes of the pair) and the 4 data bytes
+// of its 8 nibbles.  The other half of the block must sit in lane ^ 1.
+__device__ inline void encode_half(const QuantLds& s, const u32x4& a, int t, uint32_t& sc,
+                                   uint32_t& word) {
+  const uint32_t k15 = 0x000F000Fu, k8 = 0x00080008u;
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  u16x2 mx = __builtin_elementwise_max(as_u16x2(w[0] & 0x7FFF7FFFu), as_u16x2(w[1] & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_u16x2(w[2] & 0x7FFF7FFFu));
+  mx = __builtin_elementwise_max(mx, as_u16x2(w[3] & 0x7FFF7FFFu));
+  uint32_t amax = mx.x > mx.y ? mx.x : mx.y;
+  // the partner lane holds the other half of the block
+  const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true);
+  amax = amax > other ? amax : other;
+  sc = scale_code(s.e4m3[t], amax, s.inv6gs[t]);
+  const u32x4 ra = s.thr[t][sc][0], rb = s.thr[t][sc][1];
+  Thr th;
+  th.T0 = ra.x;
+  th.T1 = ra.y;
+  th.T3 = ra.z;
+  th.D51 = ra.w;
+  th.D40 = rb.x;
+  th.D20 = rb.y;
+  th.DD = rb.z;
+  // pairs (0,1),(2,3) -> nibbles e0..e3; pairs (4,5),(6,7) -> e4..e7
+  const uint32_t n0 = encode_pair(w[0], th, k15, k8) | (encode_pair(w[1], th, k15, k8) << 8);
+  const uint32_t n1 = encode_pair(w[2], th, k15, k8) | (encode_pair(w[3], th, k15, k8) << 8);
+  const uint32_t h0w = n0 | (n0 >> 12), h1w = n1 | (n1 >> 12);
+  word = __builtin_amdgcn_perm(h1w, h0w, 0x05040100u);
+}
+
 #ifndef KVFP4_QUANT_UNROLL
 #define KVFP4_QUANT_UNROLL 8
 #endif
@@ -188,7 +219,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   __shared__ QuantLds s;
   build_quant_tables(s, g.nt, gs0, gs1);
   __syncthreads();
-  const uint32_t k15 = 0x000F000Fu, k8 = 0x00080008u;
   // A lane owns half a block (8 values): 16 contiguous input bytes, 4
   // output bytes; the two halves of a block sit in adjacent lanes.
   const int hpp = (int)(g.elems() / 8);  // half-blocks per page
@@ -216,39 +246,62 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       for (int u = 0; u < kQuantUnroll; ++u) {
         const int hb = h0 + u * kThreads + (int)threadIdx.x;
         const int blk = hb >> 1;
-        const uint32_t w[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
-        u16x2 mx = __builtin_elementwise_max(as_u16x2(w[0] & 0x7FFF7FFFu), as_u16x2(w[1] & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, as_u16x2(w[2] & 0x7FFF7FFFu));
-        mx = __builtin_elementwise_max(mx, as_u16x2(w[3] & 0x7FFF7FFFu));
-        uint32_t amax = mx.x > mx.y ? mx.x : mx.y;
-        // the partner lane holds the other half of the block
-        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true);
-        amax = amax > other ? amax : other;
         const int t = blk >= bpt ? 1 : 0;
-        const uint32_t sc = scale_code(s.e4m3[t], amax, s.inv6gs[t]);
-        const u32x4 ra = s.thr[t][sc][0], rb = s.thr[t][sc][1];
-        Thr th;
-        th.T0 = ra.x;
-        th.T1 = ra.y;
-        th.T3 = ra.z;
-        th.D51 = ra.w;
-        th.D40 = rb.x;
-        th.D20 = rb.y;
-        th.DD = rb.z;
-        // pairs (0,1),(2,3) -> nibbles e0..e3; pairs (4,5),(6,7) -> e4..e7
-        const uint32_t n0 = encode_pair(w[0], th, k15, k8) | (encode_pair(w[1], th, k15, k8) << 8);
-        const uint32_t n1 = encode_pair(w[2], th, k15, k8) | (encode_pair(w[3], th, k15, k8) << 8);
-        const uint32_t h0w = n0 | (n0 >> 12), h1w = n1 | (n1 >> 12);
+        uint32_t sc, word;
+        encode_half(s, a[u], t, sc, word);
         // half-blocks past the page and the odd lane's copy of the scale
         // byte are given an offset past the buffer: the store is dropped
         const bool in = hb < hpp;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(h1w, h0w, 0x05040100u), rout,
-                                              in ? hb * 4 : kNoStore, 0, KVFP4_CODEC_STORE_AUX);
+        __builtin_amdgcn_raw_buffer_store_b32(word, rout, in ? hb * 4 : kNoStore, 0,
+                                              KVFP4_CODEC_STORE_AUX);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout,
                                              in && (hb & 1) == 0 ? data_bytes + blk : kNoStore, 0,
                                              KVFP4_CODEC_STORE_AUX);
       }
     }
+  }
+}
+
+// Append: token i's rows (all tensors and heads, [n_t][H][D] bf16) go to
+// row token_rows[i] of packed slot token_slots[i].  A lane owns half a block
+// as above; consecutive lanes walk the tokens' rows, so the input is read
+// contiguously.  Only the token's own data and scale bytes are written.
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    Geom g, const uint8_t* __restrict__ rows, int num_tokens, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ page_rows, uint8_t* __restrict__ packed, int packed_pages,
+    float gs0, float gs1) {
+  __shared__ QuantLds s;
+  build_quant_tables(s, g.nt, gs0, gs1);
+  __syncthreads();
+  // The C ABI bounds num_tokens * half-blocks per token below 2^31.
+  const uint32_t hd8 = (uint32_t)(g.H * g.D / 8);     // half-blocks per tensor row (even)
+  const uint32_t hpt = (uint32_t)g.nt * hd8;           // half-blocks per token
+  const uint32_t total = hpt * (uint32_t)num_tokens;
+  const int data_bytes = (int)g.data_bytes();
+  const uint32_t stride = gridDim.x * kThreads;
+  // the loop bound is uniform over the workgroup: every lane runs the body,
+  // since the DPP exchange needs both halves of a block
+  for (uint32_t base = blockIdx.x * kThreads; base < total; base += stride) {
+    const uint32_t gi = base + threadIdx.x;
+    const bool live = gi < total;
+    const uint32_t tok = live ? gi / hpt : 0u;
+    const uint32_t j = gi - tok * hpt;
+    const uint32_t t = j >= hd8 ? 1u : 0u;
+    const uint32_t k = j - t * hd8;  // half-block within the tensor row
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (live) a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows) + gi);
+    uint32_t sc, word;
+    encode_half(s, a, (int)t, sc, word);
+    const int slot = live ? slots[tok] : -1;
+    const int r = live ? page_rows[tok] : -1;
+    if (slot < 0 || slot >= packed_pages || r < 0 || r >= g.T) continue;
+    uint8_t* page = packed + (long long)slot * g.packed_bytes();
+    auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, (int)g.packed_bytes(), kRsrcFlags);
+    const int hb = (int)((t * (uint32_t)g.T + (uint32_t)r) * hd8 + k);  // half-block in the page
+    __builtin_amdgcn_raw_buffer_store_b32(word, rout, hb * 4, 0, KVFP4_CODEC_STORE_AUX);
+    if ((k & 1u) == 0u)
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + (hb >> 1), 0,
+                                           KVFP4_CODEC_STORE_AUX);
   }
 }
 
@@ -362,6 +415,20 @@ hipError_t launch_quantize(const Geom& g, const void* hot, int hot_pages, const 
   hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)hot, hot_pages, src, (uint8_t*)packed, packed_pages, dst,
                      num_pages, gs[0], gs1);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Geom& g, const void* rows, int num_tokens, const int32_t* slots,
+                         const int32_t* page_rows, void* packed, int packed_pages, const float* gs,
+                         hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const float gs1 = g.nt > 1 ? gs[1] : gs[0];
+  const long long hb = (long long)g.nt * g.H * g.D / 8 * num_tokens;
+  long long grid = (hb + kThreads - 1) / kThreads;
+  if (grid > KVFP4_CODEC_GRID) grid = KVFP4_CODEC_GRID;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g,
+                     (const uint8_t*)rows, num_tokens, slots, page_rows, (uint8_t*)packed,
+                     packed_pages, gs[0], gs1);
   return hipGetLastError();
 }
 

@@ -138,20 +138,30 @@ def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
 BLOCK = 16
 
 
+def tensor_scale(gs) -> float:
+    """The FP32 tensor scale as a float.  The format fixes it as an FP32 value
+    and the exactness argument above needs its 24-bit significand, so a value
+    that FP32 cannot hold exactly is refused rather than silently used."""
+    v = float(gs)
+    if not (np.isfinite(v) and v > 0.0 and float(np.float32(v)) == v):
+        raise ValueError(f"tensor scale {v!r} is not a positive finite FP32 value")
+    return v
+
+
 def encode_block_scale(amax: np.ndarray, gs: float) -> np.ndarray:
     """E4M3 scale code for blocks with largest magnitude ``amax``.
 
     ``sb = E4M3_RNE_SAT(amax / (6 gs))``: the block maximum maps onto E2M1's
     largest magnitude (6) after the tensor scale is taken out.
     """
-    q = np.asarray(amax, dtype=np.float64) / (6.0 * float(gs))
+    q = np.asarray(amax, dtype=np.float64) / (6.0 * tensor_scale(gs))
     return round_half_even_to_grid(q, E4M3_FINITE)
 
 
 def encode_magnitudes(absx: np.ndarray, scale_value: np.ndarray, gs: float) -> np.ndarray:
     """E2M1 magnitude codes of ``|x| / (sb * gs)``; all zero where sb == 0."""
     absx = np.asarray(absx, dtype=np.float64)
-    denom = np.asarray(scale_value, dtype=np.float64) * float(gs)
+    denom = np.asarray(scale_value, dtype=np.float64) * tensor_scale(gs)
     safe = np.where(denom > 0, denom, 1.0)
     y = absx / safe
     codes = round_half_even_to_grid(y, E2M1_GRID)
@@ -199,7 +209,7 @@ def exact_values(nib: np.ndarray, scales: np.ndarray, gs: float) -> np.ndarray:
     mag = E2M1_GRID[nib & 7]
     sval = E4M3_TABLE[np.asarray(scales, dtype=np.int64)]
     sval = np.repeat(sval, BLOCK, axis=-1).reshape(*nib.shape[:-1], D)
-    v = mag * sval * float(gs)
+    v = mag * sval * tensor_scale(gs)
     return np.where((nib >> 3) & 1 == 1, -v, v)
 
 
@@ -278,3 +288,31 @@ def dequantize_pages(packed_pool: np.ndarray, g: Geometry, num_pages: int, gs,
         data, scales = split_packed_page(packed_pool[s], g)
         for t in range(g.num_kv_tensors):
             hot_pool[d, t] = dequantize_rows(data[t], scales[t], float(gs[t]))
+
+
+def append_quantize(rows: np.ndarray, g: Geometry, gs, packed_pool: np.ndarray,
+                    token_slots, token_rows) -> None:
+    """Quantize new tokens' K/V rows into rows of packed pages, in place.
+
+    The write path of the cache ("Accelerating Long-Context and Agentic
+    Inference with NVFP4 KV Cache", Path 1 / Path 3: each step's new K/V are
+    quantized into the NVFP4 pool as they are written).  A block is 16
+    values of one (tensor, token, head) row, so a token's blocks never share
+    a byte or a scale with another token: appending writes exactly that
+    token's data and scale bytes and leaves the rest of the page as it was.
+
+    ``rows``: uint16 bf16 bits ``[num_tokens, n_t, H, D]``; token i goes to
+    packed slot ``token_slots[i]``, page row ``token_rows[i]``; a token whose
+    slot is outside the pool or whose row is outside ``[0, page_size)`` is
+    skipped.
+    """
+    rows = np.asarray(rows, dtype=np.uint16)
+    for i in range(rows.shape[0]):
+        s, r = int(token_slots[i]), int(token_rows[i])
+        if not (0 <= s < packed_pool.shape[0] and 0 <= r < g.page_size):
+            continue
+        data, scales = split_packed_page(packed_pool[s], g)
+        for t in range(g.num_kv_tensors):
+            dt, sc = quantize_rows(rows[i, t], float(gs[t]))
+            data[t, r] = dt
+            scales[t, r] = sc

@@ -93,6 +93,39 @@ def test_codec_zero_pages_is_a_noop(lib):
                                     None) == K.KVFP4_OK
 
 
+def _append(lib, g, num_tokens=4, gs=(1.0, 1.0), rows=FAKE, slots=FAKE + 0x200,
+            prows=FAKE + 0x300, packed=FAKE + 0x400, packed_pages=8):
+    arr = (ctypes.c_float * 2)(*gs)
+    return lib.kvfp4_append_quantize(ctypes.byref(g) if g is not None else None, rows, num_tokens,
+                                     slots, prows, packed, packed_pages, arr, None)
+
+
+@pytest.mark.parametrize("case", [
+    dict(g=None),
+    dict(g=K.Geometry(2, 64, 8, 120)),
+    dict(num_tokens=-1),
+    dict(packed_pages=-1),
+    dict(rows=None),
+    dict(slots=None),
+    dict(prows=None),
+    dict(packed=None),
+    dict(rows=FAKE + 8),              # rows must be 16-byte aligned
+    dict(num_tokens=1 << 30),         # 2^30 tokens x 2048 values overflow the index space
+    dict(gs=(0.0, 1.0)),
+    dict(gs=(1.0, float("nan"))),
+    dict(gs=(1e36, 1.0)),
+])
+def test_append_rejects_invalid_arguments(lib, case):
+    g = case.pop("g", K.Geometry(2, 64, 8, 128))
+    assert _append(lib, g, **case) == K.KVFP4_ERR_INVALID_ARG
+    assert lib.kvfp4_last_error_message().decode() != ""
+
+
+def test_append_zero_tokens_is_a_noop(lib):
+    assert _append(lib, K.Geometry(2, 64, 8, 128), num_tokens=0, rows=None, slots=None,
+                   prows=None, packed=None) == K.KVFP4_OK
+
+
 def _decode(lib, g, gs=(1.0, 1.0), batch=2, hq=32, v_dim=128, hint=1024, ws=0, wsptr=None,
             pool=FAKE, q=FAKE, bt=FAKE, sl=FAKE, out=FAKE, scale=0.088, max_pages=16,
             pool_pages=64):

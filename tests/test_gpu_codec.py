@@ -85,7 +85,8 @@ def _block_zoo(rng, gs, n_pages, geometry):
 @pytest.mark.parametrize("geometry", [(2, 16, 1, 128), (2, 64, 8, 128), (1, 64, 1, 576),
                                       (2, 8, 3, 48)])
 @pytest.mark.parametrize("gs_val", [1.0, 2.0 ** -3, float(np.float32(0.0123456)),
-                                    float(np.float32(3.1e-5)), 2.0 ** -110, 1e30])
+                                    float(np.float32(3.1e-5)), 2.0 ** -110,
+                                    float(np.float32(1e30))])
 def test_quantize_dequantize_bit_exact(geometry, gs_val):
     require_gpu()
     rng = np.random.default_rng(hash((geometry, gs_val)) % 2 ** 32)
@@ -159,3 +160,88 @@ def test_cold_pages_full_size(gs_kind):
     data2, sc2 = packed2[:, :nd].reshape(-1, nb, 8), packed2[:, nd:]
     changed = np.any(data1 != data2, axis=-1) | (sc1 != sc2)
     assert set(np.unique(sc1[changed]).tolist()) <= {1, 2}
+
+
+def gpu_append(rows: np.ndarray, geometry, gs, slots, page_rows, pool: np.ndarray) -> np.ndarray:
+    """Append through the C ABI into a device copy of ``pool``; returns the pool."""
+    pool_d = dev(pool)
+    K.kvfp4_append_quantize(geometry, dev(rows.view(np.int16)), dev(np.asarray(slots, np.int32)),
+                            dev(np.asarray(page_rows, np.int32)), pool_d, gs)
+    return host(pool_d)
+
+
+@pytest.mark.parametrize("geometry,num_tokens", [
+    ((2, 64, 8, 128), 64),    # one decode step of a 64-sequence batch
+    ((2, 8, 3, 48), 37),      # 36 half-blocks a token: ragged last wave
+    ((1, 64, 1, 576), 129),   # MLA latent rows
+    ((2, 16, 1, 16), 5),      # one block a row
+])
+def test_append_bit_exact_and_touches_only_its_rows(geometry, num_tokens):
+    """Appended rows match the oracle byte for byte, over a pool filled with
+    noise: every byte outside the appended rows must keep its noise."""
+    require_gpu()
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(num_tokens)
+    n_slots = 2 * num_tokens // g.page_size + 3
+    pool = rng.integers(0, 256, (n_slots, O.packed_page_bytes(g)), dtype=np.uint8)
+    cells = rng.choice(n_slots * g.page_size, num_tokens, replace=False)
+    slots, page_rows = (cells // g.page_size).astype(np.int32), (cells % g.page_size).astype(np.int32)
+    per_token = g.num_kv_tensors * g.num_kv_heads * g.head_dim
+    zoo_pages = max(-(-num_tokens * per_token // g.elems), -(-300 * 16 // g.elems))
+    zoo = _block_zoo(rng, 0.37, zoo_pages, geometry).reshape(-1)[:num_tokens * per_token]
+    rows = np.ascontiguousarray(zoo.reshape(num_tokens, g.num_kv_tensors, g.num_kv_heads,
+                                            g.head_dim))
+    gs = [float(np.float32(0.37)), float(np.float32(0.011))][:g.num_kv_tensors]
+    ref = pool.copy()
+    O.append_quantize(rows, g, gs, ref, slots, page_rows)
+    got = gpu_append(rows, geometry, gs, slots, page_rows, pool)
+    mism = np.nonzero(got != ref)
+    assert mism[0].size == 0, f"{mism[0].size} bytes differ, first at {mism[0][0]},{mism[1][0]}"
+
+
+def test_append_skips_bad_slots_and_rows():
+    require_gpu()
+    geometry = (2, 16, 2, 64)
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(21)
+    rows = W.f32_to_bf16_bits(rng.standard_normal((6, 2, 2, 64)).astype(np.float32))
+    slots = np.array([0, -1, 3, 1, 2, 1], np.int32)    # -1 and 3 are outside a 3-slot pool
+    page_rows = np.array([5, 0, 0, 16, -2, 15], np.int32)  # 16 and -2 are outside the page
+    pool = np.full((3, O.packed_page_bytes(g)), 0x5A, np.uint8)
+    ref = pool.copy()
+    O.append_quantize(rows, g, [1.0, 0.25], ref, slots, page_rows)
+    got = gpu_append(rows, geometry, [1.0, 0.25], slots, page_rows, pool)
+    assert np.array_equal(got, ref)
+    changed = np.nonzero(np.any(ref != 0x5A, axis=1))[0]
+    assert changed.tolist() == [0, 1]  # only tokens 0 and 5 landed
+
+
+def test_append_prefill_full_size():
+    """A 16384-token prefill of Llama-3-8B KV rows (8 KV heads x 128) into
+    256 scattered 64-token pages: more half-blocks than the grid covers in
+    one pass.  Sampled tokens are checked against the oracle; the whole pool
+    must equal quantizing the assembled bf16 pages page by page."""
+    require_gpu()
+    geometry = (2, 64, 8, 128)
+    g = O.Geometry(*geometry)
+    n_pages, n_tok = 256, 16384
+    rng = np.random.default_rng(5)
+    hot = W.f32_to_bf16_bits((rng.standard_normal((n_pages, *g.row_shape))
+                              * rng.uniform(0.1, 8.0, (n_pages, 2, 1, 8, 1))).astype(np.float32))
+    dst = rng.permutation(n_pages + 7)[:n_pages].astype(np.int32)
+    tok = np.arange(n_tok)
+    slots, page_rows = dst[tok // 64], (tok % 64).astype(np.int32)
+    rows = np.ascontiguousarray(hot.transpose(0, 2, 1, 3, 4).reshape(n_tok, 2, 8, 128))
+    gs = [float(np.float32(0.05)), float(np.float32(0.02))]
+    pool = np.zeros((n_pages + 7, O.packed_page_bytes(g)), np.uint8)
+    got = gpu_append(rows, geometry, gs, slots, page_rows, pool)
+    whole = gpu_quantize(hot, geometry, gs, dst=dst, packed_slots=n_pages + 7)
+    assert np.array_equal(got, whole)
+    sample = np.concatenate([[0, n_tok - 1], rng.choice(n_tok, 40, replace=False)])
+    ref = np.zeros_like(pool)
+    O.append_quantize(rows[sample], g, gs, ref, slots[sample], page_rows[sample])
+    data_idx, scale_idx = O.split_packed_page(np.arange(O.packed_page_bytes(g)), g)
+    for i in sample:
+        s, r = slots[i], page_rows[i]
+        idx = np.concatenate([data_idx[:, r].reshape(-1), scale_idx[:, r].reshape(-1)])
+        assert np.array_equal(got[s, idx], ref[s, idx]), f"token {i}"

@@ -159,3 +159,40 @@ def test_golden_page_bytes_are_stable():
     back = np.zeros_like(z["hot"])
     O.dequantize_pages(packed, g, 1, z["gs"], back)
     assert np.array_equal(back, z["dequant"])
+
+
+def test_append_rows_rebuild_the_page_and_touch_nothing_else():
+    """Appending a page's tokens one at a time, in any order, gives the same
+    bytes as encoding the whole page (a block never spans two tokens), and
+    each append writes only its own row's data and scale bytes."""
+    g = O.Geometry(2, 8, 3, 32)
+    rng = np.random.default_rng(11)
+    hot = _random_blocks(rng, g.elems // 16).reshape(1, *g.row_shape)
+    gs = [float(np.float32(0.7)), float(np.float32(0.02))]
+    whole = np.zeros((1, O.packed_page_bytes(g)), np.uint8)
+    O.quantize_pages(hot, g, 1, gs, whole)
+    rows = np.ascontiguousarray(hot[0].transpose(1, 0, 2, 3))  # [T, n_t, H, D]
+    order = rng.permutation(g.page_size)
+    built = np.full((2, O.packed_page_bytes(g)), 0xA5, np.uint8)
+    for r in order:
+        before = built.copy()
+        O.append_quantize(rows[r:r + 1], g, gs, built, [0], [r])
+        changed = np.nonzero(before[0] != built[0])[0]
+        data, scales = O.split_packed_page(np.arange(O.packed_page_bytes(g)), g)
+        allowed = set(data[:, r].reshape(-1)) | set(scales[:, r].reshape(-1))
+        assert set(changed.tolist()) <= allowed
+        assert np.array_equal(before[1], built[1])  # other slot untouched
+    assert np.array_equal(built[0], whole[0])
+
+
+def test_append_skips_bad_slots_and_rows():
+    g = O.Geometry(1, 4, 1, 16)
+    rng = np.random.default_rng(12)
+    rows = _random_blocks(rng, 3).reshape(3, 1, 1, 16)
+    pool = np.zeros((2, O.packed_page_bytes(g)), np.uint8)
+    O.append_quantize(rows, g, [1.0], pool, [2, -1, 0], [0, 1, 4])
+    assert np.all(pool == 0)
+    O.append_quantize(rows, g, [1.0], pool, [1, 1, 1], [3, 3, 0])
+    d, s = O.quantize_rows(rows[2, 0], 1.0)
+    data, scales = O.split_packed_page(pool[1], g)
+    assert np.array_equal(data[0, 0], d) and np.array_equal(scales[0, 0], s)
