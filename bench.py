@@ -53,6 +53,8 @@ def parse():
                    help="approximate host time budget of the oracle sample")
     p.add_argument("--no-copy-yardstick", action="store_true",
                    help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
+    p.add_argument("--no-append", action="store_true",
+                   help="skip timing the write path (append-quantize), reported beside the step")
     return p.parse_args()
 
 
@@ -73,6 +75,62 @@ def codec_bytes(geometry, pages: int) -> int:
     nt, T, H, D = geometry
     e = nt * T * H * D
     return pages * (2 * e + e * 9 // 16)
+
+
+def append_bytes(geometry, tokens: int, elem_bytes: int) -> int:
+    """Algorithmic bytes of appending `tokens` rows: the input rows, the
+    packed data and scale bytes written, the two int32 slot/row entries."""
+    nt, T, H, D = geometry
+    per = nt * H * D
+    return tokens * (per * elem_bytes + per * 9 // 16 + 8)
+
+
+def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, warmup):
+    """The write path, timed beside the step (not part of it): a prefill of
+    up to 256 of the workload's pages appended token by token (bf16 rows, and
+    the same values as FP8 rows), and one decode step that rewrites the last
+    cached token of every sequence."""
+    nt, T, H, D = geometry
+    dev = hot.device
+    used = torch.from_numpy(wl.used_slots[:256].astype(np.int64)).to(dev)
+    n_pages = int(used.shape[0])
+    pages = hot.view(wl.num_slots, nt, T, H, D)[used]
+    rows = pages.permute(0, 2, 1, 3, 4).reshape(n_pages * T, nt, H, D).contiguous()
+    tok_slots = used.to(torch.int32).repeat_interleave(T)
+    tok_rows = torch.arange(T, dtype=torch.int32, device=dev).repeat(n_pages)
+    amax = rows.view(torch.bfloat16).float().abs().max().clamp_min(1e-30)
+    rows8 = (rows.view(torch.bfloat16).float() * (448.0 / amax)).to(torch.float8_e4m3fn)
+    rows8 = rows8.view(torch.uint8).contiguous()
+    L = wl.seq_lens.astype(np.int64)
+    last = np.maximum(L - 1, 0)
+    dslots = torch.from_numpy(wl.block_table[np.arange(wl.batch), last // T].astype(np.int32)).to(dev)
+    drows = torch.from_numpy((last % T).astype(np.int32)).to(dev)
+    drow_data = rows[:wl.batch].contiguous()
+    cases = [("prefill_bf16", rows, tok_slots, tok_rows, 2),
+             ("prefill_fp8", rows8, tok_slots, tok_rows, 1),
+             ("decode_step_bf16", drow_data, dslots, drows, 2)]
+    res = {}
+    for name, r, ts, tr, eb in cases:
+        def fn():
+            K.kvfp4_append_quantize(geometry, r, ts, tr, packed, gs)
+        for _ in range(warmup):
+            fn()
+        evs = []
+        for _ in range(steps):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        ntok = int(ts.shape[0])
+        b = append_bytes(geometry, ntok, eb)
+        res[name] = {"tokens": ntok, "avg_us": round(us, 2), "bytes": b,
+                     "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    return res
 
 
 def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
@@ -302,6 +360,11 @@ def main():
     else:
         wdesc = f"cold_pages: {pages} pages x {geometry}; step = encode + decode of every page"
 
+    append = None
+    if wl is not None and not args.no_append:
+        append = time_append(K, torch, wl, geometry, gs, hot, packed, stream,
+                             (lambda: None) if args.no_flush else evict, args.steps, args.warmup)
+
     cpu = None
     if wl is not None and not args.no_cpu_baseline:
         try:
@@ -323,6 +386,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kern,
         "copy_yardstick": copy,
+        "append_write_path": append,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),

@@ -104,11 +104,18 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
                                const int32_t* dst_slots, int32_t num_pages,
                                const float* global_scale, void* stream);
 
+/* Element types of kvfp4_append_quantize's input rows. */
+#define KVFP4_ROWS_BF16 0     /* bf16, 2 bytes a value                          */
+#define KVFP4_ROWS_FP8_E4M3 1 /* OCP E4M3FN, 1 byte a value (NaN codes: unspecified) */
+
 /* Quantize newly computed tokens straight into packed pages ("Accelerating
- * Long-Context and Agentic Inference with NVFP4 KV Cache", Path 1: Prefill
- * and Path 3: Decode: new K/V rows are written to the cache in NVFP4).
- *   rows        bf16 [num_tokens][n_t][H][D], 16-byte aligned      (read)
- *               (token i's K rows of every head, then its V rows)
+ * Long-Context and Agentic Inference with NVFP4 KV Cache", Path 1: Initial
+ * prefill, Path 2: the current chunk, Path 3: Decode -- the new K/V, bf16
+ * or FP8, are quantized into the NVFP4 cache as they are written).
+ *   rows        [num_tokens][n_t][H][D] of rows_dtype, 16-byte aligned (read)
+ *               (token i's K rows of every head, then its V rows).  An FP8
+ *               value is widened exactly (every finite E4M3 value is a bf16
+ *               value) and encoded as that bf16 value.
  *   token_slots int32 [num_tokens] packed slot of token i
  *   token_rows  int32 [num_tokens] row (token position) within that page
  *   packed_pool packed slots [packed_pool_pages][9*E/16 bytes]  (written)
@@ -119,10 +126,11 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
  * whose row is outside [0, T) are skipped.  Two tokens naming the same
  * (slot, row) race (unspecified winner).  num_tokens == 0 is a no-op;
  * num_tokens * n_t * H * D must stay below 2^34. */
-int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t num_tokens,
-                              const int32_t* token_slots, const int32_t* token_rows,
-                              void* packed_pool, int32_t packed_pool_pages,
-                              const float* global_scale, void* stream);
+int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t rows_dtype,
+                              int32_t num_tokens, const int32_t* token_slots,
+                              const int32_t* token_rows, void* packed_pool,
+                              int32_t packed_pool_pages, const float* global_scale,
+                              void* stream);
 
 /* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
  * current device (0 is a valid answer). */

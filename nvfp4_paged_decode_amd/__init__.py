@@ -23,6 +23,8 @@ KVFP4_ERR_INVALID_ARG = -1
 KVFP4_ERR_UNSUPPORTED = -2
 KVFP4_ERR_WORKSPACE = -3
 KVFP4_ERR_HIP = -4
+KVFP4_ROWS_BF16 = 0
+KVFP4_ROWS_FP8_E4M3 = 1
 
 #: Every function the header declares (checked by the CPU tests).
 EXPORTS = (
@@ -80,7 +82,7 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_quantize_pages.restype = I32
     lib.kvfp4_dequantize_pages.argtypes = codec
     lib.kvfp4_dequantize_pages.restype = I32
-    lib.kvfp4_append_quantize.argtypes = [G, P, I32, P, P, P, I32, P, P]
+    lib.kvfp4_append_quantize.argtypes = [G, P, I32, I32, P, P, P, I32, P, P]
     lib.kvfp4_append_quantize.restype = I32
     lib.kvfp4_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
     lib.kvfp4_decode_workspace_bytes.restype = SZ
@@ -164,19 +166,25 @@ def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, glob
 
 
 def kvfp4_append_quantize(geometry, rows, token_slots, token_rows, packed_pool, global_scale,
-                          stream=None) -> None:
-    """Quantize ``rows`` (bf16 ``[num_tokens, n_t, H, D]``) into row
-    ``token_rows[i]`` of packed slot ``token_slots[i]`` of ``packed_pool``."""
+                          rows_dtype: Optional[int] = None, stream=None) -> None:
+    """Quantize ``rows`` (``[num_tokens, n_t, H, D]``: 2-byte elements are
+    bf16 bits, 1-byte elements E4M3FN codes unless ``rows_dtype`` says so)
+    into row ``token_rows[i]`` of packed slot ``token_slots[i]``."""
     lib = load_library()
     g = Geometry.of(geometry)
     n = int(token_slots.shape[0])
     if int(token_rows.shape[0]) != n:
         raise ValueError("token_slots and token_rows differ in length")
+    if rows_dtype is None:
+        rows_dtype = KVFP4_ROWS_FP8_E4M3 if rows.element_size() == 1 else KVFP4_ROWS_BF16
+    width = 1 if rows_dtype == KVFP4_ROWS_FP8_E4M3 else 2
     per_token = g.num_kv_tensors * g.num_kv_heads * g.head_dim
-    if rows.numel() != n * per_token:
-        raise ValueError(f"rows holds {rows.numel()} values, expected {n} x {per_token}")
+    if rows.numel() * rows.element_size() != n * per_token * width:
+        raise ValueError(f"rows holds {rows.numel() * rows.element_size()} bytes, expected "
+                         f"{n} tokens x {per_token} values x {width} bytes")
     _check(lib.kvfp4_append_quantize(
-        ctypes.byref(g), _ptr(rows), n, _ptr(token_slots), _ptr(token_rows), _ptr(packed_pool),
+        ctypes.byref(g), _ptr(rows), int(rows_dtype), n, _ptr(token_slots), _ptr(token_rows),
+        _ptr(packed_pool),
         _pages(packed_pool, kvfp4_packed_page_bytes(g)), _scales(global_scale, g.num_kv_tensors),
         _stream(stream)))
 

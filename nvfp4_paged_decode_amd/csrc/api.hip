@@ -150,12 +150,16 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
   return ok();
 }
 
-int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t num_tokens,
-                              const int32_t* token_slots, const int32_t* token_rows,
-                              void* packed_pool, int32_t packed_pool_pages,
-                              const float* global_scale, void* stream) {
+int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t rows_dtype,
+                              int32_t num_tokens, const int32_t* token_slots,
+                              const int32_t* token_rows, void* packed_pool,
+                              int32_t packed_pool_pages, const float* global_scale,
+                              void* stream) {
   int32_t st = check_geometry(g);
   if (st) return st;
+  if (rows_dtype != KVFP4_ROWS_BF16 && rows_dtype != KVFP4_ROWS_FP8_E4M3)
+    return fail(KVFP4_ERR_INVALID_ARG, "rows_dtype = %d is not KVFP4_ROWS_BF16 or "
+                "KVFP4_ROWS_FP8_E4M3", rows_dtype);
   if (num_tokens < 0) return fail(KVFP4_ERR_INVALID_ARG, "num_tokens = %d < 0", num_tokens);
   if (packed_pool_pages < 0)
     return fail(KVFP4_ERR_INVALID_ARG, "packed_pool_pages = %d < 0", packed_pool_pages);
@@ -172,7 +176,8 @@ int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t
                 num_tokens, per_token);
   st = check_scales(g, global_scale);
   if (st) return st;
-  hipError_t e = kvfp4::launch_append(to_geom(g), rows, num_tokens, token_slots, token_rows,
+  hipError_t e = kvfp4::launch_append(to_geom(g), rows, rows_dtype == KVFP4_ROWS_FP8_E4M3,
+                                      num_tokens, token_slots, token_rows,
                                       packed_pool, packed_pool_pages, global_scale,
                                       (hipStream_t)stream);
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "append launch: %s", hipGetErrorString(e));

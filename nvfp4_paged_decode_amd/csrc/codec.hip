@@ -262,46 +262,104 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   }
 }
 
-// Append: token i's rows (all tensors and heads, [n_t][H][D] bf16) go to
-// row token_rows[i] of packed slot token_slots[i].  A lane owns half a block
-// as above; consecutive lanes walk the tokens' rows, so the input is read
+// Append: token i's rows (all tensors and heads, [n_t][H][D]) go to row
+// token_rows[i] of packed slot token_slots[i].  A lane owns half a block as
+// above; consecutive lanes walk the tokens' rows, so the input is read
 // contiguously.  Only the token's own data and scale bytes are written.
+// kFp8: the input is OCP E4M3FN bytes instead of bf16.  Every finite E4M3
+// value is a bf16 value, so the codes are widened to bf16 exactly (the
+// gfx950 convert with scale 1) and encoded like bf16 input.
+// Large appends (prefill) keep 4 half-blocks in flight per lane; a decode
+// step's few tokens spread one half-block a lane over more workgroups,
+// which measured faster (latency, not bandwidth, bounds them).
+constexpr int kAppendUnroll = 4;
+constexpr long long kAppendSmall = 256LL * kThreads;  // half-blocks: one per lane below this
+// Each workgroup builds its own threshold tables (about 2.5k fp64
+// roundings): with 1024 workgroups that work hides behind the first loads,
+// with 4096 it measured 5.5 us of extra time.
+#ifndef KVFP4_APPEND_GRID
+#define KVFP4_APPEND_GRID 1024
+#endif
+
+struct AppendIn {
+  u32x4 a;        // 8 values as bf16 pairs
+  int slot, row;  // destination; slot -1 for lanes past the end
+  uint32_t t, k;  // tensor, half-block within the tensor row
+};
+
+template <bool kFp8>
+__device__ inline void append_load(AppendIn& in, uint32_t gi, uint32_t total, uint32_t hpt,
+                                   uint32_t hd8, const uint8_t* rows, const int32_t* slots,
+                                   const int32_t* page_rows) {
+  const bool live = gi < total;
+  const uint32_t tok = live ? gi / hpt : 0u;
+  const uint32_t j = gi - tok * hpt;
+  in.t = j >= hd8 ? 1u : 0u;
+  in.k = j - in.t * hd8;
+  in.slot = live ? slots[tok] : -1;
+  in.row = live ? page_rows[tok] : -1;
+  if constexpr (kFp8) {
+    u32x2 c = {0u, 0u};
+    if (live) c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(rows) + gi);
+    in.a.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
+    in.a.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
+    in.a.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
+    in.a.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
+  } else {
+    in.a = (u32x4){0u, 0u, 0u, 0u};
+    if (live) in.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows) + gi);
+  }
+}
+
+template <bool kFp8, int kUnroll>
 __global__ __launch_bounds__(kThreads) void append_kernel(
     Geom g, const uint8_t* __restrict__ rows, int num_tokens, const int32_t* __restrict__ slots,
     const int32_t* __restrict__ page_rows, uint8_t* __restrict__ packed, int packed_pages,
     float gs0, float gs1) {
   __shared__ QuantLds s;
-  build_quant_tables(s, g.nt, gs0, gs1);
-  __syncthreads();
   // The C ABI bounds num_tokens * half-blocks per token below 2^31.
   const uint32_t hd8 = (uint32_t)(g.H * g.D / 8);     // half-blocks per tensor row (even)
   const uint32_t hpt = (uint32_t)g.nt * hd8;           // half-blocks per token
   const uint32_t total = hpt * (uint32_t)num_tokens;
   const int data_bytes = (int)g.data_bytes();
-  const uint32_t stride = gridDim.x * kThreads;
+  const int page_bytes = (int)g.packed_bytes();
+  constexpr uint32_t chunk = kThreads * kUnroll;
+  const uint32_t stride = gridDim.x * chunk;
+  const uint32_t first = blockIdx.x * chunk;
+  // the first inputs are requested before the tables are built, so that
+  // their latency hides behind the table arithmetic
+  AppendIn in[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    append_load<kFp8>(in[u], first + u * kThreads + threadIdx.x, total, hpt, hd8, rows, slots,
+                      page_rows);
+  build_quant_tables(s, g.nt, gs0, gs1);
+  __syncthreads();
   // the loop bound is uniform over the workgroup: every lane runs the body,
   // since the DPP exchange needs both halves of a block
-  for (uint32_t base = blockIdx.x * kThreads; base < total; base += stride) {
-    const uint32_t gi = base + threadIdx.x;
-    const bool live = gi < total;
-    const uint32_t tok = live ? gi / hpt : 0u;
-    const uint32_t j = gi - tok * hpt;
-    const uint32_t t = j >= hd8 ? 1u : 0u;
-    const uint32_t k = j - t * hd8;  // half-block within the tensor row
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (live) a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rows) + gi);
-    uint32_t sc, word;
-    encode_half(s, a, (int)t, sc, word);
-    const int slot = live ? slots[tok] : -1;
-    const int r = live ? page_rows[tok] : -1;
-    if (slot < 0 || slot >= packed_pages || r < 0 || r >= g.T) continue;
-    uint8_t* page = packed + (long long)slot * g.packed_bytes();
-    auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, (int)g.packed_bytes(), kRsrcFlags);
-    const int hb = (int)((t * (uint32_t)g.T + (uint32_t)r) * hd8 + k);  // half-block in the page
-    __builtin_amdgcn_raw_buffer_store_b32(word, rout, hb * 4, 0, KVFP4_CODEC_STORE_AUX);
-    if ((k & 1u) == 0u)
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + (hb >> 1), 0,
-                                           KVFP4_CODEC_STORE_AUX);
+  for (uint32_t base = first; base < total; base += stride) {
+    if (base != first) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        append_load<kFp8>(in[u], base + u * kThreads + threadIdx.x, total, hpt, hd8, rows, slots,
+                          page_rows);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t sc, word;
+      encode_half(s, in[u].a, (int)in[u].t, sc, word);
+      // lanes past the end, bad slots and bad rows store nothing
+      const bool ok = in[u].slot >= 0 && in[u].slot < packed_pages && in[u].row >= 0 &&
+                      in[u].row < g.T;
+      if (!ok) continue;
+      uint8_t* page = packed + (long long)in[u].slot * page_bytes;
+      auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, page_bytes, kRsrcFlags);
+      const int hb = (int)((in[u].t * (uint32_t)g.T + (uint32_t)in[u].row) * hd8 + in[u].k);
+      __builtin_amdgcn_raw_buffer_store_b32(word, rout, hb * 4, 0, KVFP4_CODEC_STORE_AUX);
+      if ((in[u].k & 1u) == 0u)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout, data_bytes + (hb >> 1), 0,
+                                             KVFP4_CODEC_STORE_AUX);
+    }
   }
 }
 
@@ -418,15 +476,19 @@ hipError_t launch_quantize(const Geom& g, const void* hot, int hot_pages, const 
   return hipGetLastError();
 }
 
-hipError_t launch_append(const Geom& g, const void* rows, int num_tokens, const int32_t* slots,
-                         const int32_t* page_rows, void* packed, int packed_pages, const float* gs,
-                         hipStream_t stream) {
+hipError_t launch_append(const Geom& g, const void* rows, bool fp8, int num_tokens,
+                         const int32_t* slots, const int32_t* page_rows, void* packed,
+                         int packed_pages, const float* gs, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const float gs1 = g.nt > 1 ? gs[1] : gs[0];
   const long long hb = (long long)g.nt * g.H * g.D / 8 * num_tokens;
-  long long grid = (hb + kThreads - 1) / kThreads;
-  if (grid > KVFP4_CODEC_GRID) grid = KVFP4_CODEC_GRID;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g,
+  const bool small = hb <= kAppendSmall;
+  const int unroll = small ? 1 : kAppendUnroll;
+  long long grid = (hb + kThreads * unroll - 1) / (kThreads * unroll);
+  if (grid > KVFP4_APPEND_GRID) grid = KVFP4_APPEND_GRID;
+  auto kernel = fp8 ? (small ? append_kernel<true, 1> : append_kernel<true, kAppendUnroll>)
+                    : (small ? append_kernel<false, 1> : append_kernel<false, kAppendUnroll>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)rows, num_tokens, slots, page_rows, (uint8_t*)packed,
                      packed_pages, gs[0], gs1);
   return hipGetLastError();

@@ -115,9 +115,9 @@ hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages
                              const int32_t* src, void* hot, int hot_pages, const int32_t* dst,
                              int num_pages, const float* gs, hipStream_t stream);
 
-hipError_t launch_append(const Geom& g, const void* rows, int num_tokens, const int32_t* slots,
-                         const int32_t* page_rows, void* packed, int packed_pages, const float* gs,
-                         hipStream_t stream);
+hipError_t launch_append(const Geom& g, const void* rows, bool fp8, int num_tokens,
+                         const int32_t* slots, const int32_t* page_rows, void* packed,
+                         int packed_pages, const float* gs, hipStream_t stream);
 
 struct DecodeArgs {
   Geom g;

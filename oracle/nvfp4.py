@@ -131,6 +131,24 @@ def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
     return bits
 
 
+def e4m3_codes_to_bf16_bits(codes: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of OCP E4M3FN bytes, exactly.
+
+    Every finite E4M3 value (4 significant bits, magnitudes 2**-9 .. 448) is
+    a bf16 value, so the widening is exact; a NaN code is refused.  This is
+    how FP8 K/V (the pages' prefill and workspace type, "Accelerating
+    Long-Context and Agentic Inference with NVFP4 KV Cache", Path 1) enter
+    the NVFP4 encoder: as the bf16 values they equal.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    v = E4M3_TABLE[codes.astype(np.int64)]
+    if np.any(np.isnan(v)):
+        raise ValueError("E4M3 NaN codes (0x7F, 0xFF) are outside the contract")
+    bits = f64_to_bf16_rne(v)
+    assert np.array_equal(bf16_bits_to_f64(bits), v)
+    return bits
+
+
 # ----------------------------------------------------------------------------
 # Block codec
 # ----------------------------------------------------------------------------
@@ -301,11 +319,15 @@ def append_quantize(rows: np.ndarray, g: Geometry, gs, packed_pool: np.ndarray,
     a byte or a scale with another token: appending writes exactly that
     token's data and scale bytes and leaves the rest of the page as it was.
 
-    ``rows``: uint16 bf16 bits ``[num_tokens, n_t, H, D]``; token i goes to
-    packed slot ``token_slots[i]``, page row ``token_rows[i]``; a token whose
-    slot is outside the pool or whose row is outside ``[0, page_size)`` is
-    skipped.
+    ``rows``: ``[num_tokens, n_t, H, D]`` of uint16 bf16 bits, or of uint8
+    E4M3FN codes (FP8 K/V), which are encoded as the bf16 values they equal;
+    token i goes to packed slot ``token_slots[i]``, page row
+    ``token_rows[i]``; a token whose slot is outside the pool or whose row is
+    outside ``[0, page_size)`` is skipped.
     """
+    rows = np.asarray(rows)
+    if rows.dtype == np.uint8:
+        rows = e4m3_codes_to_bf16_bits(rows)
     rows = np.asarray(rows, dtype=np.uint16)
     for i in range(rows.shape[0]):
         s, r = int(token_slots[i]), int(token_rows[i])

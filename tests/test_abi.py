@@ -94,10 +94,10 @@ def test_codec_zero_pages_is_a_noop(lib):
 
 
 def _append(lib, g, num_tokens=4, gs=(1.0, 1.0), rows=FAKE, slots=FAKE + 0x200,
-            prows=FAKE + 0x300, packed=FAKE + 0x400, packed_pages=8):
+            prows=FAKE + 0x300, packed=FAKE + 0x400, packed_pages=8, dtype=K.KVFP4_ROWS_BF16):
     arr = (ctypes.c_float * 2)(*gs)
-    return lib.kvfp4_append_quantize(ctypes.byref(g) if g is not None else None, rows, num_tokens,
-                                     slots, prows, packed, packed_pages, arr, None)
+    return lib.kvfp4_append_quantize(ctypes.byref(g) if g is not None else None, rows, dtype,
+                                     num_tokens, slots, prows, packed, packed_pages, arr, None)
 
 
 @pytest.mark.parametrize("case", [
@@ -110,6 +110,9 @@ def _append(lib, g, num_tokens=4, gs=(1.0, 1.0), rows=FAKE, slots=FAKE + 0x200,
     dict(prows=None),
     dict(packed=None),
     dict(rows=FAKE + 8),              # rows must be 16-byte aligned
+    dict(rows=FAKE + 8, dtype=K.KVFP4_ROWS_FP8_E4M3),
+    dict(dtype=2),
+    dict(dtype=-1),
     dict(num_tokens=1 << 30),         # 2^30 tokens x 2048 values overflow the index space
     dict(gs=(0.0, 1.0)),
     dict(gs=(1.0, float("nan"))),

@@ -175,6 +175,7 @@ def gpu_append(rows: np.ndarray, geometry, gs, slots, page_rows, pool: np.ndarra
     ((2, 8, 3, 48), 37),      # 36 half-blocks a token: ragged last wave
     ((1, 64, 1, 576), 129),   # MLA latent rows
     ((2, 16, 1, 16), 5),      # one block a row
+    ((2, 8, 3, 48), 2001),    # past the one-half-block-a-lane size: 4 a lane, ragged
 ])
 def test_append_bit_exact_and_touches_only_its_rows(geometry, num_tokens):
     """Appended rows match the oracle byte for byte, over a pool filled with
@@ -245,3 +246,41 @@ def test_append_prefill_full_size():
         s, r = slots[i], page_rows[i]
         idx = np.concatenate([data_idx[:, r].reshape(-1), scale_idx[:, r].reshape(-1)])
         assert np.array_equal(got[s, idx], ref[s, idx]), f"token {i}"
+
+
+@pytest.mark.parametrize("geometry,num_tokens", [((2, 64, 8, 128), 96), ((2, 8, 3, 48), 37),
+                                                 ((1, 64, 1, 576), 40), ((2, 64, 8, 128), 300)])
+@pytest.mark.parametrize("gs_pair", [(1.0, 1.0), (float(np.float32(0.0123)), 2.0 ** -7),
+                                     (float(np.float32(3.3)), float(np.float32(0.71)))])
+def test_append_fp8_rows_bit_exact(geometry, num_tokens, gs_pair):
+    """FP8 (E4M3FN) input rows: every finite code appears, in blocks of mixed
+    and of uniform magnitude range, over a noise-filled pool."""
+    require_gpu()
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(num_tokens * 7 + int(gs_pair[0] * 100))
+    per_token = g.num_kv_tensors * g.num_kv_heads * g.head_dim
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = rng.choice(finite, num_tokens * per_token)
+    codes[:finite.size] = finite
+    blocks = codes.reshape(-1, 16)
+    nb = blocks.shape[0]
+    # blocks drawn from one binade band each: small (subnormal) to large codes
+    for i in rng.choice(nb, nb // 2, replace=False):
+        lo = rng.integers(0, 0x70)
+        blocks[i] = rng.integers(lo, lo + 16, 16) | (rng.integers(0, 2, 16) << 7)
+    blocks[blocks == 0x7F] = 0x7E
+    blocks[blocks == 0xFF] = 0xFE
+    rows = np.ascontiguousarray(blocks.reshape(num_tokens, g.num_kv_tensors, g.num_kv_heads,
+                                               g.head_dim).astype(np.uint8))
+    n_slots = num_tokens // g.page_size + 3
+    pool = rng.integers(0, 256, (n_slots, O.packed_page_bytes(g)), dtype=np.uint8)
+    cells = rng.choice(n_slots * g.page_size, num_tokens, replace=False)
+    slots, page_rows = (cells // g.page_size).astype(np.int32), (cells % g.page_size).astype(np.int32)
+    gs = list(gs_pair)[:g.num_kv_tensors]
+    ref = pool.copy()
+    O.append_quantize(rows, g, gs, ref, slots, page_rows)
+    pool_d = dev(pool)
+    K.kvfp4_append_quantize(geometry, dev(rows), dev(slots), dev(page_rows), pool_d, gs)
+    got = host(pool_d)
+    mism = np.nonzero(got != ref)
+    assert mism[0].size == 0, f"{mism[0].size} bytes differ, first at {mism[0][0]},{mism[1][0]}"

@@ -29,6 +29,20 @@ def test_e4m3_decode_matches_torch_for_all_256_codes():
     assert np.all(np.diff(O.E4M3_FINITE) > 0)
 
 
+def test_e4m3_widens_to_bf16_exactly_like_torch():
+    # FP8 K/V enter the encoder as bf16; torch's float8_e4m3fn -> bfloat16
+    # cast is an independent implementation of that widening
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    ours = O.e4m3_codes_to_bf16_bits(codes)
+    assert np.array_equal(ref.view(torch.int16).numpy().view(np.uint16), ours)
+    # -0, 2**-9 (smallest subnormal) and -448
+    assert O.e4m3_codes_to_bf16_bits(np.array([0x80, 0x01, 0xFE], np.uint8)).tolist() == \
+        [0x8000, 0x3B00, 0xC3E0]
+    with pytest.raises(ValueError):
+        O.e4m3_codes_to_bf16_bits(np.array([0x7F], np.uint8))
+
+
 def test_e4m3_encode_matches_torch_on_every_bf16_value():
     # every non-negative finite bf16 value up to 464 (above that torch gives
     # NaN, the oracle saturates); torch's fp32 -> e4m3fn cast rounds to
