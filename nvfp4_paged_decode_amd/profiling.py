@@ -14,8 +14,8 @@ Two commands, each printing a short text summary (to stdout or --out):
       benchmark runs (`--copy-bytes` bytes read and as many written, summed
       over every copy dispatch), so the result is in true bytes.  The
       summary ends with one `traffic` line per benchmark leg, which bench.py
-      reads back together with the digest of the kernel sources the counters
-      were taken on (a figure for other sources is not reported).
+      reads back together with the digest of that leg's kernel sources the
+      counters were taken on (a figure for other sources is not reported).
 """
 
 from __future__ import annotations
@@ -33,14 +33,27 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources (file names and contents, sorted)."""
+#: Kernel sources each benchmark leg's kernels are compiled from (the
+#: launchers that set their grids included).
+LEG_SOURCES = {
+    "quantize": ("codec.hip", "common.hpp"),
+    "dequantize": ("codec.hip", "common.hpp"),
+    "append": ("codec.hip", "common.hpp"),
+    "decode": ("decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip", "decode_mla.hip",
+               "common.hpp"),
+}
+
+
+def source_digest(leg: str | None = None) -> str:
+    """sha256 over the kernel sources of `leg` (all of them for None): file
+    names and contents, sorted."""
+    names = LEG_SOURCES[leg] if leg else [n for n in os.listdir(CSRC)
+                                          if n.endswith((".hip", ".hpp", ".h"))]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(names):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -62,6 +75,8 @@ def leg_of(kernel: str) -> str | None:
         return "quantize"
     if kernel.startswith("dequantize_kernel"):
         return "dequantize"
+    if kernel.startswith("append_kernel"):
+        return "append"
     if kernel.startswith(("decode_", "merge_")):
         return "decode"
     return None
@@ -116,10 +131,10 @@ def counters(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> 
             legs[leg][0] += rb
             legs[leg][1] += wb
     out.append("")
-    digest = source_digest()
     for leg, (rb, wb) in sorted(legs.items()):
         out.append(f"traffic workload={workload} leg={leg} read_bytes={rb:.0f} "
-                   f"written_bytes={wb:.0f} total_bytes={rb + wb:.0f} sources={digest}")
+                   f"written_bytes={wb:.0f} total_bytes={rb + wb:.0f} "
+                   f"sources={source_digest(leg)}")
     return out
 
 
@@ -128,7 +143,7 @@ def read_traffic(path: str, workload: str, leg: str) -> int | None:
     the current kernel sources for this workload; else None."""
     if not os.path.exists(path):
         return None
-    digest = source_digest()
+    digest = source_digest(leg)
     for line in open(path):
         if not line.startswith("traffic "):
             continue

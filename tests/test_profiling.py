@@ -1,0 +1,55 @@
+"""Host-side checks of the rocprofv3 summary helpers: the copy calibration
+of FETCH_SIZE / WRITE_SIZE and the per-leg source digest that bench.py
+requires before it reports a traffic figure."""
+
+import csv
+import os
+
+from nvfp4_paged_decode_amd import profiling as P
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for k, v in rows:
+            w.writerow({"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_counters_scale_by_copy_and_sum_legs(tmp_path):
+    copy = "void copyBuffer(char*, char const*)"
+    # the copy of 1 MiB reads 512 KiB on FETCH_SIZE (x2 scale) and 1024 KiB written
+    _write_counters(tmp_path / "f", "FETCH_SIZE", [
+        (copy, 512), ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 100),
+        ("void kvfp4::(anonymous namespace)::decode_gqa_mfma_kernel<2>(int)", 30),
+        ("kvfp4::(anonymous namespace)::merge_balanced_kernel<true>(int)", 10)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [
+        (copy, 1024), ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 50),
+        ("void kvfp4::(anonymous namespace)::decode_gqa_mfma_kernel<2>(int)", 1),
+        ("kvfp4::(anonymous namespace)::merge_balanced_kernel<true>(int)", 2)])
+    lines = P.counters(str(tmp_path / "f"), str(tmp_path / "w"), 1 << 20, "wl")
+    traffic = {}
+    for l in lines:
+        if l.startswith("traffic "):
+            kv = dict(p.split("=", 1) for p in l.split()[1:])
+            traffic[kv["leg"]] = kv
+    assert int(traffic["quantize"]["read_bytes"]) == 100 * 1024 * 2
+    assert int(traffic["quantize"]["written_bytes"]) == 50 * 1024
+    assert int(traffic["decode"]["total_bytes"]) == (30 + 10) * 2048 + (1 + 2) * 1024
+    assert traffic["decode"]["sources"] == P.source_digest("decode")
+    path = tmp_path / "counters.txt"
+    path.write_text("\n".join(lines) + "\n")
+    assert P.read_traffic(str(path), "wl", "quantize") == 100 * 2048 + 50 * 1024
+    assert P.read_traffic(str(path), "other", "quantize") is None
+    # a figure taken on other sources is not reported
+    path.write_text("\n".join(lines).replace(P.source_digest("quantize"), "0" * 64) + "\n")
+    assert P.read_traffic(str(path), "wl", "quantize") is None
+
+
+def test_leg_digests_cover_their_sources():
+    for leg, names in P.LEG_SOURCES.items():
+        for n in names:
+            assert os.path.exists(os.path.join(P.CSRC, n)), (leg, n)
+    assert P.source_digest("decode") != P.source_digest("quantize")
+    assert P.source_digest("quantize") == P.source_digest("dequantize")
