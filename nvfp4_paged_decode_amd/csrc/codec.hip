@@ -160,11 +160,17 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
   return code;
 }
 
-// Cache-policy bits of the codec's streaming loads and stores.  Every input
-// byte is read by exactly one load instruction and never again, so loads are
+// Cache-policy bits of the codec's streaming loads and stores.  Each input
+// line is read by one load instruction and never again, so those loads are
 // non-temporal (nt); non-temporal stores measured slower and stay default.
 #ifndef KVFP4_CODEC_LOAD_AUX
 #define KVFP4_CODEC_LOAD_AUX 2
+#endif
+// The decoder's scale bytes are the exception: the four waves of a
+// workgroup each read a quarter of the same 128-byte line, so the line is
+// kept in cache for the later ones.
+#ifndef KVFP4_CODEC_SCALE_LOAD_AUX
+#define KVFP4_CODEC_SCALE_LOAD_AUX 0
 #endif
 #ifndef KVFP4_CODEC_STORE_AUX
 #define KVFP4_CODEC_STORE_AUX 0
@@ -204,7 +210,7 @@ __device__ inline void encode_half(const QuantLds& s, const u32x4& a, int t, uin
 #define KVFP4_QUANT_UNROLL 8
 #endif
 #ifndef KVFP4_DEQUANT_UNROLL
-#define KVFP4_DEQUANT_UNROLL 8
+#define KVFP4_DEQUANT_UNROLL 16
 #endif
 #ifndef KVFP4_CODEC_GRID
 #define KVFP4_CODEC_GRID 4096
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
         const int hb = h0 + u * kThreads + (int)threadIdx.x;
         dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, KVFP4_CODEC_LOAD_AUX);
         code[u] = hb < hpp ? __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0,
-                                                                 KVFP4_CODEC_LOAD_AUX)
+                                                                 KVFP4_CODEC_SCALE_LOAD_AUX)
                            : 0u;
       }
 #pragma unroll

@@ -76,11 +76,11 @@ constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
                                // maximum exceeds it by more than this (log2
                                // units): rescales stay rare, p stays < 2^8
 
-// Tuning knobs (defaults are the measured best): tiles in flight per
-// stream (2 or 3), XOR swizzle of staged V chunks, and two independent
-// accumulation chains for the scores.
-#ifndef KVFP4_GQA_DEPTH
-#define KVFP4_GQA_DEPTH 2
+// Tuning knobs (defaults are the measured best): XOR swizzle of staged V
+// chunks, two independent accumulation chains for the scores, rotated tile
+// order per KV-head group.
+#ifndef KVFP4_GQA_ROT
+#define KVFP4_GQA_ROT 1
 #endif
 #ifndef KVFP4_GQA_SWZ
 #define KVFP4_GQA_SWZ 1
@@ -376,8 +376,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // Depth 3: tile k+2 is requested before tile k is computed, into the
-    // buffer tile k-1 used (no register copies of loads still in flight).
     auto issue = [&](Packed& p, int& n, long long t) {
       if (t < t_hi) {
         const int sl = slot_of(t);
@@ -421,37 +419,29 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       qs = ldexpf(base_scale, -sh_c);
     };
 
-#if KVFP4_GQA_DEPTH == 3
-    Packed B0, B1, B2;
-    int n0 = 0, n1 = 0, n2 = 0;
-    long long ti = t_lo + s;
-    issue(B0, n0, ti);
-    issue(B1, n1, ti + NS);
-    load_queries();
-    for (; ti < t_hi; ti += 3 * NS) {
-      issue(B2, n2, ti + 2 * NS);
-      compute(B0, n0);
-      if (ti + NS >= t_hi) break;
-      issue(B0, n0, ti + 3 * NS);
-      compute(B1, n1);
-      if (ti + 2 * NS >= t_hi) break;
-      issue(B1, n1, ti + 4 * NS);
-      compute(B2, n2);
-    }
-#else
-    // two tiles in flight: tile k+1 is requested before tile k is computed
+    // Two tiles in flight: tile k+1 is requested before tile k is computed.
+    // The KV-head groups walk the stream's tiles in rotated orders (group kg
+    // starts kg tiles later and wraps round), so the block-scale lines the
+    // groups share are fetched by one group and found in L2 by the next,
+    // instead of being missed by all of them at once.
+    const long long first_t = t_lo + s;
+    const int nk = first_t < t_hi ? (int)((t_hi - first_t + NS - 1) / NS) : 0;
+    const int rot = (KVFP4_GQA_ROT && nk > 0) ? kg % nk : 0;
+    auto tile_at = [&](int k) -> long long {
+      int kk = k + rot;
+      if (kk >= nk) kk -= nk;
+      return first_t + (long long)kk * NS;
+    };
     Packed cur, nxt;
     int n_cur = 0, n_nxt = 0;
-    long long ti = t_lo + s;
-    issue(cur, n_cur, ti);  // requested before the queries are prepared
+    if (nk > 0) issue(cur, n_cur, tile_at(0));  // requested before the queries are prepared
     load_queries();
-    for (; ti < t_hi; ti += NS) {
-      issue(nxt, n_nxt, ti + NS);
+    for (int k = 0; k < nk; ++k) {
+      if (k + 1 < nk) issue(nxt, n_nxt, tile_at(k + 1));
       compute(cur, n_cur);
       cur = nxt;
       n_cur = n_nxt;
     }
-#endif
 
     // merge the NS streams of each KV-head group, then write the partial
     l += __shfl_xor(l, 16);
