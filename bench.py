@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--no-copy-yardstick", action="store_true",
                    help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
     p.add_argument("--no-append", action="store_true",
-                   help="skip timing the write path (append-quantize), reported beside the step")
+                   help="skip timing the token-row paths (append-quantize, gather-dequantize), "
+                        "reported beside the step")
     return p.parse_args()
 
 
@@ -78,18 +79,20 @@ def codec_bytes(geometry, pages: int) -> int:
 
 
 def append_bytes(geometry, tokens: int, elem_bytes: int) -> int:
-    """Algorithmic bytes of appending `tokens` rows: the input rows, the
-    packed data and scale bytes written, the two int32 slot/row entries."""
+    """Algorithmic bytes of appending (or gathering) `tokens` rows: the bf16
+    or FP8 rows, their packed data and scale bytes, the two int32 slot/row
+    entries."""
     nt, T, H, D = geometry
     per = nt * H * D
     return tokens * (per * elem_bytes + per * 9 // 16 + 8)
 
 
 def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, warmup):
-    """The write path, timed beside the step (not part of it): a prefill of
-    up to 256 of the workload's pages appended token by token (bf16 rows, and
-    the same values as FP8 rows), and one decode step that rewrites the last
-    cached token of every sequence."""
+    """The token-row paths, timed beside the step (not part of it).  Write
+    path: a prefill of up to 256 of the workload's pages appended token by
+    token (bf16 rows, and the same values as FP8 rows), and one decode step
+    that rewrites the last cached token of every sequence.  Extend path: the
+    same pages' rows gathered back into a bf16 and an FP8 workspace."""
     nt, T, H, D = geometry
     dev = hot.device
     used = torch.from_numpy(wl.used_slots[:256].astype(np.int64)).to(dev)
@@ -106,13 +109,20 @@ def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, w
     dslots = torch.from_numpy(wl.block_table[np.arange(wl.batch), last // T].astype(np.int32)).to(dev)
     drows = torch.from_numpy((last % T).astype(np.int32)).to(dev)
     drow_data = rows[:wl.batch].contiguous()
-    cases = [("prefill_bf16", rows, tok_slots, tok_rows, 2),
-             ("prefill_fp8", rows8, tok_slots, tok_rows, 1),
-             ("decode_step_bf16", drow_data, dslots, drows, 2)]
-    res = {}
-    for name, r, ts, tr, eb in cases:
+    g16 = torch.empty_like(rows)
+    g8 = torch.empty_like(rows8)
+    cases = [("append", "prefill_bf16", rows, tok_slots, tok_rows, 2),
+             ("append", "prefill_fp8", rows8, tok_slots, tok_rows, 1),
+             ("append", "decode_step_bf16", drow_data, dslots, drows, 2),
+             ("gather", "prefix_bf16", g16, tok_slots, tok_rows, 2),
+             ("gather", "prefix_fp8", g8, tok_slots, tok_rows, 1)]
+    res = {"append": {}, "gather": {}}
+    for kind, name, r, ts, tr, eb in cases:
         def fn():
-            K.kvfp4_append_quantize(geometry, r, ts, tr, packed, gs)
+            if kind == "append":
+                K.kvfp4_append_quantize(geometry, r, ts, tr, packed, gs)
+            else:
+                K.kvfp4_gather_dequantize(geometry, packed, ts, tr, r, gs)
         for _ in range(warmup):
             fn()
         evs = []
@@ -128,8 +138,8 @@ def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, w
         us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
         ntok = int(ts.shape[0])
         b = append_bytes(geometry, ntok, eb)
-        res[name] = {"tokens": ntok, "avg_us": round(us, 2), "bytes": b,
-                     "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+        res[kind][name] = {"tokens": ntok, "avg_us": round(us, 2), "bytes": b,
+                           "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
     return res
 
 
@@ -386,7 +396,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kern,
         "copy_yardstick": copy,
-        "append_write_path": append,
+        "token_rows": append,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),

@@ -104,7 +104,8 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
                                const int32_t* dst_slots, int32_t num_pages,
                                const float* global_scale, void* stream);
 
-/* Element types of kvfp4_append_quantize's input rows. */
+/* Element types of the token rows kvfp4_append_quantize reads and
+ * kvfp4_gather_dequantize writes. */
 #define KVFP4_ROWS_BF16 0     /* bf16, 2 bytes a value                          */
 #define KVFP4_ROWS_FP8_E4M3 1 /* OCP E4M3FN, 1 byte a value (NaN codes: unspecified) */
 
@@ -131,6 +132,28 @@ int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t
                               const int32_t* token_rows, void* packed_pool,
                               int32_t packed_pool_pages, const float* global_scale,
                               void* stream);
+
+/* Gather rows of packed pages into a contiguous workspace, dequantized
+ * ("Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
+ * Path 2: Chunked prefill / Extend -- the cached prefix's NVFP4 entries are
+ * gathered, dequantized and written to a workspace, FP8 there, that the
+ * chunk's attention reads together with the chunk's own K/V).
+ *   packed_pool  packed slots [packed_pool_pages][9*E/16 bytes]       (read)
+ *   token_slots  int32 [num_tokens] packed slot of output row i
+ *   token_rows   int32 [num_tokens] row (token position) in that page
+ *   out          [num_tokens][n_t][H][D] of out_dtype (KVFP4_ROWS_BF16:
+ *                16-byte aligned; KVFP4_ROWS_FP8_E4M3: 8-byte aligned)
+ *   global_scale HOST float [num_kv_tensors], as for the other calls.
+ * Each value is the exact +-e2m1 * e4m3 * gs rounded once: to bf16 exactly
+ * as kvfp4_dequantize_pages does, or to OCP E4M3FN, nearest with ties to
+ * the even code and saturating at +-448 (never NaN); the sign bit is the
+ * nibble's.  A token whose slot is outside [0, packed_pool_pages) or whose
+ * row is outside [0, T) gives an all-zero output row.  num_tokens == 0 is a
+ * no-op; num_tokens * n_t * H * D must stay below 2^34. */
+int32_t kvfp4_gather_dequantize(const kvfp4_geometry* g, const void* packed_pool,
+                                int32_t packed_pool_pages, const int32_t* token_slots,
+                                const int32_t* token_rows, int32_t num_tokens, void* out,
+                                int32_t out_dtype, const float* global_scale, void* stream);
 
 /* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
  * current device (0 is a valid answer). */

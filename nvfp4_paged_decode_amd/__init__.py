@@ -29,7 +29,8 @@ KVFP4_ROWS_FP8_E4M3 = 1
 #: Every function the header declares (checked by the CPU tests).
 EXPORTS = (
     "kvfp4_hot_page_bytes", "kvfp4_packed_page_bytes", "kvfp4_quantize_pages",
-    "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_decode_workspace_bytes",
+    "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_gather_dequantize",
+    "kvfp4_decode_workspace_bytes",
     "kvfp4_paged_decode_attention", "kvfp4_status_string", "kvfp4_last_error_message",
 )
 
@@ -84,6 +85,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_dequantize_pages.restype = I32
     lib.kvfp4_append_quantize.argtypes = [G, P, I32, I32, P, P, P, I32, P, P]
     lib.kvfp4_append_quantize.restype = I32
+    lib.kvfp4_gather_dequantize.argtypes = [G, P, I32, P, P, I32, P, I32, P, P]
+    lib.kvfp4_gather_dequantize.restype = I32
     lib.kvfp4_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
     lib.kvfp4_decode_workspace_bytes.restype = SZ
     lib.kvfp4_paged_decode_attention.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32, P, I32,
@@ -187,6 +190,29 @@ def kvfp4_append_quantize(geometry, rows, token_slots, token_rows, packed_pool, 
         _ptr(packed_pool),
         _pages(packed_pool, kvfp4_packed_page_bytes(g)), _scales(global_scale, g.num_kv_tensors),
         _stream(stream)))
+
+
+def kvfp4_gather_dequantize(geometry, packed_pool, token_slots, token_rows, out, global_scale,
+                            out_dtype: Optional[int] = None, stream=None) -> None:
+    """Dequantize row ``token_rows[i]`` of packed slot ``token_slots[i]`` into
+    ``out[i]`` (``[num_tokens, n_t, H, D]``: 2-byte elements get bf16 bits,
+    1-byte elements E4M3FN codes unless ``out_dtype`` says so)."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    n = int(token_slots.shape[0])
+    if int(token_rows.shape[0]) != n:
+        raise ValueError("token_slots and token_rows differ in length")
+    if out_dtype is None:
+        out_dtype = KVFP4_ROWS_FP8_E4M3 if out.element_size() == 1 else KVFP4_ROWS_BF16
+    width = 1 if out_dtype == KVFP4_ROWS_FP8_E4M3 else 2
+    per_token = g.num_kv_tensors * g.num_kv_heads * g.head_dim
+    if out.numel() * out.element_size() != n * per_token * width:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes, expected "
+                         f"{n} tokens x {per_token} values x {width} bytes")
+    _check(lib.kvfp4_gather_dequantize(
+        ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        _ptr(token_slots), _ptr(token_rows), n, _ptr(out), int(out_dtype),
+        _scales(global_scale, g.num_kv_tensors), _stream(stream)))
 
 
 def kvfp4_decode_workspace_bytes(geometry, batch: int, num_q_heads: int, v_dim: int,

@@ -184,6 +184,39 @@ int32_t kvfp4_append_quantize(const kvfp4_geometry* g, const void* rows, int32_t
   return ok();
 }
 
+int32_t kvfp4_gather_dequantize(const kvfp4_geometry* g, const void* packed_pool,
+                                int32_t packed_pool_pages, const int32_t* token_slots,
+                                const int32_t* token_rows, int32_t num_tokens, void* out,
+                                int32_t out_dtype, const float* global_scale, void* stream) {
+  int32_t st = check_geometry(g);
+  if (st) return st;
+  if (out_dtype != KVFP4_ROWS_BF16 && out_dtype != KVFP4_ROWS_FP8_E4M3)
+    return fail(KVFP4_ERR_INVALID_ARG, "out_dtype = %d is not KVFP4_ROWS_BF16 or "
+                "KVFP4_ROWS_FP8_E4M3", out_dtype);
+  if (num_tokens < 0) return fail(KVFP4_ERR_INVALID_ARG, "num_tokens = %d < 0", num_tokens);
+  if (packed_pool_pages < 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "packed_pool_pages = %d < 0", packed_pool_pages);
+  if (num_tokens == 0) return ok();
+  if (!packed_pool) return fail(KVFP4_ERR_INVALID_ARG, "packed_pool is NULL");
+  if (!token_slots) return fail(KVFP4_ERR_INVALID_ARG, "token_slots is NULL");
+  if (!token_rows) return fail(KVFP4_ERR_INVALID_ARG, "token_rows is NULL");
+  if (!out) return fail(KVFP4_ERR_INVALID_ARG, "out is NULL");
+  const bool fp8 = out_dtype == KVFP4_ROWS_FP8_E4M3;
+  if (((uintptr_t)out & (fp8 ? 7u : 15u)) != 0)
+    return fail(KVFP4_ERR_INVALID_ARG, "out must be %d-byte aligned", fp8 ? 8 : 16);
+  const long long per_token = (long long)g->num_kv_tensors * g->num_kv_heads * g->head_dim;
+  if (per_token / 8 * num_tokens >= (1LL << 31))
+    return fail(KVFP4_ERR_INVALID_ARG, "num_tokens %d x %lld values per token is too large",
+                num_tokens, per_token);
+  st = check_scales(g, global_scale);
+  if (st) return st;
+  hipError_t e = kvfp4::launch_gather(to_geom(g), packed_pool, packed_pool_pages, token_slots,
+                                      token_rows, num_tokens, out, fp8, global_scale,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 static int32_t check_decode_shape(const kvfp4_geometry* g, int32_t batch, int32_t num_q_heads,
                                   int32_t v_dim, int32_t max_seq_len_hint) {
   int32_t st = check_geometry(g);

@@ -462,6 +462,135 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Gather: rows of packed pages -> a contiguous bf16 or FP8 workspace
+// ---------------------------------------------------------------------------
+
+// E4M3FN code of an exact non-negative value: nearest finite value, ties to
+// the even code, saturating at 448.  Subnormal codes are m * 2^-9 (m = 0..8,
+// and m = 8 is the first normal code); a normal value 2^e (1 + m/8) has code
+// (e + 7) * 8 + m, so a mantissa rounded up to 8 carries into the exponent.
+// Every step is exact in fp64 and rint rounds ties to even.
+__device__ inline uint32_t e4m3_code_rne(double v) {
+  if (!(v > 0.0)) return 0u;
+  if (v >= 448.0) return 126u;
+  if (v < 0x1p-6) return (uint32_t)rint(v * 512.0);
+  int E;
+  (void)frexp(v, &E);  // v in [2^(E-1), 2^E)
+  const int e = E - 1;
+  const uint32_t m = (uint32_t)rint(ldexp(v, -e) * 8.0) - 8u;  // 0..8
+  const uint32_t code = (uint32_t)((e + 7) << 3) + m;
+  return code > 126u ? 126u : code;
+}
+
+struct GatherFp8Lds {
+  // per tensor and scale code: the E4M3 codes of magnitude codes 0..7
+  uint32_t row[2][128][2];
+};
+
+__device__ inline void build_fp8_table(GatherFp8Lds& s, int nt, float gs0, float gs1) {
+  uint8_t* bytes = reinterpret_cast<uint8_t*>(&s.row[0][0][0]);
+  for (int i = threadIdx.x; i < nt * 128 * 8; i += blockDim.x) {
+    const int t = i >> 10, j = (i >> 3) & 127, c = i & 7;
+    const double gs = t == 0 ? (double)gs0 : (double)gs1;
+    const double v = (double)e2m1_mag_to_float(c) * (double)e4m3_to_float(j) * gs;  // exact
+    bytes[(t * 128 + j) * 8 + c] = (uint8_t)(j == 127 ? 0x7Fu : e4m3_code_rne(v));
+  }
+}
+
+// Eight nibbles of one data word -> eight E4M3 bytes in element order.
+__device__ inline void decode8_fp8(uint32_t w, const u32x2& row, uint32_t sign_flip,
+                                   uint32_t& o0, uint32_t& o1) {
+  const uint32_t x = w & 0x0F0F0F0Fu;
+  const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t s0 = __builtin_amdgcn_perm(y, x, 0x05010400u) ^ sign_flip;
+  const uint32_t s1 = __builtin_amdgcn_perm(y, x, 0x07030602u) ^ sign_flip;
+  o0 = __builtin_amdgcn_perm(row.y, row.x, s0 & 0x07070707u) | ((s0 & 0x08080808u) << 4);
+  o1 = __builtin_amdgcn_perm(row.y, row.x, s1 & 0x07070707u) | ((s1 & 0x08080808u) << 4);
+}
+
+union GatherLds {
+  DequantLds b;
+  GatherFp8Lds f;
+};
+
+// A lane owns half a block of an output row: it reads the 4 data bytes and
+// the scale byte from the token's page and writes 16 bytes (bf16) or 8
+// bytes (FP8) of the output, which is read-contiguous across lanes.  The
+// slot and row loads come first, then the page loads that depend on them,
+// then the lookup tables are built while those are in flight.
+template <bool kFp8, int kUnroll>
+__global__ __launch_bounds__(kThreads) void gather_kernel(
+    Geom g, const uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ page_rows, int num_tokens, uint8_t* __restrict__ out, float gs0,
+    float gs1) {
+  __shared__ GatherLds s;
+  // The C ABI bounds num_tokens * half-blocks per token below 2^31.
+  const uint32_t hd8 = (uint32_t)(g.H * g.D / 8);
+  const uint32_t hpt = (uint32_t)g.nt * hd8;
+  const uint32_t total = hpt * (uint32_t)num_tokens;
+  const int data_bytes = (int)g.data_bytes();
+  const int page_bytes = (int)g.packed_bytes();
+  constexpr uint32_t chunk = kThreads * kUnroll;
+  const uint32_t stride = gridDim.x * chunk;
+  const uint32_t first = blockIdx.x * chunk;
+  bool tables = false;
+  for (uint32_t base = first; base < total; base += stride) {
+    uint32_t dw[kUnroll], code[kUnroll];
+    bool ok[kUnroll];
+    int slot[kUnroll], row[kUnroll];
+    uint32_t t[kUnroll], k[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t gi = base + u * kThreads + threadIdx.x;
+      const bool live = gi < total;
+      const uint32_t tok = live ? gi / hpt : 0u;
+      const uint32_t j = gi - tok * hpt;
+      t[u] = j >= hd8 ? 1u : 0u;
+      k[u] = j - t[u] * hd8;
+      slot[u] = live ? slots[tok] : -1;
+      row[u] = live ? page_rows[tok] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      ok[u] = slot[u] >= 0 && slot[u] < packed_pages && row[u] >= 0 && row[u] < g.T;
+      const uint8_t* page = packed + (long long)(ok[u] ? slot[u] : 0) * page_bytes;
+      auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)page, (short)0, ok[u] ? page_bytes : 0,
+                                                   kRsrcFlags);
+      const int hb = (int)((t[u] * (uint32_t)g.T + (uint32_t)(ok[u] ? row[u] : 0)) * hd8 + k[u]);
+      dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, 0);
+      code[u] = __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0, 0);
+    }
+    if (!tables) {
+      if constexpr (kFp8)
+        build_fp8_table(s.f, g.nt, gs0, gs1);
+      else
+        build_dequant_table(s.b, g.nt, gs0, gs1);
+      __syncthreads();
+      tables = true;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t gi = base + u * kThreads + threadIdx.x;
+      if (gi >= total) continue;
+      const uint32_t flip = (code[u] & 0x80u) ? 0x08080808u : 0u;  // negative E4M3 scale
+      if constexpr (kFp8) {
+        const u32x2 r8 = *reinterpret_cast<const u32x2*>(s.f.row[t[u]][code[u] & 127]);
+        uint32_t o0, o1;
+        decode8_fp8(dw[u], r8, flip, o0, o1);
+        if (!ok[u]) o0 = o1 = 0u;  // a bad slot or row gives a zero row
+        *reinterpret_cast<u32x2*>(out + (size_t)gi * 8) = (u32x2){o0, o1};
+      } else {
+        const u32x4 r16 = *reinterpret_cast<const u32x4*>(s.b.row[t[u]][code[u] & 127]);
+        uint32_t o[4];
+        decode8(dw[u], r16, flip, o);
+        if (!ok[u]) o[0] = o[1] = o[2] = o[3] = 0u;
+        *reinterpret_cast<u32x4*>(out + (size_t)gi * 16) = (u32x4){o[0], o[1], o[2], o[3]};
+      }
+    }
+  }
+}
+
 int grid_for(int num_pages) {
   // one workgroup per page up to 16 per CU of a 256-CU part; each walks its
   // contiguous run of pages
@@ -508,6 +637,24 @@ hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages
   hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
                      num_pages, gs[0], gs1);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Geom& g, const void* packed, int packed_pages, const int32_t* slots,
+                         const int32_t* page_rows, int num_tokens, void* out, bool fp8,
+                         const float* gs, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const float gs1 = g.nt > 1 ? gs[1] : gs[0];
+  const long long hb = (long long)g.nt * g.H * g.D / 8 * num_tokens;
+  const bool small = hb <= kAppendSmall;
+  const int unroll = small ? 1 : 4;
+  long long grid = (hb + kThreads * unroll - 1) / (kThreads * unroll);
+  if (grid > KVFP4_APPEND_GRID) grid = KVFP4_APPEND_GRID;
+  auto kernel = fp8 ? (small ? gather_kernel<true, 1> : gather_kernel<true, 4>)
+                    : (small ? gather_kernel<false, 1> : gather_kernel<false, 4>);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g,
+                     (const uint8_t*)packed, packed_pages, slots, page_rows, num_tokens,
+                     (uint8_t*)out, gs[0], gs1);
   return hipGetLastError();
 }
 

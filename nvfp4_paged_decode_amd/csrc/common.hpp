@@ -119,6 +119,10 @@ hipError_t launch_append(const Geom& g, const void* rows, bool fp8, int num_toke
                          const int32_t* slots, const int32_t* page_rows, void* packed,
                          int packed_pages, const float* gs, hipStream_t stream);
 
+hipError_t launch_gather(const Geom& g, const void* packed, int packed_pages, const int32_t* slots,
+                         const int32_t* page_rows, int num_tokens, void* out, bool fp8,
+                         const float* gs, hipStream_t stream);
+
 struct DecodeArgs {
   Geom g;
   const uint8_t* pool;

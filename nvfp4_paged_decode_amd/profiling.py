@@ -39,6 +39,7 @@ LEG_SOURCES = {
     "quantize": ("codec.hip", "common.hpp"),
     "dequantize": ("codec.hip", "common.hpp"),
     "append": ("codec.hip", "common.hpp"),
+    "gather": ("codec.hip", "common.hpp"),
     "decode": ("decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip", "decode_mla.hip",
                "common.hpp"),
 }
@@ -77,6 +78,8 @@ def leg_of(kernel: str) -> str | None:
         return "dequantize"
     if kernel.startswith("append_kernel"):
         return "append"
+    if kernel.startswith("gather_kernel"):
+        return "gather"
     if kernel.startswith(("decode_", "merge_")):
         return "decode"
     return None

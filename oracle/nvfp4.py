@@ -338,3 +338,46 @@ def append_quantize(rows: np.ndarray, g: Geometry, gs, packed_pool: np.ndarray,
             dt, sc = quantize_rows(rows[i, t], float(gs[t]))
             data[t, r] = dt
             scales[t, r] = sc
+
+
+def f64_to_e4m3_rne(v: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN codes of exact fp64 values: the magnitude rounded once to
+    the nearest finite E4M3 value, ties to the even code, saturating at 448
+    (never NaN); the sign bit is the value's sign bit (-0.0 gives 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = round_half_even_to_grid(np.abs(v), E4M3_FINITE)
+    return (mag | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def gather_dequantize(packed_pool: np.ndarray, g: Geometry, gs, token_slots, token_rows,
+                      out_dtype: str = "bf16") -> np.ndarray:
+    """Rows of packed pages gathered into a contiguous workspace.
+
+    The extend path ("Accelerating Long-Context and Agentic Inference with
+    NVFP4 KV Cache", Path 2: Chunked prefill / Extend): the cached prefix's
+    NVFP4 entries are gathered, dequantized and written to a workspace that
+    prefill attention reads (the page's workspace type is FP8; bf16 is the
+    lossless alternative).  Output row i is row ``token_rows[i]`` of packed
+    slot ``token_slots[i]``, ``[n_t, H, D]``, each value the exact
+    ``+-e2m1 * e4m3 * gs[t]`` rounded once: to bf16 (``"bf16"``, uint16
+    bits, as :func:`dequantize_rows`) or to E4M3FN (``"fp8"``, uint8 codes,
+    :func:`f64_to_e4m3_rne`).  A token whose slot is outside the pool or whose
+    row is outside ``[0, page_size)`` gives an all-zero row.
+    """
+    n = len(token_slots)
+    nt, T, H, D = g.row_shape
+    dt = np.uint16 if out_dtype == "bf16" else np.uint8
+    out = np.zeros((n, nt, H, D), dtype=dt)
+    for i in range(n):
+        s, r = int(token_slots[i]), int(token_rows[i])
+        if not (0 <= s < packed_pool.shape[0] and 0 <= r < T):
+            continue
+        data, scales = split_packed_page(packed_pool[s], g)
+        for t in range(nt):
+            d = np.asarray(data[t, r], dtype=np.uint8)
+            nib = np.empty((H, D), dtype=np.int64)
+            nib[:, 0::2] = d & 0xF
+            nib[:, 1::2] = d >> 4
+            v = exact_values(nib, scales[t, r], float(gs[t]))
+            out[i, t] = f64_to_bf16_rne(v) if out_dtype == "bf16" else f64_to_e4m3_rne(v)
+    return out

@@ -129,6 +129,40 @@ def test_append_zero_tokens_is_a_noop(lib):
                    prows=None, packed=None) == K.KVFP4_OK
 
 
+def _gather(lib, g, num_tokens=4, gs=(1.0, 1.0), packed=FAKE, slots=FAKE + 0x200,
+            prows=FAKE + 0x300, out=FAKE + 0x400, packed_pages=8, dtype=K.KVFP4_ROWS_BF16):
+    arr = (ctypes.c_float * 2)(*gs)
+    return lib.kvfp4_gather_dequantize(ctypes.byref(g) if g is not None else None, packed,
+                                       packed_pages, slots, prows, num_tokens, out, dtype, arr,
+                                       None)
+
+
+@pytest.mark.parametrize("case", [
+    dict(g=None),
+    dict(g=K.Geometry(1, 64, 1, 500)),
+    dict(num_tokens=-1),
+    dict(packed_pages=-1),
+    dict(packed=None),
+    dict(slots=None),
+    dict(prows=None),
+    dict(out=None),
+    dict(out=FAKE + 8),                               # bf16 rows need 16-byte alignment
+    dict(out=FAKE + 4, dtype=K.KVFP4_ROWS_FP8_E4M3),  # FP8 rows need 8
+    dict(dtype=7),
+    dict(num_tokens=1 << 30),
+    dict(gs=(-1.0, 1.0)),
+])
+def test_gather_rejects_invalid_arguments(lib, case):
+    g = case.pop("g", K.Geometry(2, 64, 8, 128))
+    assert _gather(lib, g, **case) == K.KVFP4_ERR_INVALID_ARG
+    assert lib.kvfp4_last_error_message().decode() != ""
+
+
+def test_gather_zero_tokens_is_a_noop(lib):
+    assert _gather(lib, K.Geometry(2, 64, 8, 128), num_tokens=0, packed=None, slots=None,
+                   prows=None, out=None) == K.KVFP4_OK
+
+
 def _decode(lib, g, gs=(1.0, 1.0), batch=2, hq=32, v_dim=128, hint=1024, ws=0, wsptr=None,
             pool=FAKE, q=FAKE, bt=FAKE, sl=FAKE, out=FAKE, scale=0.088, max_pages=16,
             pool_pages=64):

@@ -20,6 +20,7 @@ def gpu_quantize(hot: np.ndarray, geometry, gs, num_pages=None, src=None, dst=No
     g = O.Geometry(*geometry)
     n = hot.shape[0] if num_pages is None else num_pages
     slots = hot.shape[0] if packed_slots is None else packed_slots
+    assert all(a is None or len(a) >= n for a in (src, dst)), "slot arrays shorter than num_pages"
     hot_d = dev(hot.view(np.int16))
     packed_d = torch.zeros((slots, O.packed_page_bytes(g)), dtype=torch.uint8, device="cuda")
     K.kvfp4_quantize_pages(geometry, hot_d, packed_d, n, gs,
@@ -33,6 +34,7 @@ def gpu_dequantize(packed: np.ndarray, geometry, gs, num_pages=None, src=None, d
     g = O.Geometry(*geometry)
     n = packed.shape[0] if num_pages is None else num_pages
     slots = packed.shape[0] if hot_slots is None else hot_slots
+    assert all(a is None or len(a) >= n for a in (src, dst)), "slot arrays shorter than num_pages"
     hot_d = torch.full((slots, *g.row_shape), fill, dtype=torch.int16, device="cuda")
     K.kvfp4_dequantize_pages(geometry, dev(packed), hot_d, n, gs,
                              None if src is None else dev(src.astype(np.int32)),
@@ -284,3 +286,75 @@ def test_append_fp8_rows_bit_exact(geometry, num_tokens, gs_pair):
     got = host(pool_d)
     mism = np.nonzero(got != ref)
     assert mism[0].size == 0, f"{mism[0].size} bytes differ, first at {mism[0][0]},{mism[1][0]}"
+
+
+def _valid_pool(rng, g, n_slots, gs):
+    """Packed slots holding encoder output of random data, with some scale
+    bytes negated (the decoder's sign flip); no NaN scale codes."""
+    hot = W.f32_to_bf16_bits((rng.standard_normal((n_slots, *g.row_shape))
+                              * 10.0 ** rng.uniform(-3, 3, (n_slots, g.num_kv_tensors, 1, 1, 1)))
+                             .astype(np.float32))
+    pool = np.zeros((n_slots, O.packed_page_bytes(g)), np.uint8)
+    O.quantize_pages(hot, g, n_slots, gs, pool)
+    nd = g.elems // 2
+    sc = pool[:, nd:]
+    neg = rng.random(sc.shape) < 0.05
+    sc[neg & (sc != 0x7F)] |= 0x80
+    return pool
+
+
+@pytest.mark.parametrize("geometry,num_tokens", [((2, 64, 8, 128), 100), ((2, 8, 3, 48), 37),
+                                                 ((1, 64, 1, 576), 70), ((2, 8, 3, 48), 2001)])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp8"])
+def test_gather_bit_exact(geometry, num_tokens, out_dtype):
+    """Gathered rows match the oracle bit for bit, bf16 and FP8, including
+    tokens with a bad slot or row (zero rows) and repeated tokens."""
+    require_gpu()
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(num_tokens + (7 if out_dtype == "fp8" else 0))
+    gs = [float(np.float32(0.37)), float(np.float32(0.011))][:g.num_kv_tensors]
+    n_slots = 2 * num_tokens // g.page_size + 3
+    pool = _valid_pool(rng, g, n_slots, gs)
+    slots = rng.integers(0, n_slots, num_tokens).astype(np.int32)
+    page_rows = rng.integers(0, g.page_size, num_tokens).astype(np.int32)
+    slots[::17] = -1
+    page_rows[5::19] = g.page_size
+    ref = O.gather_dequantize(pool, g, gs, slots, page_rows, out_dtype)
+    dt = torch.int16 if out_dtype == "bf16" else torch.uint8
+    out = torch.full(ref.shape, 0x55, dtype=dt, device="cuda")
+    K.kvfp4_gather_dequantize(geometry, dev(pool), dev(slots), dev(page_rows), out, gs)
+    got = host(out)
+    got = got.view(np.uint16) if out_dtype == "bf16" else got
+    mism = np.nonzero(got.reshape(num_tokens, -1) != ref.reshape(num_tokens, -1))
+    assert mism[0].size == 0, f"{mism[0].size} values differ, first at token {mism[0][0]}"
+
+
+def test_gather_prefix_full_size():
+    """The extend-path gather at Llama-3-8B size: the 8192-token prefixes of
+    4 sequences of 64-token pages (32768 rows) in bf16 and FP8.  The bf16
+    rows must equal the page dequantizer's pages; sampled rows of both
+    outputs are checked against the oracle."""
+    require_gpu()
+    geometry = (2, 64, 8, 128)
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(8)
+    n_pages, n_slots = 512, 600
+    gs = [float(np.float32(0.05)), float(np.float32(0.02))]
+    hot = W.f32_to_bf16_bits(rng.standard_normal((n_pages, *g.row_shape)).astype(np.float32))
+    dst = rng.permutation(n_slots)[:n_pages].astype(np.int32)
+    packed = gpu_quantize(hot, geometry, gs, dst=dst, packed_slots=n_slots)
+    tok = np.arange(n_pages * 64)
+    slots, page_rows = dst[tok // 64], (tok % 64).astype(np.int32)
+    pool_d = dev(packed)
+    out16 = torch.empty((tok.size, 2, 8, 128), dtype=torch.int16, device="cuda")
+    out8 = torch.empty((tok.size, 2, 8, 128), dtype=torch.uint8, device="cuda")
+    K.kvfp4_gather_dequantize(geometry, pool_d, dev(slots), dev(page_rows), out16, gs)
+    K.kvfp4_gather_dequantize(geometry, pool_d, dev(slots), dev(page_rows), out8, gs)
+    got16, got8 = host(out16).view(np.uint16), host(out8)
+    pages = gpu_dequantize(packed, geometry, gs, num_pages=n_pages, src=dst,
+                           dst=np.arange(n_pages), hot_slots=n_pages)
+    assert np.array_equal(got16, pages.transpose(0, 2, 1, 3, 4).reshape(tok.size, 2, 8, 128))
+    sample = np.concatenate([[0, tok.size - 1], rng.choice(tok.size, 40, replace=False)])
+    for dt, got in (("bf16", got16), ("fp8", got8)):
+        ref = O.gather_dequantize(packed, g, gs, slots[sample], page_rows[sample], dt)
+        assert np.array_equal(got[sample], ref), dt

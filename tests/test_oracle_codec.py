@@ -196,3 +196,56 @@ def test_append_skips_bad_slots_and_rows():
     d, s = O.quantize_rows(rows[2, 0], 1.0)
     data, scales = O.split_packed_page(pool[1], g)
     assert np.array_equal(data[0, 0], d) and np.array_equal(scales[0, 0], s)
+
+
+def test_gather_returns_representable_rows_exactly():
+    """Rows whose values are exactly e2m1 * e4m3 * gs (and bf16) come back
+    from the gather bit for bit, in any token order; bad slots and rows give
+    zero rows."""
+    g = O.Geometry(2, 8, 2, 32)
+    rng = np.random.default_rng(31)
+    gs = [1.0, 0.375]
+    n_tok = 10
+    x = np.zeros((n_tok, 2, 2, 32))
+    for t in range(2):
+        sb = O.E4M3_FINITE[rng.integers(40, 110, size=(n_tok, 2, 2))]
+        codes = rng.integers(0, 8, size=(n_tok, 2, 32))
+        codes[:, :, 0] = 7  # the block maximum maps onto 6 exactly
+        codes[:, :, 16] = 7
+        vals = O.E2M1_GRID[codes] * np.repeat(sb, 16, axis=-1) * gs[t]
+        x[:, t] = vals * rng.choice([-1.0, 1.0], size=vals.shape)
+    bits = O.f64_to_bf16_rne(x)
+    assert np.array_equal(O.bf16_bits_to_f64(bits), x)  # representable
+    pool = np.zeros((3, O.packed_page_bytes(g)), np.uint8)
+    cells = rng.choice(3 * g.page_size, n_tok, replace=False)
+    slots, rows = cells // g.page_size, cells % g.page_size
+    O.append_quantize(bits, g, gs, pool, slots, rows)
+    order = rng.permutation(n_tok)
+    got = O.gather_dequantize(pool, g, gs, slots[order], rows[order], "bf16")
+    assert np.array_equal(got, bits[order])
+    bad = O.gather_dequantize(pool, g, gs, [3, -1, 0], [0, 0, 8], "fp8")
+    assert bad.shape == (3, 2, 2, 32) and np.all(bad == 0)
+
+
+def test_gather_fp8_equals_torch_cast_of_exact_values():
+    """FP8 output: each value is the exact e2m1 * e4m3 * gs rounded once to
+    E4M3FN.  With gs = 1 every such value fits bf16 exactly, so torch's
+    bfloat16 -> float8_e4m3fn cast of the bf16 gather is an independent
+    rounding of the same value (it matches below 464, where torch saturates
+    to NaN instead)."""
+    import torch
+    g = O.Geometry(2, 16, 2, 64)
+    rng = np.random.default_rng(32)
+    hot = _random_blocks(rng, g.elems // 16, lo=-4, hi=3).reshape(1, *g.row_shape)
+    gs = [1.0, 1.0]
+    pool = np.zeros((1, O.packed_page_bytes(g)), np.uint8)
+    O.quantize_pages(hot, g, 1, gs, pool)
+    slots, rows = np.zeros(16, np.int64), np.arange(16)
+    b16 = O.gather_dequantize(pool, g, gs, slots, rows, "bf16")
+    f8 = O.gather_dequantize(pool, g, gs, slots, rows, "fp8")
+    v = O.bf16_bits_to_f64(b16)
+    keep = np.abs(v) < 464
+    ref = torch.from_numpy(b16.view(np.int16)).view(torch.bfloat16).to(torch.float8_e4m3fn)
+    ref = ref.view(torch.uint8).numpy()
+    assert keep.mean() > 0.9 and np.array_equal(f8[keep], ref[keep])
+    assert np.all((f8[~keep] & 0x7F) == 0x7E)  # saturated to +-448

@@ -43,6 +43,24 @@ def test_e4m3_widens_to_bf16_exactly_like_torch():
         O.e4m3_codes_to_bf16_bits(np.array([0x7F], np.uint8))
 
 
+def test_e4m3_rounding_of_exact_values_matches_torch():
+    # every exact product e2m1 * e4m3 * gs for a few gs whose products fit
+    # fp32 exactly (so torch's fp32 -> float8_e4m3fn cast sees the value
+    # itself); torch gives NaN past 464, where the oracle saturates to 448
+    for gs in (1.0, 0.375, 2.0 ** -5, 3.0, 1.25):
+        v = np.outer(O.E2M1_GRID, O.E4M3_FINITE).reshape(-1) * gs
+        v = np.concatenate([v, -v])
+        keep = np.abs(v) < 464.0
+        ref = torch.from_numpy(v[keep].astype(np.float32)).to(torch.float8_e4m3fn)
+        ours = O.f64_to_e4m3_rne(v[keep])
+        assert np.array_equal(ref.view(torch.uint8).numpy(), ours), gs
+    # saturation, signed zeros, and the subnormal ties: 2^-10 lies halfway
+    # between 0 and 2^-9 (code 0 is even), 3 * 2^-10 between codes 1 and 2
+    assert O.f64_to_e4m3_rne(np.array([464.0, 1e30, -1e30, -0.0, 0.0, 2.0 ** -10,
+                                       3 * 2.0 ** -11, 3 * 2.0 ** -10])).tolist() == \
+        [0x7E, 0x7E, 0xFE, 0x80, 0x00, 0x00, 0x01, 0x02]
+
+
 def test_e4m3_encode_matches_torch_on_every_bf16_value():
     # every non-negative finite bf16 value up to 464 (above that torch gives
     # NaN, the oracle saturates); torch's fp32 -> e4m3fn cast rounds to
