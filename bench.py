@@ -143,6 +143,47 @@ def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, w
     return res
 
 
+def time_offload(K, torch, wl, geometry, gs, hot, stream, steps, warmup, pages=256):
+    """Cold-page offload and onboard with the packed pool in pinned host
+    memory (timed beside the step): the encoder writes each packed page
+    across the host link and the decoder reads it back.  The yardstick is a
+    plain copy of the same packed bytes each way between device and pinned
+    host memory."""
+    dev = hot.device
+    pages = min(pages, int(wl.used_slots.shape[0]))
+    pb = K.kvfp4_packed_page_bytes(geometry)
+    slots = torch.from_numpy(wl.used_slots[:pages].astype(np.int32)).to(dev)
+    idx = torch.arange(pages, dtype=torch.int32, device=dev)
+    host_pool = torch.empty((pages, pb), dtype=torch.uint8).pin_memory()
+    dev_pool = torch.empty((pages, pb), dtype=torch.uint8, device=dev)
+    back = torch.empty((pages,) + tuple(hot.shape[1:]), dtype=hot.dtype, device=dev)
+    cases = {
+        "offload_quantize_to_host": lambda: K.kvfp4_quantize_pages(
+            geometry, hot, host_pool, pages, gs, slots, idx),
+        "onboard_dequantize_from_host": lambda: K.kvfp4_dequantize_pages(
+            geometry, host_pool, back, pages, gs, idx, idx),
+        "copy_device_to_host": lambda: host_pool.copy_(dev_pool, non_blocking=True),
+        "copy_host_to_device": lambda: dev_pool.copy_(host_pool, non_blocking=True),
+    }
+    res = {"pages": pages, "packed_bytes": pages * pb}
+    for name, fn in cases.items():
+        for _ in range(warmup):
+            fn()
+        evs = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        res[name] = {"avg_us": round(us, 1),
+                     "host_link_GB/s": round(pages * pb / (us * 1e-6) / 1e9, 2)}
+    return res
+
+
 def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
                  step_bytes: float) -> dict:
     """The oracle as it stands, on one host thread, over a bounded sample of
@@ -375,6 +416,11 @@ def main():
         append = time_append(K, torch, wl, geometry, gs, hot, packed, stream,
                              (lambda: None) if args.no_flush else evict, args.steps, args.warmup)
 
+    offload = None
+    if wl is not None and not args.no_append:
+        offload = time_offload(K, torch, wl, geometry, gs, hot, stream, min(args.steps, 10),
+                               min(args.warmup, 2))
+
     cpu = None
     if wl is not None and not args.no_cpu_baseline:
         try:
@@ -397,6 +443,7 @@ def main():
         "kernels": kern,
         "copy_yardstick": copy,
         "token_rows": append,
+        "host_offload": offload,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),

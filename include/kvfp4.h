@@ -83,6 +83,11 @@ size_t kvfp4_packed_page_bytes(const kvfp4_geometry* g);
  *   hot_pool    bf16 slots [hot_pool_pages][2*E bytes]           (read)
  *   src_slots   int32 [num_pages] hot slot of page i; NULL = i
  *   packed_pool packed slots [packed_pool_pages][9*E/16 bytes]  (written)
+ *               device memory, or pinned host memory from hipHostMalloc
+ *               (mapped into the GPU's address space): then the encoder's
+ *               stores cross the host link directly and the compression
+ *               rides the offload copy (same page, NVFP4 Cold-Page
+ *               Compression: compress while the page leaves the GPU).
  *   dst_slots   int32 [num_pages] packed slot of page i; NULL = i
  *   global_scale HOST float [num_kv_tensors]: finite, > 0, and
  *               2688 * gs <= FLT_MAX.
@@ -97,7 +102,8 @@ int32_t kvfp4_quantize_pages(const kvfp4_geometry* g, const void* hot_pool,
 
 /* Decode packed pages back into bf16 hot slots (onboard), bit-exact per the
  * arithmetic above.  Same argument rules as kvfp4_quantize_pages with the
- * roles of the pools swapped. */
+ * roles of the pools swapped; packed_pool may likewise be pinned host
+ * memory, read across the host link by the decoder. */
 int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
                                int32_t packed_pool_pages, const int32_t* src_slots,
                                void* hot_pool, int32_t hot_pool_pages,

@@ -108,12 +108,15 @@ def _check(status: int) -> int:
     return status
 
 
-def _ptr(t) -> Optional[int]:
-    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+def _ptr(t, host_ok: bool = False) -> Optional[int]:
+    """Device pointer of a contiguous GPU tensor (None -> NULL).  With
+    ``host_ok`` a pinned host tensor is accepted too: pinned host memory is
+    mapped into the GPU's address space at the same address."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError("tensor must live on the GPU")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError("tensor must live on the GPU" +
+                         (" or in pinned host memory" if host_ok else ""))
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr()
@@ -148,22 +151,26 @@ def kvfp4_packed_page_bytes(geometry) -> int:
 
 def kvfp4_quantize_pages(geometry, hot_pool, packed_pool, num_pages: int, global_scale,
                          src_slots=None, dst_slots=None, stream=None) -> None:
-    """Encode ``num_pages`` bf16 pages of ``hot_pool`` into ``packed_pool``."""
+    """Encode ``num_pages`` bf16 pages of ``hot_pool`` into ``packed_pool``
+    (device memory, or pinned host memory: the offload path)."""
     lib = load_library()
     g = Geometry.of(geometry)
     _check(lib.kvfp4_quantize_pages(
         ctypes.byref(g), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)), _ptr(src_slots),
-        _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)), _ptr(dst_slots),
+        _ptr(packed_pool, host_ok=True), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        _ptr(dst_slots),
         int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
 
 
 def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, global_scale,
                            src_slots=None, dst_slots=None, stream=None) -> None:
-    """Decode ``num_pages`` packed pages of ``packed_pool`` into ``hot_pool``."""
+    """Decode ``num_pages`` packed pages of ``packed_pool`` (device memory, or
+    pinned host memory: the onboard path) into ``hot_pool``."""
     lib = load_library()
     g = Geometry.of(geometry)
     _check(lib.kvfp4_dequantize_pages(
-        ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        ctypes.byref(g), _ptr(packed_pool, host_ok=True),
+        _pages(packed_pool, kvfp4_packed_page_bytes(g)),
         _ptr(src_slots), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
         _ptr(dst_slots), int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
 

@@ -215,3 +215,13 @@ def test_python_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "_lib", None)
     with pytest.raises(ImportError):
         K.load_library()
+
+
+def test_binding_rejects_pageable_host_tensors():
+    import torch
+    t = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        K._ptr(t)
+    with pytest.raises(ValueError):
+        K._ptr(t, host_ok=True)  # pageable host memory is not mapped for the GPU
+    assert K._ptr(None) is None

@@ -358,3 +358,38 @@ def test_gather_prefix_full_size():
     for dt, got in (("bf16", got16), ("fp8", got8)):
         ref = O.gather_dequantize(packed, g, gs, slots[sample], page_rows[sample], dt)
         assert np.array_equal(got[sample], ref), dt
+
+
+def test_offload_to_pinned_host_and_back():
+    """The cold-page path with the packed pool in pinned host memory: the
+    encoder writes across the host link and the decoder reads back across
+    it.  The host bytes must equal the oracle's (sampled pages) and the
+    device-pool encoding (every page), and the decoded pages the device
+    decoder's."""
+    require_gpu()
+    geometry = (2, 64, 8, 128)
+    g = O.Geometry(*geometry)
+    rng = np.random.default_rng(9)
+    n_pages = 96
+    gs = [float(np.float32(0.03)), float(np.float32(0.01))]
+    hot = W.f32_to_bf16_bits(rng.standard_normal((n_pages, *g.row_shape)).astype(np.float32))
+    src = rng.permutation(n_pages).astype(np.int32)
+    dst = rng.permutation(n_pages + 5)[:n_pages].astype(np.int32)
+    hot_d = dev(hot.view(np.int16))
+    pb = O.packed_page_bytes(g)
+    host_pool = torch.zeros((n_pages + 5, pb), dtype=torch.uint8).pin_memory()
+    dev_pool = torch.zeros((n_pages + 5, pb), dtype=torch.uint8, device="cuda")
+    K.kvfp4_quantize_pages(geometry, hot_d, host_pool, n_pages, gs, dev(src), dev(dst))
+    K.kvfp4_quantize_pages(geometry, hot_d, dev_pool, n_pages, gs, dev(src), dev(dst))
+    torch.cuda.synchronize()
+    got = host_pool.numpy().copy()
+    assert np.array_equal(got, host(dev_pool))
+    sample = rng.choice(n_pages, 6, replace=False)
+    ref = np.zeros((n_pages + 5, pb), np.uint8)
+    O.quantize_pages(hot, g, len(sample), gs, ref, src[sample], dst[sample])
+    assert np.array_equal(got[dst[sample]], ref[dst[sample]])
+    back_h = torch.zeros_like(hot_d)
+    back_d = torch.zeros_like(hot_d)
+    K.kvfp4_dequantize_pages(geometry, host_pool, back_h, n_pages, gs, dev(dst), dev(src))
+    K.kvfp4_dequantize_pages(geometry, dev_pool, back_d, n_pages, gs, dev(dst), dev(src))
+    assert np.array_equal(host(back_h), host(back_d))
