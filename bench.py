@@ -184,6 +184,47 @@ def time_offload(K, torch, wl, geometry, gs, hot, stream, steps, warmup, pages=2
     return res
 
 
+def time_rope_layouts(K, torch, wl, geometry, gs, hot, stream, evict, steps, warmup, pages=1024):
+    """Cold-page codec with K's last 64 dims (the MLA latent's RoPE part) in
+    each storage variant, timed beside the step on up to 1024 pages: bytes
+    are the hot page read or written plus the packed slot with its
+    extension."""
+    dev = hot.device
+    pages = min(pages, int(wl.used_slots.shape[0]))
+    slots = torch.from_numpy(wl.used_slots[:pages].astype(np.int32)).to(dev)
+    idx = torch.arange(pages, dtype=torch.int32, device=dev)
+    back = torch.empty((pages,) + tuple(hot.shape[1:]), dtype=hot.dtype, device=dev)
+    hot_b = K.kvfp4_hot_page_bytes(geometry)
+    res = {"pages": pages, "rope_dims": 64}
+    for mode, name in ((1, "bf16"), (2, "2fp4")):
+        rope = (64, mode)
+        pb = K.kvfp4_packed_page_bytes_rope(geometry, rope)
+        pool = torch.empty((pages, pb), dtype=torch.uint8, device=dev)
+        legs = {"quantize": lambda: K.kvfp4_quantize_pages_rope(geometry, rope, hot, pool, pages,
+                                                                 gs, slots, idx),
+                "dequantize": lambda: K.kvfp4_dequantize_pages_rope(geometry, rope, pool, back,
+                                                                     pages, gs, idx, idx)}
+        out = {"slot_bytes": pb}
+        for leg, fn in legs.items():
+            for _ in range(warmup):
+                fn()
+            evs = []
+            for _ in range(steps):
+                evict()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+            out[leg] = {"avg_us": round(us, 1),
+                        "GB/s": round(pages * (hot_b + pb) / (us * 1e-6) / 1e9, 1)}
+        res[name] = out
+    return res
+
+
 def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
                  step_bytes: float) -> dict:
     """The oracle as it stands, on one host thread, over a bounded sample of
@@ -421,6 +462,12 @@ def main():
         offload = time_offload(K, torch, wl, geometry, gs, hot, stream, min(args.steps, 10),
                                min(args.warmup, 2))
 
+    rope = None
+    if wl is not None and not args.no_append:
+        rope = time_rope_layouts(K, torch, wl, geometry, gs, hot, stream,
+                                 (lambda: None) if args.no_flush else evict,
+                                 min(args.steps, 10), min(args.warmup, 2))
+
     cpu = None
     if wl is not None and not args.no_cpu_baseline:
         try:
@@ -444,6 +491,7 @@ def main():
         "copy_yardstick": copy,
         "token_rows": append,
         "host_offload": offload,
+        "rope_layouts": rope,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall, 3),

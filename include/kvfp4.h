@@ -161,6 +161,50 @@ int32_t kvfp4_gather_dequantize(const kvfp4_geometry* g, const void* packed_pool
                                 const int32_t* token_rows, int32_t num_tokens, void* out,
                                 int32_t out_dtype, const float* global_scale, void* stream);
 
+/* RoPE-part storage of the cold-page codec ("KV Cache Compression in
+ * TensorRT LLM", How It Works / The RoPE part of K).  The RoPE part is the
+ * last rope_dims dims of every head row of tensor 0 (K; for MLA the latent,
+ * whose last 64 of 576 dims carry the rotary embedding).
+ *   KVFP4_ROPE_NVFP4  quantized like the rest (the plain layout)
+ *   KVFP4_ROPE_BF16   kept at its original bf16 precision
+ *   KVFP4_ROPE_2FP4   two NVFP4 layers: the second encodes the exact
+ *                     residual x - D1 of the first with the same rules and
+ *                     tensor scale; decoding gives bf16_RNE(D1 + D2), one
+ *                     rounding of the exact sum.  A zero residual keeps the
+ *                     sign of x.
+ * A packed slot keeps the plain layout (every value NVFP4-encoded) and
+ * appends an extension region [T][H][rope_dims]: bf16 values (mode BF16),
+ * or the second layer's data [T][H][rope_dims/2] then its scales
+ * [T][H][rope_dims/16] (mode 2FP4).  The decoder returns the RoPE dims from
+ * the extension.  Pages in these layouts are for the cold-page path (they
+ * are decoded before attention reads them); the decode-attention call reads
+ * the plain layout only. */
+#define KVFP4_ROPE_NVFP4 0
+#define KVFP4_ROPE_BF16 1
+#define KVFP4_ROPE_2FP4 2
+typedef struct kvfp4_rope_layout {
+  int32_t rope_dims; /* multiple of 16, 0 < rope_dims <= head_dim */
+  int32_t mode;      /* KVFP4_ROPE_*                              */
+} kvfp4_rope_layout;
+
+/* Bytes of one packed slot in this layout (0 when invalid). */
+size_t kvfp4_packed_page_bytes_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope);
+
+/* kvfp4_quantize_pages / kvfp4_dequantize_pages for slots in a RoPE layout;
+ * same arguments plus `rope`, slots of kvfp4_packed_page_bytes_rope bytes.
+ * KVFP4_ERR_UNSUPPORTED unless the plain slot size and the extension size
+ * are both multiples of 16 bytes (true for page sizes of 16 or more). */
+int32_t kvfp4_quantize_pages_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope,
+                                  const void* hot_pool, int32_t hot_pool_pages,
+                                  const int32_t* src_slots, void* packed_pool,
+                                  int32_t packed_pool_pages, const int32_t* dst_slots,
+                                  int32_t num_pages, const float* global_scale, void* stream);
+int32_t kvfp4_dequantize_pages_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope,
+                                    const void* packed_pool, int32_t packed_pool_pages,
+                                    const int32_t* src_slots, void* hot_pool,
+                                    int32_t hot_pool_pages, const int32_t* dst_slots,
+                                    int32_t num_pages, const float* global_scale, void* stream);
+
 /* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
  * current device (0 is a valid answer). */
 size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,

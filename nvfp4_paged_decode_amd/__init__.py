@@ -30,6 +30,7 @@ KVFP4_ROWS_FP8_E4M3 = 1
 EXPORTS = (
     "kvfp4_hot_page_bytes", "kvfp4_packed_page_bytes", "kvfp4_quantize_pages",
     "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_gather_dequantize",
+    "kvfp4_packed_page_bytes_rope", "kvfp4_quantize_pages_rope", "kvfp4_dequantize_pages_rope",
     "kvfp4_decode_workspace_bytes",
     "kvfp4_paged_decode_attention", "kvfp4_status_string", "kvfp4_last_error_message",
 )
@@ -44,6 +45,21 @@ class Geometry(ctypes.Structure):
     @classmethod
     def of(cls, g) -> "Geometry":
         return g if isinstance(g, cls) else cls(*[int(v) for v in g])
+
+
+KVFP4_ROPE_NVFP4 = 0
+KVFP4_ROPE_BF16 = 1
+KVFP4_ROPE_2FP4 = 2
+
+
+class RopeLayout(ctypes.Structure):
+    """``kvfp4_rope_layout``: (rope_dims, mode)."""
+
+    _fields_ = [("rope_dims", ctypes.c_int32), ("mode", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, r) -> "RopeLayout":
+        return r if isinstance(r, cls) else cls(*[int(v) for v in r])
 
 
 class KvFp4Error(RuntimeError):
@@ -87,6 +103,13 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_append_quantize.restype = I32
     lib.kvfp4_gather_dequantize.argtypes = [G, P, I32, P, P, I32, P, I32, P, P]
     lib.kvfp4_gather_dequantize.restype = I32
+    RL = ctypes.POINTER(RopeLayout)
+    lib.kvfp4_packed_page_bytes_rope.argtypes = [G, RL]
+    lib.kvfp4_packed_page_bytes_rope.restype = SZ
+    lib.kvfp4_quantize_pages_rope.argtypes = [G, RL] + codec[1:]
+    lib.kvfp4_quantize_pages_rope.restype = I32
+    lib.kvfp4_dequantize_pages_rope.argtypes = [G, RL] + codec[1:]
+    lib.kvfp4_dequantize_pages_rope.restype = I32
     lib.kvfp4_decode_workspace_bytes.argtypes = [G, I32, I32, I32, I32]
     lib.kvfp4_decode_workspace_bytes.restype = SZ
     lib.kvfp4_paged_decode_attention.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32, P, I32,
@@ -173,6 +196,36 @@ def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, glob
         _pages(packed_pool, kvfp4_packed_page_bytes(g)),
         _ptr(src_slots), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
         _ptr(dst_slots), int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_packed_page_bytes_rope(geometry, rope) -> int:
+    return int(load_library().kvfp4_packed_page_bytes_rope(
+        ctypes.byref(Geometry.of(geometry)), ctypes.byref(RopeLayout.of(rope))))
+
+
+def kvfp4_quantize_pages_rope(geometry, rope, hot_pool, packed_pool, num_pages: int,
+                              global_scale, src_slots=None, dst_slots=None, stream=None) -> None:
+    """kvfp4_quantize_pages into slots of a RoPE layout ``(rope_dims, mode)``."""
+    lib = load_library()
+    g, r = Geometry.of(geometry), RopeLayout.of(rope)
+    _check(lib.kvfp4_quantize_pages_rope(
+        ctypes.byref(g), ctypes.byref(r), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
+        _ptr(src_slots), _ptr(packed_pool, host_ok=True),
+        _pages(packed_pool, kvfp4_packed_page_bytes_rope(g, r)), _ptr(dst_slots), int(num_pages),
+        _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_dequantize_pages_rope(geometry, rope, packed_pool, hot_pool, num_pages: int,
+                                global_scale, src_slots=None, dst_slots=None,
+                                stream=None) -> None:
+    """kvfp4_dequantize_pages from slots of a RoPE layout ``(rope_dims, mode)``."""
+    lib = load_library()
+    g, r = Geometry.of(geometry), RopeLayout.of(rope)
+    _check(lib.kvfp4_dequantize_pages_rope(
+        ctypes.byref(g), ctypes.byref(r), _ptr(packed_pool, host_ok=True),
+        _pages(packed_pool, kvfp4_packed_page_bytes_rope(g, r)), _ptr(src_slots), _ptr(hot_pool),
+        _pages(hot_pool, kvfp4_hot_page_bytes(g)), _ptr(dst_slots), int(num_pages),
+        _scales(global_scale, g.num_kv_tensors), _stream(stream)))
 
 
 def kvfp4_append_quantize(geometry, rows, token_slots, token_rows, packed_pool, global_scale,

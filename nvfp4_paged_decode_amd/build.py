@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvfp4.so")
 
-SOURCES = ["api.hip", "codec.hip", "decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip", "decode_mla.hip"]
+SOURCES = ["api.hip", "codec.hip", "decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip",
+           "decode_mla.hip", "rope.hip"]
 
 # gfx950 only.  Packed-fp32 VALU ops are switched off (the host pass warns
 # that it does not know the feature; harmless).  No fast-math: the codec

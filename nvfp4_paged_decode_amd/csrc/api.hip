@@ -106,6 +106,45 @@ int32_t check_codec(const kvfp4_geometry* g, const void* from, int32_t from_page
 
 }  // namespace
 
+namespace {
+
+long long rope_ext_bytes(const kvfp4_geometry* g, const kvfp4_rope_layout* r) {
+  const long long n = (long long)g->page_size * g->num_kv_heads * r->rope_dims;
+  if (r->mode == KVFP4_ROPE_BF16) return 2 * n;
+  if (r->mode == KVFP4_ROPE_2FP4) return n / 2 + n / 16;
+  return 0;
+}
+
+bool rope_valid(const kvfp4_geometry* g, const kvfp4_rope_layout* r) {
+  return geometry_valid(g) && r && r->rope_dims > 0 && r->rope_dims % 16 == 0 &&
+         r->rope_dims <= g->head_dim &&
+         (r->mode == KVFP4_ROPE_NVFP4 || r->mode == KVFP4_ROPE_BF16 ||
+          r->mode == KVFP4_ROPE_2FP4);
+}
+
+int32_t check_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* r) {
+  if (!r) return fail(KVFP4_ERR_INVALID_ARG, "rope layout is NULL");
+  if (!rope_valid(g, r))
+    return fail(KVFP4_ERR_INVALID_ARG,
+                "invalid rope layout (rope_dims=%d mode=%d): need rope_dims a positive multiple "
+                "of 16 <= head_dim and mode KVFP4_ROPE_NVFP4, _BF16 or _2FP4",
+                r->rope_dims, r->mode);
+  const long long base = to_geom(g).packed_bytes();
+  if (base % 16 != 0 || rope_ext_bytes(g, r) % 16 != 0)
+    return fail(KVFP4_ERR_UNSUPPORTED,
+                "rope layouts need the plain slot (%lld B) and the extension (%lld B) to be "
+                "multiples of 16 bytes", base, rope_ext_bytes(g, r));
+  return KVFP4_OK;
+}
+
+kvfp4::Geom rope_geom(const kvfp4_geometry* g, const kvfp4_rope_layout* r) {
+  kvfp4::Geom k = to_geom(g);
+  k.stride = k.packed_bytes() + rope_ext_bytes(g, r);
+  return k;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t kvfp4_hot_page_bytes(const kvfp4_geometry* g) {
@@ -146,6 +185,59 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
   hipError_t e = kvfp4::launch_dequantize(to_geom(g), packed_pool, packed_pool_pages, src_slots,
                                           hot_pool, hot_pool_pages, dst_slots, num_pages,
                                           global_scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "dequantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t kvfp4_packed_page_bytes_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope) {
+  if (!rope_valid(g, rope)) return 0;
+  return (size_t)(to_geom(g).packed_bytes() + rope_ext_bytes(g, rope));
+}
+
+int32_t kvfp4_quantize_pages_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope,
+                                  const void* hot_pool, int32_t hot_pool_pages,
+                                  const int32_t* src_slots, void* packed_pool,
+                                  int32_t packed_pool_pages, const int32_t* dst_slots,
+                                  int32_t num_pages, const float* global_scale, void* stream) {
+  int32_t st = check_codec(g, hot_pool, hot_pool_pages, src_slots, packed_pool,
+                           packed_pool_pages, dst_slots, num_pages, global_scale, "hot_pool",
+                           "packed_pool");
+  if (st) return st;
+  st = check_rope(g, rope);
+  if (st) return st;
+  if (num_pages == 0) return ok();
+  const kvfp4::Geom k = rope_geom(g, rope);
+  hipError_t e = kvfp4::launch_quantize(k, hot_pool, hot_pool_pages, src_slots, packed_pool,
+                                        packed_pool_pages, dst_slots, num_pages, global_scale,
+                                        (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = kvfp4::launch_rope_encode(k, rope->rope_dims, rope->mode, k.packed_bytes(), hot_pool,
+                                  hot_pool_pages, src_slots, packed_pool, packed_pool_pages,
+                                  dst_slots, num_pages, global_scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t kvfp4_dequantize_pages_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope,
+                                    const void* packed_pool, int32_t packed_pool_pages,
+                                    const int32_t* src_slots, void* hot_pool,
+                                    int32_t hot_pool_pages, const int32_t* dst_slots,
+                                    int32_t num_pages, const float* global_scale, void* stream) {
+  int32_t st = check_codec(g, packed_pool, packed_pool_pages, src_slots, hot_pool,
+                           hot_pool_pages, dst_slots, num_pages, global_scale, "packed_pool",
+                           "hot_pool");
+  if (st) return st;
+  st = check_rope(g, rope);
+  if (st) return st;
+  if (num_pages == 0) return ok();
+  const kvfp4::Geom k = rope_geom(g, rope);
+  hipError_t e = kvfp4::launch_dequantize(k, packed_pool, packed_pool_pages, src_slots, hot_pool,
+                                          hot_pool_pages, dst_slots, num_pages, global_scale,
+                                          (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = kvfp4::launch_rope_decode(k, rope->rope_dims, rope->mode, k.packed_bytes(), packed_pool,
+                                  packed_pool_pages, src_slots, hot_pool, hot_pool_pages,
+                                  dst_slots, num_pages, global_scale, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "dequantize launch: %s", hipGetErrorString(e));
   return ok();
 }

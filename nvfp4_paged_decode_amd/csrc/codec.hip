@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const int ds = page_slot(dst, p, packed_pages);
     if (ss < 0 || ds < 0) continue;
     const uint8_t* in = hot + (long long)ss * g.hot_bytes();
-    uint8_t* out = packed + (long long)ds * g.packed_bytes();
+    uint8_t* out = packed + (long long)ds * g.page_stride();
     auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)in, (short)0, (int)g.hot_bytes(), kRsrcFlags);
     auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)g.packed_bytes(), kRsrcFlags);
     for (int h0 = 0; h0 < hpp; h0 += kThreads * kQuantUnroll) {
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const int ss = page_slot(src, p, packed_pages);
     const int ds = page_slot(dst, p, hot_pages);
     if (ss < 0 || ds < 0) continue;
-    const uint8_t* in = packed + (long long)ss * g.packed_bytes();
+    const uint8_t* in = packed + (long long)ss * g.page_stride();
     uint8_t* out = hot + (long long)ds * g.hot_bytes();
     auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)in, (short)0, (int)g.packed_bytes(), kRsrcFlags);
     auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)g.hot_bytes(), kRsrcFlags);

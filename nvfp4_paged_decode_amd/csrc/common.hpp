@@ -21,6 +21,8 @@ struct Geom {
   int T;   // tokens per page
   int H;   // KV heads
   int D;   // head dim (multiple of 16)
+  long long stride = 0;  // bytes between packed slots; 0: packed_bytes()
+  __host__ __device__ long long page_stride() const { return stride ? stride : packed_bytes(); }
   __host__ __device__ long long elems() const { return (long long)nt * T * H * D; }
   __host__ __device__ long long hot_bytes() const { return 2 * elems(); }
   __host__ __device__ long long data_bytes() const { return elems() / 2; }
@@ -75,10 +77,12 @@ __device__ inline float e2m1_mag_to_float(uint32_t m) {
   return __uint_as_float(bits);
 }
 
-// bf16 bits of a finite fp64 value, rounded to nearest even once (used by
-// the dequantizer when the tensor scale is so small that fp32 products
-// would leave the normal range).
-__device__ inline uint32_t bf16_rne_from_f64(double v) {
+// bf16 bits of a finite fp64 value, rounded to nearest even once.  When v
+// is the rounded head of an exact value v + e (|e| below half an fp64 ulp
+// of v), tie_bias is the sign of e relative to v: +1 if the exact magnitude
+// is above |v|, -1 if below, 0 if v is exact.  It only matters when v lies
+// exactly halfway between two bf16 values.
+__device__ inline uint32_t bf16_rne_from_f64(double v, int tie_bias = 0) {
   uint64_t b = (uint64_t)__double_as_longlong(v);
   uint32_t sign = (uint32_t)(b >> 63) << 15;
   int ex = (int)((b >> 52) & 0x7FF);
@@ -99,7 +103,7 @@ __device__ inline uint32_t bf16_rne_from_f64(double v) {
   uint64_t keep = m53 >> shift;
   uint64_t rem = m53 & ((1ull << shift) - 1);
   uint64_t half = 1ull << (shift - 1);
-  keep += (rem > half || (rem == half && (keep & 1))) ? 1 : 0;
+  keep += (rem > half || (rem == half && (tie_bias > 0 || (tie_bias == 0 && (keep & 1))))) ? 1 : 0;
   uint32_t bits = base + (uint32_t)keep;
   if (bits >= 0x7F80u) bits = 0x7F80u;  // overflow to inf
   return sign | bits;
@@ -122,6 +126,15 @@ hipError_t launch_append(const Geom& g, const void* rows, bool fp8, int num_toke
 hipError_t launch_gather(const Geom& g, const void* packed, int packed_pages, const int32_t* slots,
                          const int32_t* page_rows, int num_tokens, void* out, bool fp8,
                          const float* gs, hipStream_t stream);
+
+hipError_t launch_rope_encode(const Geom& g, int rope_dims, int mode, long long ext_off,
+                              const void* hot, int hot_pages, const int32_t* src, void* packed,
+                              int packed_pages, const int32_t* dst, int num_pages, const float* gs,
+                              hipStream_t stream);
+hipError_t launch_rope_decode(const Geom& g, int rope_dims, int mode, long long ext_off,
+                              const void* packed, int packed_pages, const int32_t* src, void* hot,
+                              int hot_pages, const int32_t* dst, int num_pages, const float* gs,
+                              hipStream_t stream);
 
 struct DecodeArgs {
   Geom g;

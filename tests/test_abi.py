@@ -225,3 +225,42 @@ def test_binding_rejects_pageable_host_tensors():
     with pytest.raises(ValueError):
         K._ptr(t, host_ok=True)  # pageable host memory is not mapped for the GPU
     assert K._ptr(None) is None
+
+
+def test_rope_page_sizes(lib):
+    g = K.Geometry(1, 64, 1, 576)
+    base = 64 * 576 * 9 // 16
+    sizes = [K.kvfp4_packed_page_bytes_rope(g, (64, m)) for m in range(3)]
+    assert sizes == [base, base + 64 * 64 * 2, base + 64 * 64 * 9 // 16]
+    for bad in [(0, 1), (8, 1), (592, 1), (64, 3), (64, -1)]:
+        assert K.kvfp4_packed_page_bytes_rope(g, bad) == 0
+    assert lib.kvfp4_packed_page_bytes_rope(ctypes.byref(g), None) == 0
+
+
+@pytest.mark.parametrize("rope,code", [
+    (None, K.KVFP4_ERR_INVALID_ARG),
+    ((0, 2), K.KVFP4_ERR_INVALID_ARG),
+    ((24, 2), K.KVFP4_ERR_INVALID_ARG),
+    ((144, 2), K.KVFP4_ERR_INVALID_ARG),   # more than head_dim
+    ((64, 5), K.KVFP4_ERR_INVALID_ARG),
+])
+def test_rope_codec_rejects_invalid_layouts(lib, rope, code):
+    g = K.Geometry(2, 64, 8, 128)
+    arr = (ctypes.c_float * 2)(1.0, 1.0)
+    r = ctypes.byref(K.RopeLayout(*rope)) if rope is not None else None
+    for fn in (lib.kvfp4_quantize_pages_rope, lib.kvfp4_dequantize_pages_rope):
+        st = fn(ctypes.byref(g), r, FAKE, 8, None, FAKE + 0x100, 8, None, 4, arr, None)
+        assert st == code
+        assert lib.kvfp4_last_error_message().decode() != ""
+
+
+def test_rope_codec_needs_16_byte_slots(lib):
+    # 4 tokens x 1 head x 16 dims: a 36-byte plain slot
+    g = K.Geometry(1, 4, 1, 16)
+    arr = (ctypes.c_float * 1)(1.0)
+    st = lib.kvfp4_quantize_pages_rope(ctypes.byref(g), ctypes.byref(K.RopeLayout(16, 2)), FAKE,
+                                       8, None, FAKE + 0x100, 8, None, 4, arr, None)
+    assert st == K.KVFP4_ERR_UNSUPPORTED
+    # the plain codec takes the same geometry
+    assert lib.kvfp4_quantize_pages(ctypes.byref(g), None, 0, None, None, 0, None, 0, arr,
+                                    None) == K.KVFP4_OK
