@@ -394,6 +394,7 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
                                      : (size_t)(plan.nwg + batch) * num_q_heads;
   a.ws_o = (float*)workspace;
   a.ws_ml = a.ws_o + partials * v_dim;
+  a.ws_idx = reinterpret_cast<int32_t*>(a.ws_ml + partials * 2);
   hipError_t e = kvfp4::launch_decode(plan, a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();

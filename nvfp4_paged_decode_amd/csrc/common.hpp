@@ -157,6 +157,10 @@ struct DecodeArgs {
   int nwg;
   float* ws_o;           // partial outputs, v_dim floats each
   float* ws_ml;          // partial (max, sum), scores in log2 units
+  // Balanced kernels: the first and last workgroup whose range holds pages
+  // of sequence b ([batch][2], written for every sequence with pages), then
+  // the batch's page count; the merge reads these instead of rescanning.
+  int32_t* ws_idx;
 };
 
 // Which decode kernel a shape uses, and how it splits the context.

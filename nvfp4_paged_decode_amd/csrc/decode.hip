@@ -186,169 +186,131 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   }
 }
 
-__device__ inline long long wave_sum_ll(long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 __device__ inline uint32_t bf16_rne_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ inline float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) r = fmaxf(r, red[w]);
-  __syncthreads();
-  return r;
-}
+constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
 
-__device__ inline float block_sum(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) r += red[w];
-  __syncthreads();
-  return r;
-}
-
-constexpr int kMergeChunk = 512;  // partial weights staged in LDS per pass
-
-// Merge for the balanced kernels: sequence b's partials sit in slots
-// w + b for every workgroup w whose page range overlaps b's pages.  One
-// workgroup per (head, sequence).  The page prefix over the batch, the
-// running maximum and the weight sum are workgroup-wide reductions over
-// the slots; the weights of up to kMergeChunk slots at a time sit in LDS.
-// Output: with VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte
-// aligned out) a thread owns 4 columns of one group of slots (slot index
-// mod G, G = threads / (v_dim / 4) groups when v_dim is small), the groups
-// are summed through LDS; otherwise one column per thread.
-template <bool VEC>
+// Merge for the balanced kernels: sequence b's partials sit in slots w + b
+// for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
+// (recorded by the decode kernel with the batch's page count).  One
+// workgroup per (head, sequence), two dependent rounds of global reads:
+// the sequence's length and slot range, then every partial at once.
+// Slots are split over G thread groups (G = threads / (v_dim / 4) when
+// v_dim is small, else 1); a group folds its slots with a running maximum,
+// kMergeBatch of them per round of loads, and the groups combine through
+// LDS.  VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte aligned
+// out): a thread owns 4 columns; otherwise one column per thread, G = 1.
+template <bool VEC, int K4>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
+  static_assert(!VEC || K4 * 4 * kMergeThreads >= 512, "v_dim up to 512");
   const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  __shared__ long long s_red[2][kMergeThreads / 64];
-  __shared__ float s_f[kMergeThreads / 64];
-  __shared__ float s_wt[kMergeChunk];
+  __shared__ float s_m[kMergeThreads], s_l[kMergeThreads];
   __shared__ f32x4 s_acc[kMergeThreads];
-  long long tot = 0, start = 0;
-  for (int i = tid; i < a.batch; i += kMergeThreads) {
-    const long long np = pages_of(a, i);
-    tot += np;
-    if (i < b) start += np;
-  }
-  tot = wave_sum_ll(tot);
-  start = wave_sum_ll(start);
-  if ((tid & 63) == 0) {
-    s_red[0][tid >> 6] = tot;
-    s_red[1][tid >> 6] = start;
-  }
-  __syncthreads();
-  long long ptot = 0, first = 0;
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) {
-    ptot += s_red[0][w];
-    first += s_red[1][w];
-  }
-  const long long last = first + pages_of(a, b);
-  const int nwg = a.nwg;
-  int w_lo = 0, w_hi = -1;
-  if (last > first) {
-    // first workgroup whose range ends after `first`, last one starting before `last`
-    int w = (int)(first * nwg / ptot);
-    while (w > 0 && range_begin(ptot, w, nwg) > first) --w;
-    while (range_begin(ptot, w + 1, nwg) <= first) ++w;
-    w_lo = w;
-    int hi = (int)(last * nwg / ptot);
-    if (hi < w_lo) hi = w_lo;
-    if (hi > nwg - 1) hi = nwg - 1;
-    while (hi > w_lo && range_begin(ptot, hi, nwg) >= last) --hi;
-    while (hi + 1 < nwg && range_begin(ptot, hi + 1, nwg) < last) ++hi;
-    w_hi = hi;
-  }
   const long long row = (long long)b * a.hq + head;
-  // a slot holds a partial only if its workgroup's range is not empty
-  auto ms_of = [&](int v) -> float {
-    if (range_begin(ptot, v, nwg) >= range_begin(ptot, v + 1, nwg)) return -INFINITY;
-    return a.ws_ml[(((long long)v + b) * a.hq + head) * 2];
+  const int L = clamped_len(a, b);
+  const int nwg = a.nwg;
+  int w_lo = a.ws_idx[2 * b], w_hi = a.ws_idx[2 * b + 1];
+  const long long ptot = a.ws_idx[2 * a.batch];
+  if (L == 0) {
+    for (int c = tid; c < a.v_dim; c += kMergeThreads) a.out[row * a.v_dim + c] = 0;
+    if (tid == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  // the decode kernel wrote both for every sequence with pages; clamp anyway
+  w_lo = w_lo < 0 ? 0 : (w_lo > nwg - 1 ? nwg - 1 : w_lo);
+  w_hi = w_hi < w_lo ? w_lo : (w_hi > nwg - 1 ? nwg - 1 : w_hi);
+  auto holds = [&](int v) {  // slot v + b holds a partial: v's range is not empty
+    return (long long)v * ptot / nwg < (long long)(v + 1) * ptot / nwg;
   };
-  float M = -INFINITY;
-  for (int v = w_lo + tid; v <= w_hi; v += kMergeThreads) M = fmaxf(M, ms_of(v));
-  M = block_max(M, s_f);
 
   const int D4 = a.v_dim / 4;
   const int G = VEC ? (D4 >= kMergeThreads ? 1 : kMergeThreads / D4) : 1;
   const int grp = VEC ? tid / (D4 >= kMergeThreads ? kMergeThreads : D4) : 0;
   const int d4 = VEC ? (D4 >= kMergeThreads ? tid : tid % D4) : tid;
-  f32x4 o4[(kMaxD / 4 + kMergeThreads - 1) / kMergeThreads];  // VEC: columns d4 + k*threads
-  float o1[(kMaxD + kMergeThreads - 1) / kMergeThreads];      // scalar: columns tid + k*threads
+  // K4: 4-column blocks per thread (VEC: ceil(v_dim / 4 / threads));
+  // K1: columns per thread otherwise
+  constexpr int K1 = VEC ? 1 : (kMaxD + kMergeThreads - 1) / kMergeThreads;
+  f32x4 o4[K4];
+  float o1[K1];
 #pragma unroll
-  for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) o4[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K4; ++k) o4[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) o1[k] = 0.f;
-  float Lpart = 0.f;
-  for (int c0 = w_lo; c0 <= w_hi; c0 += kMergeChunk) {
-    const int cn = (w_hi - c0 + 1) < kMergeChunk ? (w_hi - c0 + 1) : kMergeChunk;
-    for (int i = tid; i < cn; i += kMergeThreads) {
-      const float ms = ms_of(c0 + i);
-      float wt = 0.f;
-      if (ms != -INFINITY) {
-        wt = exp2f(ms - M);
-        Lpart += wt * a.ws_ml[(((long long)c0 + i + b) * a.hq + head) * 2 + 1];
-      }
-      s_wt[i] = wt;
-    }
-    __syncthreads();
-    if (VEC) {
-      if (grp < G) {
-        for (int i = grp; i < cn; i += G) {
-          const float wt = s_wt[i];
-          if (wt == 0.f) continue;
-          const float* src = a.ws_o + (((long long)c0 + i + b) * a.hq + head) * a.v_dim;
+  for (int k = 0; k < K1; ++k) o1[k] = 0.f;
+  float mg = -INFINITY, lg = 0.f;
+  if (grp < G) {
+    for (int v0 = w_lo + grp; v0 <= w_hi; v0 += G * kMergeBatch) {
+      // every load of this round is issued before any is used
+      float mv[kMergeBatch], lv[kMergeBatch];
+      f32x4 ov4[kMergeBatch][K4];
+      float ov1[kMergeBatch][K1];
 #pragma unroll
-          for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) {
+      for (int i = 0; i < kMergeBatch; ++i) {
+        const int v = v0 + i * G;
+        const bool ok = v <= w_hi && holds(v);
+        const long long sp = ((long long)v + b) * a.hq + head;
+        mv[i] = ok ? a.ws_ml[sp * 2] : -INFINITY;
+        lv[i] = ok ? a.ws_ml[sp * 2 + 1] : 0.f;
+        const float* src = a.ws_o + sp * a.v_dim;
+        if (VEC) {
+#pragma unroll
+          for (int k = 0; k < K4; ++k) {
             const int c = d4 + k * kMergeThreads;
-            if (c < D4) o4[k] += *reinterpret_cast<const f32x4*>(src + 4 * c) * wt;
+            ov4[i][k] = (ok && c < D4) ? *reinterpret_cast<const f32x4*>(src + 4 * c)
+                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < K1; ++k) {
+            const int c = tid + k * kMergeThreads;
+            ov1[i][k] = (ok && c < a.v_dim) ? src[c] : 0.f;
           }
         }
       }
-    } else {
-      for (int i = 0; i < cn; ++i) {
-        const float wt = s_wt[i];
-        if (wt == 0.f) continue;
-        const float* src = a.ws_o + (((long long)c0 + i + b) * a.hq + head) * a.v_dim;
 #pragma unroll
-        for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) {
-          const int c = tid + k * kMergeThreads;
-          if (c < a.v_dim) o1[k] += src[c] * wt;
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (mv[i] == -INFINITY) continue;  // no partial in this slot
+        const float mn = fmaxf(mg, mv[i]);
+        const float so = exp2f(mg - mn), sn = exp2f(mv[i] - mn);  // exp2(-inf) = 0
+        lg = lg * so + lv[i] * sn;
+        if (VEC) {
+#pragma unroll
+          for (int k = 0; k < K4; ++k) o4[k] = o4[k] * so + ov4[i][k] * sn;
+        } else {
+#pragma unroll
+          for (int k = 0; k < K1; ++k) o1[k] = o1[k] * so + ov1[i][k] * sn;
         }
+        mg = mn;
       }
     }
-    __syncthreads();  // s_wt is rewritten by the next chunk
   }
-  const float Lsum = block_sum(Lpart, s_f);
+  float M = mg, Lsum = lg;
+  if (VEC && G > 1) {
+    // combine the G groups (here D4 < threads, so one column block: k = 0)
+    if (d4 == 0 && grp < G) {
+      s_m[grp] = mg;
+      s_l[grp] = lg;
+    }
+    s_acc[tid] = o4[0];
+    __syncthreads();
+    M = -INFINITY;
+    for (int gg = 0; gg < G; ++gg) M = fmaxf(M, s_m[gg]);
+    Lsum = 0.f;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int gg = 0; gg < G; ++gg) {
+      if (s_m[gg] == -INFINITY) continue;
+      const float wgt = exp2f(s_m[gg] - M);
+      Lsum += s_l[gg] * wgt;
+      if (tid < D4) t += s_acc[gg * D4 + tid] * wgt;
+    }
+    o4[0] = t;
+  }
   const float inv = (Lsum > 0.f) ? a.gs_v / Lsum : 0.f;
   if (VEC) {
-    if (G > 1) {
-      // sum the G slot groups of each column block (D4 < threads: one k)
-      s_acc[tid] = o4[0];
-      __syncthreads();
-      if (tid < D4) {
-        f32x4 t = s_acc[tid];
-        for (int gg = 1; gg < G; ++gg) t += s_acc[gg * D4 + tid];
-        o4[0] = t;
-      }
-    }
 #pragma unroll
-    for (int k = 0; k < (int)(sizeof(o4) / sizeof(o4[0])); ++k) {
+    for (int k = 0; k < K4; ++k) {
       const int c = d4 + k * kMergeThreads;
       if (grp == 0 && c < D4) {
         const f32x4 o = o4[k] * inv;
@@ -360,7 +322,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < (int)(sizeof(o1) / sizeof(o1[0])); ++k) {
+    for (int k = 0; k < K1; ++k) {
       const int c = tid + k * kMergeThreads;
       if (c < a.v_dim) a.out[row * a.v_dim + c] = (uint16_t)bf16_rne_bits(o1[k] * inv);
     }
@@ -396,7 +358,9 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
     p.nwg = (int)(nwg > 0 ? nwg : 1);
     p.splits = 0;
     p.pages_per_split = 0;
-    p.workspace_bytes = (size_t)(p.nwg + batch) * hq * (size_t)(v_dim + 2) * sizeof(float);
+    // partials, then the merge's index ([batch][2] + the page count, padded)
+    p.workspace_bytes = (size_t)(p.nwg + batch) * hq * (size_t)(v_dim + 2) * sizeof(float) +
+                        (((size_t)2 * batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
     return p;
   }
   p.kernel = 0;
@@ -435,12 +399,9 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   } else {
     const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_o & 15) == 0 &&
                      ((uintptr_t)a.out & 7) == 0;
-    if (vec)
-      hipLaunchKernelGGL(merge_balanced_kernel<true>, dim3(a.hq, a.batch), dim3(kMergeThreads),
-                         0, stream, a);
-    else
-      hipLaunchKernelGGL(merge_balanced_kernel<false>, dim3(a.hq, a.batch), dim3(kMergeThreads),
-                         0, stream, a);
+    // the balanced kernels have v_dim <= 512: one f32x4 column block a thread
+    auto kernel = vec ? merge_balanced_kernel<true, 1> : merge_balanced_kernel<false, 1>;
+    hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

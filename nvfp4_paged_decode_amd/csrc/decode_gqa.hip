@@ -244,6 +244,7 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
 
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
+  note_total(a, w, rng.ptot);
   long long seq_start = rng.start_first;
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
     const int L = uniform(clamped_len(a, b));
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
     const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;
+    note_segment(a, w, b, p_lo, p_hi, npages);
 
     Stream<G> st;
     const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q) +

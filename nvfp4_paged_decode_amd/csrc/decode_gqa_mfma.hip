@@ -250,6 +250,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
+  note_total(a, w, rng.ptot);
   long long seq_start = rng.start_first;
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
     const int L = uniform(clamped_len(a, b));
@@ -259,6 +260,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;
+    note_segment(a, w, b, p_lo, p_hi, npages);
     tg.L = L;
     const long long t_lo = p_lo * tg.tiles_per_page;
     long long t_hi = p_hi * tg.tiles_per_page;

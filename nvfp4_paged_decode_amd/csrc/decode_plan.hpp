@@ -93,4 +93,19 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
   }
 }
 
+// Records for the merge which workgroups hold sequence b's first and last
+// pages (a single lane stores; the merge runs after this kernel ends).
+__device__ inline void note_segment(const DecodeArgs& a, int w, int b, long long p_lo,
+                                    long long p_hi, long long npages) {
+  if (threadIdx.x == 0) {
+    if (p_lo == 0) a.ws_idx[2 * b] = w;
+    if (p_hi == npages) a.ws_idx[2 * b + 1] = w;
+  }
+}
+
+// Workgroup 0 records the batch's page count (whether or not its range is empty).
+__device__ inline void note_total(const DecodeArgs& a, int w, long long ptot) {
+  if (w == 0 && threadIdx.x == 0) a.ws_idx[2 * a.batch] = (int32_t)ptot;
+}
+
 }  // namespace kvfp4
