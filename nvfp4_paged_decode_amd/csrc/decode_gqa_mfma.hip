@@ -95,8 +95,10 @@ constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
 struct StageLds {
   _Float16 v[kWaves][4][kTile][kPitch];  // per wave: 4 KV heads x 16 tokens
 };
+constexpr int kMergePitch = kD + 4;  // floats: rows 4 banks apart, so the
+                                     // 8 lanes of a 16-byte access hit distinct banks
 struct MergeLds {
-  float o[kWaves][16][kD];   // per wave: 16 query heads x 128 dims
+  float o[kWaves][16][kMergePitch];  // per wave: 16 query heads x 128 dims
   float ml[kWaves][16][2];   // running max and sum per query head
 };
 constexpr size_t kLdsBytes = sizeof(StageLds) > sizeof(MergeLds) ? sizeof(StageLds)
@@ -451,8 +453,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     __syncthreads();  // every wave is done with its staged V rows
 #pragma unroll
     for (int dt = 0; dt < kD / 16; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mg.o[wave][lr][16 * dt + 4 * lg + r] = acc[dt][r];
+      *reinterpret_cast<f32x4*>(&mg.o[wave][lr][16 * dt + 4 * lg]) = acc[dt];
     if (lg == 0) {
       mg.ml[wave][lr][0] = m;
       mg.ml[wave][lr][1] = l;
