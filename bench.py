@@ -53,6 +53,9 @@ def parse():
                    help="approximate host time budget of the oracle sample")
     p.add_argument("--no-copy-yardstick", action="store_true",
                    help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
+    p.add_argument("--extras-only", action="store_true",
+                   help="time only the paths reported beside the step (no step, no JSON "
+                        "metric line); for profiling those kernels on their own")
     p.add_argument("--no-append", action="store_true",
                    help="skip timing the token-row paths (append-quantize, gather-dequantize), "
                         "reported beside the step")
@@ -379,6 +382,27 @@ def main():
                     fn()
         return ev
 
+    def run_extras():
+        """The "next" paths, timed beside the step (never part of it)."""
+        ev = (lambda: None) if args.no_flush else evict
+        return {
+            "token_rows": time_append(K, torch, wl, geometry, gs, hot, packed, stream, ev,
+                                      args.steps, args.warmup),
+            "host_offload": time_offload(K, torch, wl, geometry, gs, hot, stream,
+                                         min(args.steps, 10), min(args.warmup, 2)),
+            "rope_layouts": time_rope_layouts(K, torch, wl, geometry, gs, hot, stream, ev,
+                                              min(args.steps, 10), min(args.warmup, 2)),
+        }
+
+    if args.extras_only:
+        if wl is None:
+            print("--extras-only needs a decode workload", file=sys.stderr)
+            sys.exit(2)
+        k_quant()  # the packed pool the gathers read
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "extras-only", "workload": name, **run_extras()}), flush=True)
+        return
+
     copy = None
     if not args.no_copy_yardstick:
         # a plain device-to-device copy of 1 GiB: reads 1 GiB and writes 1 GiB
@@ -452,21 +476,10 @@ def main():
     else:
         wdesc = f"cold_pages: {pages} pages x {geometry}; step = encode + decode of every page"
 
-    append = None
-    if wl is not None and not args.no_append:
-        append = time_append(K, torch, wl, geometry, gs, hot, packed, stream,
-                             (lambda: None) if args.no_flush else evict, args.steps, args.warmup)
-
-    offload = None
-    if wl is not None and not args.no_append:
-        offload = time_offload(K, torch, wl, geometry, gs, hot, stream, min(args.steps, 10),
-                               min(args.warmup, 2))
-
-    rope = None
-    if wl is not None and not args.no_append:
-        rope = time_rope_layouts(K, torch, wl, geometry, gs, hot, stream,
-                                 (lambda: None) if args.no_flush else evict,
-                                 min(args.steps, 10), min(args.warmup, 2))
+    extras = run_extras() if wl is not None and not args.no_append else {}
+    append = extras.get("token_rows")
+    offload = extras.get("host_offload")
+    rope = extras.get("rope_layouts")
 
     cpu = None
     if wl is not None and not args.no_cpu_baseline:
