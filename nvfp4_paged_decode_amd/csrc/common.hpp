@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kvfp4 {
 
 constexpr int kBlock = 16;  // values per NVFP4 block (one E4M3 scale each)
@@ -135,6 +137,21 @@ hipError_t launch_rope_decode(const Geom& g, int rope_dims, int mode, long long 
                               const void* packed, int packed_pages, const int32_t* src, void* hot,
                               int hot_pages, const int32_t* dst, int num_pages, const float* gs,
                               hipStream_t stream);
+
+// Raises a kernel's dynamic-LDS limit once per device (the setting is
+// idempotent; doing it once keeps it out of launches a caller may be
+// capturing into a graph).  `done` is that kernel's own device bitmask.
+inline hipError_t allow_lds_once(std::atomic<unsigned long long>& done, const void* kernel,
+                                 size_t bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct DecodeArgs {
   Geom g;

@@ -492,8 +492,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 
 template <int NKG>
 hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_mfma_kernel<NKG>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  static std::atomic<unsigned long long> lds_set{0};
+  hipError_t e = allow_lds_once(lds_set, (const void*)decode_gqa_mfma_kernel<NKG>, kLdsBytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_gqa_mfma_kernel<NKG>), dim3(a.nwg), dim3(64 * kWaves), kLdsBytes,
                      stream, a);

@@ -353,8 +353,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
 template <int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = sizeof(MlaLds);  // above the 64 KiB default: opt in
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mla_kernel<NW>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<unsigned long long> lds_set{0};
+  hipError_t e = allow_lds_once(lds_set, (const void*)decode_mla_kernel<NW>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_mla_kernel<NW>), dim3(a.nwg), dim3(64 * NW), lds, stream, a);
   return hipGetLastError();
