@@ -228,57 +228,130 @@ def time_rope_layouts(K, torch, wl, geometry, gs, hot, stream, evict, steps, war
     return res
 
 
-def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
-                 step_bytes: float) -> dict:
-    """The oracle as it stands, on one host thread, over a bounded sample of
-    the same workload: pages encoded, then decoded, in chunks of 16 until
-    each direction has used about a quarter of `budget_s`, then decode
-    attention for whole sequences (all query heads) until about half of it
-    is used.  Each leg's rate is scaled to that leg's bytes in one step, and
-    the figure is the step's algorithmic bytes over the summed time."""
-    from threadpoolctl import threadpool_limits
+def _oracle_encode(task):
+    """Pool worker: encode a chunk of hot pages with the oracle."""
+    from oracle import nvfp4 as O
+    hot, geometry, gs = task
+    g = O.Geometry(*geometry)
+    out = np.zeros((hot.shape[0], O.packed_page_bytes(g)), np.uint8)
+    O.quantize_pages(hot, g, hot.shape[0], gs, out)
+    return out
+
+
+def _oracle_decode(task):
+    """Pool worker: decode a chunk of packed pages with the oracle."""
+    from oracle import nvfp4 as O
+    packed, geometry, gs = task
+    g = O.Geometry(*geometry)
+    back = np.zeros((packed.shape[0], *g.row_shape), np.uint16)
+    O.dequantize_pages(packed, g, packed.shape[0], gs, back)
+    return back.shape[0]
+
+
+def _oracle_attend(task):
+    """Pool worker: decode attention of one sequence (all query heads)."""
     from oracle import nvfp4 as O
     from oracle import attention as A
+    packed, geometry, gs, q, L, scale, v_dim = task
+    g = O.Geometry(*geometry)
+    bt = np.arange(packed.shape[0], dtype=np.int32)[None, :]
+    A.decode_attention(packed, g, gs, q, bt, np.array([L], np.int32), scale, v_dim,
+                       batch_indices=[0])
+    return L
+
+
+def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
+                 step_bytes: float) -> dict:
+    """The oracle as it stands, on the host's cores, over a bounded sample of
+    the same workload.  A pool of processes (one per core the process may
+    use, at most 16, each with one BLAS thread) encodes chunks of 16 pages,
+    decodes them back, and runs decode attention for whole sequences (all
+    query heads); the sample sizes come from a short single-process timing
+    so that the three legs take about a quarter, a quarter and a half of
+    `budget_s` of wall time.  Each leg's rate is scaled to that leg's bytes
+    in one step, and the figure is the step's algorithmic bytes over the
+    summed time."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from oracle import nvfp4 as O
     g = O.Geometry(*wl.geometry)
     per_page = codec_bytes(wl.geometry, 1)
-    packed = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
     chunk = 16
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    used = wl.used_slots
+    n_chunks = used.shape[0] // chunk
+    seq_packed = {}
+
+    def enc_task(i):
+        return (wl.hot_pool[used[i * chunk:(i + 1) * chunk]], wl.geometry, gs)
+
+    def seq_pages(b):
+        need = -(-int(wl.seq_lens[b]) // wl.page_size)
+        return (wl.hot_pool[wl.block_table[b, :need]], wl.geometry, gs)
+
+    def att_task(b):
+        if b not in seq_packed:
+            seq_packed[b] = _oracle_encode(seq_pages(b))
+        return (seq_packed[b], wl.geometry, gs, wl.q[b:b + 1], int(wl.seq_lens[b]),
+                wl.softmax_scale, wl.v_dim)
+
+    # single-process timing of one task of each kind sizes the samples
     with threadpool_limits(limits=1):
-        n_q = 0
         t0 = time.perf_counter()
-        while n_q + chunk <= wl.used_slots.shape[0] and time.perf_counter() - t0 < budget_s / 4:
-            sl = wl.used_slots[n_q:n_q + chunk]
-            O.quantize_pages(wl.hot_pool, g, chunk, gs, packed, sl, sl)
-            n_q += chunk
-        q_s = time.perf_counter() - t0
-        back = np.zeros((chunk, *g.row_shape), np.uint16)
-        n_d = 0
+        packed0 = _oracle_encode(enc_task(0))
+        t_enc = time.perf_counter() - t0
         t0 = time.perf_counter()
-        while n_d + chunk <= n_q and time.perf_counter() - t0 < budget_s / 4:
-            O.dequantize_pages(packed, g, chunk, gs, back, wl.used_slots[n_d:n_d + chunk], None)
-            n_d += chunk
-        dq_s = time.perf_counter() - t0
-        # attention reads the pages of each sampled sequence, encoded first
-        # (untimed: that is the encode leg's work)
-        tokens, seqs, dec_s = 0, 0, 0.0
-        while seqs < wl.batch and dec_s < budget_s / 2:
-            need = -(-int(wl.seq_lens[seqs]) // wl.page_size)
-            bslots = wl.block_table[seqs, :need]
-            O.quantize_pages(wl.hot_pool, g, need, gs, packed, bslots, bslots)
+        _oracle_decode((packed0, wl.geometry, gs))
+        t_dec = time.perf_counter() - t0
+        task0 = att_task(0)
+        t0 = time.perf_counter()
+        _oracle_attend(task0)
+        t_att = time.perf_counter() - t0
+    n_enc = int(max(1, min(n_chunks, cores * round(budget_s / 4 / t_enc / cores + 0.5))))
+    n_att = int(max(1, min(wl.batch, cores * max(1, int(budget_s / 2 / t_att / cores)))))
+
+    env = dict(os.environ)
+    os.environ["OMP_NUM_THREADS"] = "1"  # the workers inherit one BLAS thread each
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores) as pool:
+            pool.map(_oracle_decode, [(packed0, wl.geometry, gs)] * cores)  # workers up
             t0 = time.perf_counter()
-            A.decode_attention(packed, g, gs, wl.q, wl.block_table, wl.seq_lens,
-                               wl.softmax_scale, wl.v_dim, batch_indices=[seqs])
-            dec_s += time.perf_counter() - t0
-            tokens += int(wl.seq_lens[seqs])
-            seqs += 1
+            packed = pool.map(_oracle_encode, [enc_task(i) for i in range(n_enc)])
+            q_s = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            pool.map(_oracle_decode, [(p, wl.geometry, gs) for p in packed])
+            dq_s = time.perf_counter() - t0
+            # the sampled sequences' pages, encoded first (untimed: that is
+            # the encode leg's work)
+            for b, pk in zip(range(1, n_att), pool.map(_oracle_encode,
+                                                       [seq_pages(b) for b in range(1, n_att)])):
+                seq_packed[b] = pk
+            tasks = [att_task(b) for b in range(n_att)]
+            t0 = time.perf_counter()
+            tokens = sum(pool.map(_oracle_attend, tasks))
+            dec_s = time.perf_counter() - t0
+    finally:
+        os.environ.clear()
+        os.environ.update(env)
+    n_q = n_enc * chunk
     t_step = (step_unit_bytes["quantize"] / (n_q * per_page)) * q_s + \
-             (step_unit_bytes["dequantize"] / (n_d * per_page)) * dq_s + \
+             (step_unit_bytes["dequantize"] / (n_q * per_page)) * dq_s + \
              (step_unit_bytes["decode"] / (tokens * dec_bytes_per_token)) * dec_s
-    return {"value": round(step_bytes / t_step / 1e9, 6), "unit": "GB/s", "cores": 1,
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(step_bytes / t_step / 1e9, 6), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"oracle (NumPy fp64) on 1 host thread: encode {n_q} pages ({q_s:.1f} s), "
-                       f"decode {n_d} pages ({dq_s:.1f} s), attention for {seqs} sequence(s) "
-                       f"({tokens} tokens, all {wl.num_q_heads} q heads, {dec_s:.1f} s); each leg "
+            "sample": (f"oracle (NumPy fp64) in {cores} processes, one thread each, on {cpu}: "
+                       f"encode {n_q} pages ({q_s:.1f} s), decode {n_q} pages ({dq_s:.1f} s), "
+                       f"attention for {n_att} sequence(s) ({tokens} tokens, all "
+                       f"{wl.num_q_heads} q heads, {dec_s:.1f} s) of wall time; each leg "
                        f"scaled to the step's bytes of that leg"),
             "seconds": round(q_s + dq_s + dec_s, 2)}
 

@@ -13,9 +13,12 @@
  * - Plain C ABI; pointers are device pointers unless marked HOST.
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *   default stream), never synchronizes, never allocates, and keeps no
- *   state between calls, so calls are thread-safe and re-entrant.  The
- *   caller owns every buffer; they must stay valid until the stream work
- *   has completed.  Input and output buffers must not overlap.
+ *   state between calls beyond two per-device caches (the CU count, and
+ *   whether a decode kernel's dynamic-LDS limit has been raised), so calls
+ *   are thread-safe and re-entrant, and after the first call on a device
+ *   they can be captured into a HIP graph.  The caller owns every buffer;
+ *   they must stay valid until the stream work has completed.  Input and
+ *   output buffers must not overlap.
  * - All arguments are validated on the host BEFORE anything is launched;
  *   on error nothing is launched and a negative status is returned, with
  *   a thread-local message in kvfp4_last_error_message().
