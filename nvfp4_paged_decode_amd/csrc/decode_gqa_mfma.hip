@@ -198,16 +198,24 @@ __device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long l
   p.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, KVFP4_GQA_AUX));
 }
 
-template <int NKG>
+// NKG groups of 4 KV heads (H = 4 NKG) and SUB subgroups of 4 query heads
+// per KV head (G = 4 SUB query heads per KV head): wave group gt = (kg, sub)
+// takes KV heads 4 kg .. 4 kg + 3 and, of each, query heads 4 sub .. +3.
+// The SUB groups of one kg read the same K/V rows; their tile walks are
+// staggered, so the later ones find the rows in L2.
+template <int NKG, int SUB>
 __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs a) {
-  constexpr int NS = kWaves / NKG;  // token streams per KV-head group
+  constexpr int NGT = NKG * SUB;    // wave groups
+  constexpr int NS = kWaves / NGT;  // token streams per wave group
+  constexpr int G = 4 * SUB;        // query heads per KV head
   extern __shared__ __align__(16) unsigned char smem[];
   StageLds& st = *reinterpret_cast<StageLds*>(smem);
   MergeLds& mg = *reinterpret_cast<MergeLds*>(smem);
   const Geom g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int kg = wave / NS, s = wave % NS;
+  const int gt = wave / NS, s = wave % NS;
+  const int kg = gt % NKG, sub = gt / NKG;
   const int lr = lane & 15, lg = lane >> 4;   // MFMA row/column, k-group
   const bool diag = (lr >> 2) == lg;          // column lr's KV head is group lg
   const int w = blockIdx.x, nwg = gridDim.x;
@@ -269,7 +277,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     const long long t_end = (L + kTile - 1) / kTile;
     if (t_hi > t_end) t_hi = t_end;
 
-    const int head = 16 * kg + lr;
+    // column lr: KV head 4 kg + lr / 4, its query head 4 sub + lr % 4
+    const int head = (4 * kg + (lr >> 2)) * G + 4 * sub + (lr & 3);
     f16x8 qb[16];   // queries: filled once the first tile is requested
     float qs = 0.f;
 
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     // instead of being missed by all of them at once.
     const long long first_t = t_lo + s;
     const int nk = first_t < t_hi ? (int)((t_hi - first_t + NS - 1) / NS) : 0;
-    const int rot = (KVFP4_GQA_ROT && nk > 0) ? kg % nk : 0;
+    const int rot = (KVFP4_GQA_ROT && nk > 0) ? gt % nk : 0;
     auto tile_at = [&](int k) -> long long {
       int kk = k + rot;
       if (kk >= nk) kk -= nk;
@@ -464,12 +473,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       constexpr int DW = kD / NS, DL = DW / 4;  // dims per wave, per lane
       float M = kNoMax;
 #pragma unroll
-      for (int u = 0; u < NS; ++u) M = fmaxf(M, mg.ml[kg * NS + u][lr][0]);
+      for (int u = 0; u < NS; ++u) M = fmaxf(M, mg.ml[gt * NS + u][lr][0]);
       float wt[NS], Ls = 0.f;
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
-        wt[u] = __builtin_amdgcn_exp2f(mg.ml[kg * NS + u][lr][0] - M);
-        Ls += wt[u] * mg.ml[kg * NS + u][lr][1];
+        wt[u] = __builtin_amdgcn_exp2f(mg.ml[gt * NS + u][lr][0] - M);
+        Ls += wt[u] * mg.ml[gt * NS + u][lr][1];
       }
       const long long slotp = ((long long)w + b) * a.hq + head;
       const int d0 = s * DW + lg * DL;
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NS; ++u)
-          o += *reinterpret_cast<const f32x4*>(&mg.o[kg * NS + u][lr][d0 + i]) * wt[u];
+          o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
         *reinterpret_cast<f32x4*>(a.ws_o + slotp * kD + d0 + i) = o;
       }
       if (s == 0 && lg == 0) {
@@ -490,12 +499,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   }
 }
 
-template <int NKG>
+template <int NKG, int SUB>
 hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
   static std::atomic<unsigned long long> lds_set{0};
-  hipError_t e = allow_lds_once(lds_set, (const void*)decode_gqa_mfma_kernel<NKG>, kLdsBytes);
+  hipError_t e = allow_lds_once(lds_set, (const void*)decode_gqa_mfma_kernel<NKG, SUB>,
+                                kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_gqa_mfma_kernel<NKG>), dim3(a.nwg), dim3(64 * kWaves), kLdsBytes,
+  hipLaunchKernelGGL((decode_gqa_mfma_kernel<NKG, SUB>), dim3(a.nwg), dim3(64 * kWaves), kLdsBytes,
                      stream, a);
   return hipGetLastError();
 }
@@ -506,17 +516,27 @@ bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
   if (g.nt != 2 || g.D != kD || v_dim != kD) return false;
   if (g.T % kTile != 0 || g.T > 4096) return false;
   if (!(g.H == 4 || g.H == 8 || g.H == 16 || g.H == 32)) return false;
-  return hq == 4 * g.H;
+  if (hq % g.H != 0) return false;
+  const int G = hq / g.H;
+  if (G != 4 && G != 8 && G != 16) return false;
+  return (g.H / 4) * (G / 4) <= kWaves;  // one wave group per (KV-head group, query subgroup)
 }
 
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (!gqa_mfma_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
   if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
-  switch (a.g.H) {
-    case 4: return launch_nkg<1>(a, stream);
-    case 8: return launch_nkg<2>(a, stream);
-    case 16: return launch_nkg<4>(a, stream);
-    default: return launch_nkg<8>(a, stream);
+  const int nkg = a.g.H / 4, sub = a.hq / a.g.H / 4;
+  switch (nkg * 16 + sub) {
+    case 1 * 16 + 1: return launch_nkg<1, 1>(a, stream);
+    case 2 * 16 + 1: return launch_nkg<2, 1>(a, stream);
+    case 4 * 16 + 1: return launch_nkg<4, 1>(a, stream);
+    case 8 * 16 + 1: return launch_nkg<8, 1>(a, stream);
+    case 1 * 16 + 2: return launch_nkg<1, 2>(a, stream);
+    case 2 * 16 + 2: return launch_nkg<2, 2>(a, stream);
+    case 4 * 16 + 2: return launch_nkg<4, 2>(a, stream);
+    case 1 * 16 + 4: return launch_nkg<1, 4>(a, stream);
+    case 2 * 16 + 4: return launch_nkg<2, 4>(a, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
