@@ -33,20 +33,18 @@ constexpr int kGenHeads = 16;   // query heads per workgroup
 constexpr int kGenTile = 8;     // tokens per LDS tile
 constexpr int kMaxD = 576;
 
-// Dequantized value c * sb of element d of a packed row (exact in fp32).
-__device__ inline float packed_elem(const uint8_t* data_row, const uint8_t* scale_row, int d) {
-  uint32_t byte = data_row[d >> 1];
-  uint32_t nib = (d & 1) ? (byte >> 4) : (byte & 0xF);
-  float v = e2m1_mag_to_float(nib & 7) * e4m3_to_float(scale_row[d >> 4]);
-  return (nib & 8) ? -v : v;
-}
-
 // Generic decode: one workgroup per (split, kv head x 16-query-head chunk,
 // sequence).  Thread (qh = tid / 16, r = tid % 16) keeps query head qh's
 // elements r, r+16, ... in registers and the matching accumulator slice.
 // Correct for every supported geometry (D <= 576); the shape-specialised
-// kernels are the fast paths.
+// kernels are the fast paths.  DMAX (64, 128, 256 or 576) bounds D so that
+// the per-thread loops run D / 16 steps, not 36.
+// Staging: a thread takes whole 16-value blocks of the tile (8 data bytes
+// and the scale byte in two loads) and writes their 16 exact values c * sb
+// to LDS in fp32.
+template <int DMAX>
 __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs a) {
+  constexpr int NI = DMAX / 16;
   const Geom g = a.g;
   const int split = blockIdx.x;
   const int b = blockIdx.z;
@@ -59,16 +57,17 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
   const int head = h * G + qc * kGenHeads + qh;  // query head of this thread
   const bool active = (qc * kGenHeads + qh) < G;
 
-  __shared__ float ks[kGenTile][kMaxD + 1];
-  __shared__ float vs[kGenTile][kMaxD + 1];
+  __shared__ float ks[kGenTile][DMAX + 1];
+  __shared__ float vs[kGenTile][DMAX + 1];
+  __shared__ int s_slot[kGenTile];
 
   const int D = g.D, Dv = a.v_dim;
-  const int nd = (D + 15) / 16, nv = (Dv + 15) / 16;
-  float qreg[kMaxD / 16];
-  float acc[kMaxD / 16];
+  const int nd = D / 16, nv = (Dv + 15) / 16;
+  float qreg[NI];
+  float acc[NI];
   const float qscale = a.softmax_scale * a.gs_k * kLog2e;
 #pragma unroll
-  for (int i = 0; i < kMaxD / 16; ++i) {
+  for (int i = 0; i < NI; ++i) {
     int d = r + 16 * i;
     float v = 0.f;
     if (active && i < nd && d < D)
@@ -86,33 +85,54 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
   int t_end = t_begin + a.pages_per_split * g.T;
   if (t_end > L) t_end = L;
 
-  const long long page_bytes = g.packed_bytes();
+  const long long page_bytes = g.packed_bytes(), data_bytes = g.data_bytes();
   const long long row_data = D / 2, row_scale = D / 16;
+  const int units = (g.nt == 2 ? 2 : 1) * kGenTile * nd;  // (tensor, token, block) units
   for (int t0 = t_begin; t0 < t_end; t0 += kGenTile) {
-    // dequantize the tile: K (tensor 0) and V (tensor 1, or the latent prefix)
-    __syncthreads();
-    for (int e = tid; e < kGenTile * D; e += kGenThreads) {
-      int tt = e / D, d = e - tt * D;
-      int tok = t0 + tt;
-      float kv = 0.f, vv = 0.f;
+    __syncthreads();  // the previous tile's reads are done
+    if (tid < kGenTile) {
+      const int tok = t0 + tid;
+      int slot = -1;
       if (tok < t_end) {
-        int slot = a.block_table[(long long)b * a.max_pages + tok / g.T];
-        if (slot >= 0 && slot < a.pool_pages) {
-          int row = tok % g.T;
-          const uint8_t* page = a.pool + (long long)slot * page_bytes;
-          long long r0 = (long long)row * g.H + h;  // row index within tensor 0
-          kv = packed_elem(page + r0 * row_data, page + g.data_bytes() + r0 * row_scale, d);
-          if (g.nt == 2) {
-            long long r1 = (long long)(g.T + row) * g.H + h;  // tensor 1
-            if (d < Dv)
-              vv = packed_elem(page + r1 * row_data, page + g.data_bytes() + r1 * row_scale, d);
-          } else {
-            vv = kv;
-          }
-        }
+        slot = a.block_table[(long long)b * a.max_pages + tok / g.T];
+        if (slot < 0 || slot >= a.pool_pages) slot = -1;
       }
-      ks[tt][d] = kv;
-      vs[tt][d] = vv;
+      s_slot[tid] = slot;
+    }
+    __syncthreads();
+    for (int u = tid; u < units; u += kGenThreads) {
+      const int tensor = u / (kGenTile * nd);
+      const int rem = u - tensor * kGenTile * nd;
+      const int tt = rem / nd, blk = rem - tt * nd;
+      const int slot = s_slot[tt];
+      float vals[16];
+      if (slot >= 0) {
+        const uint8_t* page = a.pool + (long long)slot * page_bytes;
+        const long long row = ((long long)tensor * g.T + (t0 + tt) % g.T) * g.H + h;
+        const uint8_t* dp = page + row * row_data + 8 * blk;
+        const uint32_t w0 = (uint32_t)dp[0] | ((uint32_t)dp[1] << 8) | ((uint32_t)dp[2] << 16) |
+                            ((uint32_t)dp[3] << 24);
+        const uint32_t w1 = (uint32_t)dp[4] | ((uint32_t)dp[5] << 8) | ((uint32_t)dp[6] << 16) |
+                            ((uint32_t)dp[7] << 24);
+        const float sb = e4m3_to_float(page[data_bytes + row * row_scale + blk]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t nib = ((e < 8 ? w0 : w1) >> (4 * (e & 7))) & 0xFu;
+          const float v = e2m1_mag_to_float(nib & 7u) * sb;
+          vals[e] = (nib & 8u) ? -v : v;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vals[e] = 0.f;
+      }
+      float* dst = tensor == 0 ? &ks[tt][16 * blk] : &vs[tt][16 * blk];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dst[e] = vals[e];
+      if (g.nt == 1) {  // MLA-style latent: the values are its prefix
+        float* vd = &vs[tt][16 * blk];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vd[e] = (16 * blk + e < Dv) ? vals[e] : 0.f;
+      }
     }
     __syncthreads();
     float s[kGenTile];
@@ -120,8 +140,8 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
     for (int tt = 0; tt < kGenTile; ++tt) {
       float p = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxD / 16; ++i)
-        if (i < nd && r + 16 * i < D) p += qreg[i] * ks[tt][r + 16 * i];
+      for (int i = 0; i < NI; ++i)
+        if (i < nd) p += qreg[i] * ks[tt][r + 16 * i];
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) p += __shfl_xor(p, off, 16);
       s[tt] = (t0 + tt < t_end) ? p : -INFINITY;
@@ -132,13 +152,13 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
     float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mt);
     l *= alpha;
 #pragma unroll
-    for (int i = 0; i < kMaxD / 16; ++i) acc[i] *= alpha;
+    for (int i = 0; i < NI; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int tt = 0; tt < kGenTile; ++tt) {
       float p = (s[tt] == -INFINITY) ? 0.f : exp2f(s[tt] - mt);
       l += p;
 #pragma unroll
-      for (int i = 0; i < kMaxD / 16; ++i)
+      for (int i = 0; i < NI; ++i)
         if (i < nv && r + 16 * i < Dv) acc[i] += p * vs[tt][r + 16 * i];
     }
     m = mt;
@@ -146,7 +166,7 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
   if (!active) return;
   long long base = (((long long)b * a.hq + head) * a.splits + split);
 #pragma unroll
-  for (int i = 0; i < kMaxD / 16; ++i) {
+  for (int i = 0; i < NI; ++i) {
     int d = r + 16 * i;
     if (i < nv && d < Dv) a.ws_o[base * Dv + d] = acc[i];
   }
@@ -366,7 +386,7 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
   p.kernel = 0;
   int G = hq / g.H;
   long long items = (long long)batch * g.H * ((G + kGenHeads - 1) / kGenHeads);
-  long long want = 2LL * cus;
+  long long want = 8LL * cus;  // the split loop is latency-bound: many workgroups per CU
   long long s = (want + items - 1) / items;
   if (s < 1) s = 1;
   if (s > pages_max) s = pages_max;
@@ -389,8 +409,16 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   } else {
     int G = a.hq / a.g.H;
     int nqc = (G + kGenHeads - 1) / kGenHeads;
-    hipLaunchKernelGGL(decode_generic_kernel, dim3(a.splits, a.g.H * nqc, a.batch),
-                       dim3(kGenThreads), 0, stream, a);
+    const dim3 grid(a.splits, a.g.H * nqc, a.batch);
+    const int dmax = a.g.D > a.v_dim ? a.g.D : a.v_dim;
+    if (dmax <= 64)
+      hipLaunchKernelGGL(decode_generic_kernel<64>, grid, dim3(kGenThreads), 0, stream, a);
+    else if (dmax <= 128)
+      hipLaunchKernelGGL(decode_generic_kernel<128>, grid, dim3(kGenThreads), 0, stream, a);
+    else if (dmax <= 256)
+      hipLaunchKernelGGL(decode_generic_kernel<256>, grid, dim3(kGenThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_generic_kernel<kMaxD>, grid, dim3(kGenThreads), 0, stream, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
