@@ -1,0 +1,43 @@
+"""Host-side checks of bench.py: the algorithmic byte counts behind its
+GB/s figures, and the one-GPU contract (no GPU needed)."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from nvfp4_paged_decode_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_codec_and_append_bytes():
+    # 4096 Llama-3-8B-shaped pages: 1 GiB of bf16 in, 9/16 of the values' count out
+    e = 2 * 64 * 8 * 128
+    assert bench.codec_bytes((2, 64, 8, 128), 4096) == 4096 * (2 * e + e * 9 // 16)
+    assert bench.codec_bytes((2, 64, 8, 128), 4096) == 1375731712
+    # a token: 2048 values as bf16 rows, their 1152 packed bytes, 8 bytes of slot and row
+    assert bench.append_bytes((2, 64, 8, 128), 1, 2) == 4096 + 1152 + 8
+    assert bench.append_bytes((2, 64, 8, 128), 10, 1) == 10 * (2048 + 1152 + 8)
+
+
+def test_decode_bytes_follow_the_definition():
+    wl = W.llama3_8b(seed=3, batch=2, context=200)
+    db = bench.decode_bytes(wl)
+    L = wl.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * 2 * 8 * 128 * 9 // 16
+    q = 2 * 32 * 128 * 2
+    out = 2 * 32 * 128 * 2 + 2 * 32 * 4
+    bt = int(np.sum(-(-L // 64))) * 4 + 2 * 4
+    assert db["bytes"] == kv + q + out + bt
+    assert db["kv_bytes"] == kv
+    assert db["flops"] == 2 * int(L.sum()) * 32 * (128 + 128)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
