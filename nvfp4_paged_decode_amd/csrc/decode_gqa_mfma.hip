@@ -300,8 +300,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
     };
 
-    // One tile of the stream: V rows to LDS, scores, softmax, P.V.
-    auto compute = [&](const Packed& cur, int n_cur) {
+    // One tile of the stream, in two phases: (a) V rows to LDS and the
+    // scores -- after which the tile's registers are free -- and (b)
+    // softmax and P.V from LDS.
+    auto phase_a = [&](const Packed& cur) -> f32x4 {
       // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 2)
       {
         f16x2 vsc[4];
@@ -332,8 +334,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
             sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka1, qb[ks + 1], sc0, 0, 0, 0);
         }
       }
-      const f32x4 sc = sc0 + sc1;
-
+      return sc0 + sc1;
+    };
+    auto phase_b = [&](const f32x4 sc, int n_cur) {
       // online softmax of column lr over rows 4 lg + r
       float sv[4];
       float mx = kNoMax;
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     load_queries();
     for (int k = 0; k < nk; ++k) {
       if (k + 1 < nk) issue(nxt, n_nxt, tile_at(k + 1));
-      compute(cur, n_cur);
+      phase_b(phase_a(cur), n_cur);
       cur = nxt;
       n_cur = n_nxt;
     }
