@@ -1,5 +1,5 @@
-// Paged NVFP4 decode attention for query groups of 4 (head_dim 128, 4 to 32
-// KV heads, pages a multiple of 16 tokens) on MFMA.
+// Paged NVFP4 decode attention for query groups of 4, 8 or 16 (head_dim 64
+// or 128, 4 to 32 KV heads, pages a multiple of 16 tokens) on MFMA.
 //
 // "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
 // NVFP4 KV Decode Attention Kernel Implementation / Figure 3: packed K/V
@@ -31,7 +31,7 @@
 //
 // Per 16-token tile of a wave (4 KV heads):
 //   scores   S^T = K Q^T: A = K, lane (token t, KV head g) dequantizes its
-//            own 64-byte row, 8 values per k-step; B = Q^T block-diagonal
+//            own row (head_dim / 2 bytes), 8 values per k-step; B = Q^T block-diagonal
 //            (lane (column c, group g) holds query c's 8 values when g is
 //            c's KV head, else 0), kept in registers per sequence.  Lane
 //            (c, g) receives rows 4g..4g+3 of column c.
@@ -64,12 +64,13 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;       // head dim
 constexpr int kTile = 16;     // tokens per tile
 constexpr int kWaves = 8;     // waves per workgroup
-constexpr int kPitch = kD + 16;  // fp16 per staged V row: 72 dwords (8 banks
-                                 // mod 32), so the 16 lanes of a transposed
-                                 // read hit distinct banks
+// fp16 per staged V row for head dim KD: KD/2 + 8 dwords, which is 8 banks
+// mod 32 for KD = 64 and 128, so the 16 lanes of a transposed read hit
+// distinct banks
+template <int KD>
+constexpr int pitch_of() { return KD + 16; }
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
@@ -92,23 +93,31 @@ constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
 #define KVFP4_GQA_AUX 0
 #endif
 
+template <int KD>
 struct StageLds {
-  _Float16 v[kWaves][4][kTile][kPitch];  // per wave: 4 KV heads x 16 tokens
+  _Float16 v[kWaves][4][kTile][pitch_of<KD>()];  // per wave: 4 KV heads x 16 tokens
 };
-constexpr int kMergePitch = kD + 4;  // floats: rows 4 banks apart, so the
-                                     // 8 lanes of a 16-byte access hit distinct banks
+// floats per merge row: rows 4 banks apart, so the 8 lanes of a 16-byte
+// access hit distinct banks
+template <int KD>
+constexpr int merge_pitch_of() { return KD + 4; }
+template <int KD>
 struct MergeLds {
-  float o[kWaves][16][kMergePitch];  // per wave: 16 query heads x 128 dims
+  float o[kWaves][16][merge_pitch_of<KD>()];  // per wave: 16 query heads x KD dims
   float ml[kWaves][16][2];   // running max and sum per query head
 };
-constexpr size_t kLdsBytes = sizeof(StageLds) > sizeof(MergeLds) ? sizeof(StageLds)
-                                                                  : sizeof(MergeLds);
+template <int KD>
+constexpr size_t lds_bytes() {
+  return sizeof(StageLds<KD>) > sizeof(MergeLds<KD>) ? sizeof(StageLds<KD>)
+                                                     : sizeof(MergeLds<KD>);
+}
 
-// One lane's packed share of a tile: its 64-byte K row and V row and
-// their 8 scale bytes each.
+// One lane's packed share of a tile: its K row and V row (KD/2 bytes each)
+// and their KD/16 scale bytes each.
+template <int KD>
 struct Packed {
-  u32x4 k[4], v[4];
-  u32x2 ks, vs;
+  u32x4 k[KD / 32], v[KD / 32];
+  uint32_t ks[KD / 64], vs[KD / 64];
 };
 
 __device__ inline f16x2 fp4x2(uint32_t w, int sel) {
@@ -120,12 +129,14 @@ __device__ inline f16x2 fp4x2(uint32_t w, int sel) {
   }
 }
 
-// The 8 block scales of a row (E4M3 bytes) as fp16 pairs (exact).
-__device__ inline void scales8(u32x2 s, f16x2 (&o)[4]) {
-  o[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.x, 1.0f, false);
-  o[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.x, 1.0f, true);
-  o[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.y, 1.0f, false);
-  o[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.y, 1.0f, true);
+// The KD/16 block scales of a row (E4M3 bytes) as fp16 pairs (exact).
+template <int KD>
+__device__ inline void scales_row(const uint32_t (&s)[KD / 64], f16x2 (&o)[KD / 32]) {
+#pragma unroll
+  for (int i = 0; i < KD / 64; ++i) {
+    o[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[i], 1.0f, false);
+    o[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[i], 1.0f, true);
+  }
 }
 
 // 8 values of dword w (dims 8i..8i+7 of a row) times their block scale.
@@ -136,7 +147,8 @@ __device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
   return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-__device__ inline _Float16 block_scale(const f16x2 (&s)[4], int blk) {
+template <int N>
+__device__ inline _Float16 block_scale(const f16x2 (&s)[N], int blk) {
   return (blk & 1) ? s[blk >> 1].y : s[blk >> 1].x;
 }
 
@@ -177,9 +189,10 @@ __device__ inline int tile_rows(const TileGeom& tg, int slot, long long ti) {
   return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
 }
 
-__device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long long ti, int n) {
+template <int KD>
+__device__ inline void load_tile(Packed<KD>& p, const TileGeom& tg, int slot, long long ti, int n) {
   const int row0 = (int)(ti % tg.tiles_per_page) * kTile;
-  const int rowb = tg.H * (kD / 2), rows = tg.H * (kD / 16);
+  const int rowb = tg.H * (KD / 2), rows = tg.H * (KD / 16);
   const uint8_t* page = tg.pool + (long long)(n > 0 ? slot : 0) * tg.page_bytes;
   const uint8_t* kd = page + (long long)row0 * rowb;
   const uint8_t* vd = page + (long long)tg.T * rowb + (long long)row0 * rowb;
@@ -190,12 +203,21 @@ __device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long l
   auto rks = __builtin_amdgcn_make_buffer_rsrc((void*)kss, (short)0, n * rows, 0x00020000);
   auto rvs = __builtin_amdgcn_make_buffer_rsrc((void*)vss, (short)0, n * rows, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < KD / 32; ++j) {
     p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
     p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
   }
-  p.ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, KVFP4_GQA_AUX));
-  p.vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, KVFP4_GQA_AUX));
+  if constexpr (KD == 128) {
+    const u32x2 ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, KVFP4_GQA_AUX));
+    const u32x2 vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, KVFP4_GQA_AUX));
+    p.ks[0] = ks.x;
+    p.ks[1] = ks.y;
+    p.vs[0] = vs.x;
+    p.vs[1] = vs.y;
+  } else {
+    p.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, tg.off_scale, 0, KVFP4_GQA_AUX);
+    p.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rvs, tg.off_scale, 0, KVFP4_GQA_AUX);
+  }
 }
 
 // NKG groups of 4 KV heads (H = 4 NKG) and SUB subgroups of 4 query heads
@@ -203,14 +225,17 @@ __device__ inline void load_tile(Packed& p, const TileGeom& tg, int slot, long l
 // takes KV heads 4 kg .. 4 kg + 3 and, of each, query heads 4 sub .. +3.
 // The SUB groups of one kg read the same K/V rows; their tile walks are
 // staggered, so the later ones find the rows in L2.
-template <int NKG, int SUB>
+template <int KD, int NKG, int SUB>
 __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs a) {
+  static_assert(KD == 64 || KD == 128, "head dim 64 or 128");
+  using Packed = ::kvfp4::Packed<KD>;
   constexpr int NGT = NKG * SUB;    // wave groups
   constexpr int NS = kWaves / NGT;  // token streams per wave group
   constexpr int G = 4 * SUB;        // query heads per KV head
+  constexpr int kPitch = pitch_of<KD>();
   extern __shared__ __align__(16) unsigned char smem[];
-  StageLds& st = *reinterpret_cast<StageLds*>(smem);
-  MergeLds& mg = *reinterpret_cast<MergeLds*>(smem);
+  StageLds<KD>& st = *reinterpret_cast<StageLds<KD>*>(smem);
+  MergeLds<KD>& mg = *reinterpret_cast<MergeLds<KD>*>(smem);
   const Geom g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -228,8 +253,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   tg.T = g.T;
   tg.H = g.H;
   tg.tiles_per_page = g.T / kTile;
-  tg.off_data = (uint32_t)((lr * g.H + 4 * kg + lg) * (kD / 2));
-  tg.off_scale = (uint32_t)((lr * g.H + 4 * kg + lg) * (kD / 16));
+  tg.off_data = (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 2));
+  tg.off_scale = (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 16));
 
   // transposed-read addresses: lane (q = (lane&15)>>2, j = lane&3) of
   // k-group lg points at row 4x + q, dims 4j.. of KV head lg
@@ -279,12 +304,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 
     // column lr: KV head 4 kg + lr / 4, its query head 4 sub + lr % 4
     const int head = (4 * kg + (lr >> 2)) * G + 4 * sub + (lr & 3);
-    f16x8 qb[16];   // queries: filled once the first tile is requested
+    f16x8 qb[KD / 8];   // queries: filled once the first tile is requested
     float qs = 0.f;
 
-    f32x4 acc[kD / 16];
+    f32x4 acc[KD / 16];
 #pragma unroll
-    for (int dt = 0; dt < kD / 16; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < KD / 16; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m = kNoMax, l = 0.f;
 
     // page-table entries of pages c0 .. c0+63, one per lane
@@ -306,12 +331,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     auto phase_a = [&](const Packed& cur) -> f32x4 {
       // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 2)
       {
-        f16x2 vsc[4];
-        scales8(cur.vs, vsc);
+        f16x2 vsc[KD / 32];
+        scales_row<KD>(cur.vs, vsc);
         _Float16* dst = vw + lr * kPitch;
         const int sw = KVFP4_GQA_SWZ ? (lr >> 2) & 1 : 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < KD / 32; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             *reinterpret_cast<f16x8*>(dst + 8 * ((4 * j + e) ^ sw)) =
@@ -321,10 +346,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       // scores S^T[token][column], two independent accumulation chains
       f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
       {
-        f16x2 ksc[4];
-        scales8(cur.ks, ksc);
+        f16x2 ksc[KD / 32];
+        scales_row<KD>(cur.ks, ksc);
 #pragma unroll
-        for (int ks = 0; ks < 16; ks += 2) {
+        for (int ks = 0; ks < KD / 8; ks += 2) {
           const f16x8 ka0 = dequant8(cur.k[ks >> 2][ks & 3], block_scale(ksc, ks >> 1));
           sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka0, qb[ks], sc0, 0, 0, 0);
           const f16x8 ka1 = dequant8(cur.k[ks >> 2][(ks & 3) + 1], block_scale(ksc, ks >> 1));
@@ -352,7 +377,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         l *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < kD / 16; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < KD / 16; ++dt) acc[dt] *= alpha;
         m = mn;
       }
       float p[4];
@@ -380,7 +405,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int dt = 0; dt < kD / 16; ++dt) {
+        for (int dt = 0; dt < KD / 16; ++dt) {
           const f16x4 lo = lds_read_tr(tr_base[mm][0] + 16 * dt);
           const f16x4 hi = lds_read_tr(tr_base[mm][1] + 16 * dt);
           const f16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -404,13 +429,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     // of two that puts it in [2^14, 2^15); lanes off the diagonal scale by
     // 2^-200, which makes their operand exactly 0
     auto load_queries = [&]() {
-      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * kD;
-      u32x4 raw[kD / 8];
+      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * KD;
+      u32x4 raw[KD / 8];
       uint32_t mb = 0;
 #pragma unroll
-      for (int i = 0; i < kD / 8; ++i) raw[i] = load_q8(qrow, i);
+      for (int i = 0; i < KD / 8; ++i) raw[i] = load_q8(qrow, i);
 #pragma unroll
-      for (int i = 0; i < kD / 8; ++i)
+      for (int i = 0; i < KD / 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           mb = max(mb, raw[i][e] & 0x7FFFu);
@@ -424,7 +449,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       }
       const int shq = diag ? sh : -200;
 #pragma unroll
-      for (int i = 0; i < kD / 8; ++i)
+      for (int i = 0; i < KD / 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[i][e] << 16), shq);
@@ -464,7 +489,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     l += __shfl_xor(l, 32);
     __syncthreads();  // every wave is done with its staged V rows
 #pragma unroll
-    for (int dt = 0; dt < kD / 16; ++dt)
+    for (int dt = 0; dt < KD / 16; ++dt)
       *reinterpret_cast<f32x4*>(&mg.o[wave][lr][16 * dt + 4 * lg]) = acc[dt];
     if (lg == 0) {
       mg.ml[wave][lr][0] = m;
@@ -472,8 +497,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     }
     __syncthreads();
     {
-      // wave (kg, s) finishes dims [s * 128/NS, (s+1) * 128/NS) of its group
-      constexpr int DW = kD / NS, DL = DW / 4;  // dims per wave, per lane
+      // wave (kg, s) finishes dims [s * KD/NS, (s+1) * KD/NS) of its group
+      constexpr int DW = KD / NS, DL = DW / 4;  // dims per wave, per lane
       float M = kNoMax;
 #pragma unroll
       for (int u = 0; u < NS; ++u) M = fmaxf(M, mg.ml[gt * NS + u][lr][0]);
@@ -485,13 +510,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       }
       const long long slotp = ((long long)w + b) * a.hq + head;
       const int d0 = s * DW + lg * DL;
+      if constexpr (DL % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < DL; i += 4) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < DL; i += 4) {
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NS; ++u)
-          o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
-        *reinterpret_cast<f32x4*>(a.ws_o + slotp * kD + d0 + i) = o;
+          for (int u = 0; u < NS; ++u)
+            o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
+          *reinterpret_cast<f32x4*>(a.ws_o + slotp * KD + d0 + i) = o;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DL; ++i) {
+          float o = 0.f;
+#pragma unroll
+          for (int u = 0; u < NS; ++u) o += mg.o[gt * NS + u][lr][d0 + i] * wt[u];
+          a.ws_o[slotp * KD + d0 + i] = o;
+        }
       }
       if (s == 0 && lg == 0) {
         a.ws_ml[slotp * 2] = M;
@@ -502,21 +537,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   }
 }
 
-template <int NKG, int SUB>
+template <int KD, int NKG, int SUB>
 hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
   static std::atomic<unsigned long long> lds_set{0};
-  hipError_t e = allow_lds_once(lds_set, (const void*)decode_gqa_mfma_kernel<NKG, SUB>,
-                                kLdsBytes);
+  constexpr size_t bytes = lds_bytes<KD>();
+  hipError_t e = allow_lds_once(lds_set, (const void*)decode_gqa_mfma_kernel<KD, NKG, SUB>, bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_gqa_mfma_kernel<NKG, SUB>), dim3(a.nwg), dim3(64 * kWaves), kLdsBytes,
+  hipLaunchKernelGGL((decode_gqa_mfma_kernel<KD, NKG, SUB>), dim3(a.nwg), dim3(64 * kWaves), bytes,
                      stream, a);
   return hipGetLastError();
+}
+
+template <int KD>
+hipError_t launch_kd(const DecodeArgs& a, hipStream_t stream) {
+  const int nkg = a.g.H / 4, sub = a.hq / a.g.H / 4;
+  switch (nkg * 16 + sub) {
+    case 1 * 16 + 1: return launch_nkg<KD, 1, 1>(a, stream);
+    case 2 * 16 + 1: return launch_nkg<KD, 2, 1>(a, stream);
+    case 4 * 16 + 1: return launch_nkg<KD, 4, 1>(a, stream);
+    case 8 * 16 + 1: return launch_nkg<KD, 8, 1>(a, stream);
+    case 1 * 16 + 2: return launch_nkg<KD, 1, 2>(a, stream);
+    case 2 * 16 + 2: return launch_nkg<KD, 2, 2>(a, stream);
+    case 4 * 16 + 2: return launch_nkg<KD, 4, 2>(a, stream);
+    case 1 * 16 + 4: return launch_nkg<KD, 1, 4>(a, stream);
+    case 2 * 16 + 4: return launch_nkg<KD, 2, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
-  if (g.nt != 2 || g.D != kD || v_dim != kD) return false;
+  if (g.nt != 2 || !(g.D == 64 || g.D == 128) || v_dim != g.D) return false;
   if (g.T % kTile != 0 || g.T > 4096) return false;
   if (!(g.H == 4 || g.H == 8 || g.H == 16 || g.H == 32)) return false;
   if (hq % g.H != 0) return false;
@@ -528,19 +580,7 @@ bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (!gqa_mfma_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
   if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
-  const int nkg = a.g.H / 4, sub = a.hq / a.g.H / 4;
-  switch (nkg * 16 + sub) {
-    case 1 * 16 + 1: return launch_nkg<1, 1>(a, stream);
-    case 2 * 16 + 1: return launch_nkg<2, 1>(a, stream);
-    case 4 * 16 + 1: return launch_nkg<4, 1>(a, stream);
-    case 8 * 16 + 1: return launch_nkg<8, 1>(a, stream);
-    case 1 * 16 + 2: return launch_nkg<1, 2>(a, stream);
-    case 2 * 16 + 2: return launch_nkg<2, 2>(a, stream);
-    case 4 * 16 + 2: return launch_nkg<4, 2>(a, stream);
-    case 1 * 16 + 4: return launch_nkg<1, 4>(a, stream);
-    case 2 * 16 + 4: return launch_nkg<2, 4>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return a.g.D == 64 ? launch_kd<64>(a, stream) : launch_kd<128>(a, stream);
 }
 
 }  // namespace kvfp4

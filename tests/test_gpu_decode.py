@@ -99,6 +99,10 @@ GEOMETRIES = {
     "mfma_gqa_G8_H16_T16": (2, 16, 16, 128, 128, 128),
     "mfma_gqa_G16_H4_T16": (2, 16, 4, 128, 64, 128),
     "mfma_gqa_G16_H8_T64": (2, 64, 8, 128, 128, 128),
+    "mfma_gqa_D64_T16_H4": (2, 16, 4, 64, 16, 64),
+    "mfma_gqa_D64_G8_H8_T32": (2, 32, 8, 64, 64, 64),
+    "mfma_gqa_D64_G16_H8_T64": (2, 64, 8, 64, 128, 64),
+    "mfma_gqa_D64_T128_H32": (2, 128, 32, 64, 128, 64),
     "generic_G16_H16": (2, 16, 16, 128, 256, 128),  # 16 wave groups: past the MFMA kernel
     "valu_gqa_G1_H8": (2, 64, 8, 128, 8, 128),
     "valu_gqa_G2_H2": (2, 32, 2, 128, 4, 128),
