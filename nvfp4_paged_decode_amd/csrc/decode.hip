@@ -212,6 +212,11 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
 }
 
 constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
+// Threads of the balanced merge: 256 when a partial row is at most 128
+// columns (8 groups of 32 threads request 64 slots per round, so a sequence
+// split over up to 64 workgroups is merged after one round of partial
+// loads), else 128 (wide rows: one group; more threads measured slower).
+constexpr int kBalMergeWide = 128, kBalMergeNarrow = 256;
 
 // Merge for the balanced kernels: sequence b's partials sit in slots w + b
 // for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
@@ -223,7 +228,7 @@ constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
 // kMergeBatch of them per round of loads, and the groups combine through
 // LDS.  VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte aligned
 // out): a thread owns 4 columns; otherwise one column per thread, G = 1.
-template <bool VEC, int K4>
+template <bool VEC, int K4, int kMergeThreads>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
   static_assert(!VEC || K4 * 4 * kMergeThreads >= 512, "v_dim up to 512");
   const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -428,8 +433,15 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
     const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_o & 15) == 0 &&
                      ((uintptr_t)a.out & 7) == 0;
     // the balanced kernels have v_dim <= 512: one f32x4 column block a thread
-    auto kernel = vec ? merge_balanced_kernel<true, 1> : merge_balanced_kernel<false, 1>;
-    hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
+    if (a.v_dim <= 128) {
+      auto kernel = vec ? merge_balanced_kernel<true, 1, kBalMergeNarrow>
+                        : merge_balanced_kernel<false, 1, kBalMergeNarrow>;
+      hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeNarrow), 0, stream, a);
+    } else {
+      auto kernel = vec ? merge_balanced_kernel<true, 1, kBalMergeWide>
+                        : merge_balanced_kernel<false, 1, kBalMergeWide>;
+      hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeWide), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }
