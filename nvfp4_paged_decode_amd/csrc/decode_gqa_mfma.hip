@@ -432,8 +432,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * KD;
       u32x4 raw[KD / 8];
       uint32_t mb = 0;
+      // only the diagonal lane of a column uses its row (the others hold
+      // zeros), so only it loads: a quarter of the requests
 #pragma unroll
-      for (int i = 0; i < KD / 8; ++i) raw[i] = load_q8(qrow, i);
+      for (int i = 0; i < KD / 8; ++i) raw[i] = (u32x4){0u, 0u, 0u, 0u};
+      if (diag) {
+#pragma unroll
+        for (int i = 0; i < KD / 8; ++i) raw[i] = load_q8(qrow, i);
+      }
 #pragma unroll
       for (int i = 0; i < KD / 8; ++i)
 #pragma unroll
