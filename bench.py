@@ -90,6 +90,51 @@ def append_bytes(geometry, tokens: int, elem_bytes: int) -> int:
     return tokens * (per * elem_bytes + per * 9 // 16 + 8)
 
 
+# Each leg's traffic mix, for reading its bandwidth against a plain stream of
+# the same mix: decode reads (the merge's few writes aside); the encoder reads
+# 32 bytes of bf16 for every 9 it writes, the decoder the reverse.
+LEG_MIX = {"decode": "read", "quantize": "read4_write1", "dequantize": "read1_write4"}
+YARDSTICK_KINDS = {"read": (0, 1.0), "write": (1, 1.0), "read4_write1": (2, 1.25),
+                   "read1_write4": (3, 1.25)}
+
+
+def stream_yardsticks(torch, src, dst, stream, evict, calls=COPY_CALLS):
+    """Plain streams of 1 GiB per traffic mix (libkvfp4_yardstick.so), timed
+    like the legs: cache eviction before each call, median after the first.
+    GB/s counts both directions (read 1 GiB + write 256 MiB for read4_write1)."""
+    import ctypes
+    lib_path = os.path.join(ROOT, "nvfp4_paged_decode_amd", "libkvfp4_yardstick.so")
+    if not os.path.exists(lib_path):
+        return None
+    lib = ctypes.CDLL(lib_path)
+    lib.kvfp4_yardstick.restype = ctypes.c_int
+    lib.kvfp4_yardstick.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    sink = torch.empty(1024, dtype=torch.uint8, device=src.device)
+    nbytes = src.numel()
+    out = {}
+    for name, (kind, factor) in YARDSTICK_KINDS.items():
+        times = []
+        for _ in range(calls):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.kvfp4_yardstick(kind, src.data_ptr(), dst.data_ptr(), sink.data_ptr(), nbytes,
+                                     ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"kvfp4_yardstick({name}) failed: {rc}")
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
+        moved = factor * nbytes
+        out[name] = {"bytes": int(moved), "median_us": round(ms * 1e3, 2),
+                     "GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, warmup):
     """The token-row paths, timed beside the step (not part of it).  Write
     path: a prefill of up to 256 of the workload's pages appended token by
@@ -478,6 +523,7 @@ def main():
         return
 
     copy = None
+    mixes = None
     if not args.no_copy_yardstick:
         # a plain device-to-device copy of 1 GiB: reads 1 GiB and writes 1 GiB
         src_c = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -495,6 +541,7 @@ def main():
         ms_c = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
         copy = {"bytes": 2 * COPY_BYTES, "median_us": round(ms_c * 1e3, 2),
                 "GB/s": round(2 * COPY_BYTES / (ms_c * 1e-3) / 1e9, 1)}
+        mixes = stream_yardsticks(torch, src_c, dst_c, stream, evict)
         del src_c, dst_c
 
     run(args.warmup, False)
@@ -539,6 +586,8 @@ def main():
                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         if copy is not None:
             kern[k]["frac_copy_yardstick"] = round(gbs / copy["GB/s"], 4)
+        if mixes and LEG_MIX[k] in mixes:
+            kern[k]["frac_mix_yardstick"] = round(gbs / mixes[LEG_MIX[k]]["GB/s"], 4)
         if k in warm:
             kern[k]["warm_avg_us_no_eviction"] = round(warm[k] * 1e3, 2)
     if wl is not None:
@@ -598,6 +647,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kern,
         "copy_yardstick": copy,
+        "stream_yardsticks": mixes,
         "token_rows": append,
         "host_offload": offload,
         "rope_layouts": rope,

@@ -1,8 +1,10 @@
-"""Build libkvfp4.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libkvfp4.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree,
+and libkvfp4_yardstick.so (the benchmark's streaming yardsticks, no part of
+the library's interface).
 
     python -m nvfp4_paged_decode_amd.build
 
-Every build recompiles from source.  The library lands next to this file.
+Every build recompiles from source.  The libraries land next to this file.
 """
 
 from __future__ import annotations
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvfp4.so")
+YARDSTICK_LIB = os.path.join(PKG, "libkvfp4_yardstick.so")
 
 SOURCES = ["api.hip", "codec.hip", "decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip",
            "decode_mla.hip", "rope.hip"]
@@ -39,9 +42,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvfp4)")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources, out: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -52,8 +55,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _compile(["yardstick.hip"], YARDSTICK_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

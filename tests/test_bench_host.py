@@ -41,3 +41,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_every_leg_has_a_mix_yardstick():
+    """Each timed leg is read against a stream of its own traffic mix, and
+    the mixes' byte factors match the directions they move (1 GiB on the
+    reference side, a quarter of it on the other)."""
+    assert set(bench.LEG_MIX) == {"decode", "quantize", "dequantize"}
+    for leg, mix in bench.LEG_MIX.items():
+        assert mix in bench.YARDSTICK_KINDS, (leg, mix)
+    kinds = sorted(k for k, _ in bench.YARDSTICK_KINDS.values())
+    assert kinds == [0, 1, 2, 3]
+    assert bench.YARDSTICK_KINDS["read"][1] == 1.0
+    assert bench.YARDSTICK_KINDS["read4_write1"][1] == 1.25
+    assert bench.YARDSTICK_KINDS["read1_write4"][1] == 1.25
