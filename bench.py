@@ -360,7 +360,8 @@ def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_t
     os.environ["OMP_NUM_THREADS"] = "1"  # the workers inherit one BLAS thread each
     try:
         ctx = mp.get_context("spawn")
-        with ctx.Pool(cores) as pool:
+        pool = ctx.Pool(cores)
+        try:
             pool.map(_oracle_decode, [(packed0, wl.geometry, gs)] * cores)  # workers up
             t0 = time.perf_counter()
             packed = pool.map(_oracle_encode, [enc_task(i) for i in range(n_enc)])
@@ -377,6 +378,11 @@ def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_t
             t0 = time.perf_counter()
             tokens = sum(pool.map(_oracle_attend, tasks))
             dec_s = time.perf_counter() - t0
+        finally:
+            # the workers finish and exit on their own (no SIGTERM, which a
+            # preloaded profiler's signal handler in the children can stall)
+            pool.close()
+            pool.join()
     finally:
         os.environ.clear()
         os.environ.update(env)
