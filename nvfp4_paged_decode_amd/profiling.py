@@ -59,7 +59,7 @@ def source_digest(leg: str | None = None) -> str:
 
 
 def short_name(name: str) -> str:
-    n = re.sub(r"kvfp4::\(anonymous namespace\)::", "", name)
+    n = re.sub(r"(kvfp4::)?\(anonymous namespace\)::", "", name)
     n = n.replace("void ", "")
     if "copyBuffer" in n:
         return "copyBuffer"

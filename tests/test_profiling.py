@@ -53,3 +53,11 @@ def test_leg_digests_cover_their_sources():
             assert os.path.exists(os.path.join(P.CSRC, n)), (leg, n)
     assert P.source_digest("decode") != P.source_digest("quantize")
     assert P.source_digest("quantize") == P.source_digest("dequantize")
+
+
+def test_names_outside_the_library_namespace_are_kept():
+    """The benchmark's stream yardsticks live in an anonymous namespace of
+    their own: they keep their names and belong to no leg."""
+    n = P.short_name("void (anonymous namespace)::read4_write1_kernel<8>(unsigned int const*)")
+    assert n == "read4_write1_kernel<8>"
+    assert P.leg_of(n) is None
