@@ -129,6 +129,34 @@ def test_decode_geometries(name):
     check(wl, gs, packed, out, lse, what=name)
 
 
+# (nt, T, H, D, Hq, v_dim) for the balanced kernels
+MANY = {
+    "mfma_gqa_D128": (2, 64, 8, 128, 32, 128),
+    "mfma_gqa_D64": (2, 16, 8, 64, 32, 64),
+    "mla_128_heads": (1, 64, 1, 576, 128, 512),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY))
+def test_decode_more_sequences_than_workgroups(name):
+    """300 short sequences (about a tenth of them empty) over at most 256
+    workgroups: a workgroup then walks several whole sequences one after
+    another, the page-range scan covers the batch in 64-lane chunks, and
+    empty sequences sit between the others."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = MANY[name]
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 3 * T, 300)
+    lens[rng.random(300) < 0.1] = 0
+    wl = W.geometry_case(90 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=name)
+    empty = np.asarray(lens) == 0
+    assert np.all(out[empty] == 0) and np.all(lse[empty] == -np.inf)
+
+
 def test_decode_unaligned_output():
     """An output buffer that is only 2-byte aligned takes the merge's
     one-column-per-thread path; results are the same."""
