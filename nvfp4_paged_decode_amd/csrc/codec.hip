@@ -591,13 +591,21 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   }
 }
 
-int grid_for(int num_pages) {
-  // one workgroup per page: with fewer workgroups than pages some take two
-  // pages and the rest wait for them (4800 pages over 4096 workgroups cost
-  // 23% more time than over 4800); past the cap each walks a contiguous run
-  // of pages, and the runs differ by at most one page
-  const int cap = KVFP4_CODEC_GRID;
-  return num_pages < cap ? num_pages : cap;
+int grid_for(const Geom& g, int num_pages, long long target_bytes) {
+  // A workgroup takes at most ppw whole pages, ppw = the pages in about
+  // target_bytes of bf16: fewer workgroups than that would leave some with
+  // one page more while the rest wait for them (4800 Llama-3-8B-shaped
+  // pages over 4096 workgroups took 23% longer than over 4800), more would
+  // repeat each workgroup's table build over little data.  Measured: the
+  // encoder wants about 320 KiB (MLA pages one a workgroup encoded 6%
+  // slower than four), the decoder, whose table is cheaper, one page up to
+  // 96 KiB (MLA pages four a workgroup decoded 3% slower than one).  Past
+  // the cap the runs grow, still differing by at most one page.
+  long long ppw = target_bytes / g.hot_bytes();
+  if (ppw < 1) ppw = 1;
+  long long grid = ((long long)num_pages + ppw - 1) / ppw;
+  const long long cap = KVFP4_CODEC_GRID;
+  return (int)(grid < cap ? grid : cap);
 }
 
 }  // namespace
@@ -607,7 +615,7 @@ hipError_t launch_quantize(const Geom& g, const void* hot, int hot_pages, const 
                            const float* gs, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
   float gs1 = g.nt > 1 ? gs[1] : gs[0];
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(g, num_pages, 320LL << 10)), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)hot, hot_pages, src, (uint8_t*)packed, packed_pages, dst,
                      num_pages, gs[0], gs1);
   return hipGetLastError();
@@ -636,7 +644,7 @@ hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages
                              int num_pages, const float* gs, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
   float gs1 = g.nt > 1 ? gs[1] : gs[0];
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(num_pages)), dim3(kThreads), 0, stream, g,
+  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(g, num_pages, 96LL << 10)), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
                      num_pages, gs[0], gs1);
   return hipGetLastError();
