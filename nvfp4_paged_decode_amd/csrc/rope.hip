@@ -222,7 +222,10 @@ __global__ __launch_bounds__(kThreads) void rope_decode_kernel(
   }
 }
 
-int rope_grid(int num_pages) { return num_pages < 4096 ? num_pages : 4096; }
+// One workgroup per page (no per-workgroup table to amortize); with fewer
+// workgroups than pages some would take one page more while the rest wait.
+// Past the cap each walks a contiguous run, the runs differing by at most one.
+int rope_grid(int num_pages) { return num_pages < 65536 ? num_pages : 65536; }
 
 }  // namespace
 
