@@ -1,5 +1,7 @@
-// Paged NVFP4 decode attention for query groups of 4, 8 or 16 (head_dim 64
-// or 128, 4 to 32 KV heads, pages a multiple of 16 tokens) on MFMA.
+// Paged NVFP4 decode attention on MFMA for 1 to 16 query heads per KV head
+// (padded to 4, 8 or 16 query columns: the padding columns hold zero
+// queries and are never written), head_dim 64 or 128, 4 to 32 KV heads,
+// pages a multiple of 16 tokens.
 //
 // "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
 // NVFP4 KV Decode Attention Kernel Implementation / Figure 3: packed K/V
@@ -231,7 +233,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   using Packed = ::kvfp4::Packed<KD>;
   constexpr int NGT = NKG * SUB;    // wave groups
   constexpr int NS = kWaves / NGT;  // token streams per wave group
-  constexpr int G = 4 * SUB;        // query heads per KV head
+  // query heads per KV head: up to 4 SUB; columns past it are padding
+  // (zero queries, nothing written)
+  const int G = a.hq / a.g.H;
   constexpr int kPitch = pitch_of<KD>();
   extern __shared__ __align__(16) unsigned char smem[];
   StageLds<KD>& st = *reinterpret_cast<StageLds<KD>*>(smem);
@@ -303,7 +307,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     if (t_hi > t_end) t_hi = t_end;
 
     // column lr: KV head 4 kg + lr / 4, its query head 4 sub + lr % 4
-    const int head = (4 * kg + (lr >> 2)) * G + 4 * sub + (lr & 3);
+    const int q_of_kv = 4 * sub + (lr & 3);
+    const bool col_ok = q_of_kv < G;
+    const int head = (4 * kg + (lr >> 2)) * G + (col_ok ? q_of_kv : 0);
     f16x8 qb[KD / 8];   // queries: filled once the first tile is requested
     float qs = 0.f;
 
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       // zeros), so only it loads: a quarter of the requests
 #pragma unroll
       for (int i = 0; i < KD / 8; ++i) raw[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (diag) {
+      if (diag && col_ok) {
 #pragma unroll
         for (int i = 0; i < KD / 8; ++i) raw[i] = load_q8(qrow, i);
       }
@@ -516,27 +522,29 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       }
       const long long slotp = ((long long)w + b) * a.hq + head;
       const int d0 = s * DW + lg * DL;
-      if constexpr (DL % 4 == 0) {
+      if (col_ok) {
+        if constexpr (DL % 4 == 0) {
 #pragma unroll
-        for (int i = 0; i < DL; i += 4) {
-          f32x4 o = {0.f, 0.f, 0.f, 0.f};
+          for (int i = 0; i < DL; i += 4) {
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < NS; ++u)
-            o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
-          *reinterpret_cast<f32x4*>(a.ws_o + slotp * KD + d0 + i) = o;
+            for (int u = 0; u < NS; ++u)
+              o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
+            *reinterpret_cast<f32x4*>(a.ws_o + slotp * KD + d0 + i) = o;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < DL; ++i) {
+            float o = 0.f;
+#pragma unroll
+            for (int u = 0; u < NS; ++u) o += mg.o[gt * NS + u][lr][d0 + i] * wt[u];
+            a.ws_o[slotp * KD + d0 + i] = o;
+          }
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < DL; ++i) {
-          float o = 0.f;
-#pragma unroll
-          for (int u = 0; u < NS; ++u) o += mg.o[gt * NS + u][lr][d0 + i] * wt[u];
-          a.ws_o[slotp * KD + d0 + i] = o;
+        if (s == 0 && lg == 0) {
+          a.ws_ml[slotp * 2] = M;
+          a.ws_ml[slotp * 2 + 1] = Ls;
         }
-      }
-      if (s == 0 && lg == 0) {
-        a.ws_ml[slotp * 2] = M;
-        a.ws_ml[slotp * 2 + 1] = Ls;
       }
     }
     __syncthreads();  // the merge area is staged V rows again next segment
@@ -554,9 +562,13 @@ hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Query subgroups of 4 per KV head for G query heads per KV head (G <= 16):
+// the wave groups of a workgroup are (H/4) x subgroups, 1, 2, 4 or 8 of them.
+int gqa_subgroups(int G) { return G <= 4 ? 1 : G <= 8 ? 2 : 4; }
+
 template <int KD>
 hipError_t launch_kd(const DecodeArgs& a, hipStream_t stream) {
-  const int nkg = a.g.H / 4, sub = a.hq / a.g.H / 4;
+  const int nkg = a.g.H / 4, sub = gqa_subgroups(a.hq / a.g.H);
   switch (nkg * 16 + sub) {
     case 1 * 16 + 1: return launch_nkg<KD, 1, 1>(a, stream);
     case 2 * 16 + 1: return launch_nkg<KD, 2, 1>(a, stream);
@@ -579,8 +591,9 @@ bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
   if (!(g.H == 4 || g.H == 8 || g.H == 16 || g.H == 32)) return false;
   if (hq % g.H != 0) return false;
   const int G = hq / g.H;
-  if (G != 4 && G != 8 && G != 16) return false;
-  return (g.H / 4) * (G / 4) <= kWaves;  // one wave group per (KV-head group, query subgroup)
+  if (G < 1 || G > 16) return false;
+  // one wave group per (KV-head group, query subgroup)
+  return (g.H / 4) * gqa_subgroups(G) <= kWaves;
 }
 
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {

@@ -104,7 +104,14 @@ GEOMETRIES = {
     "mfma_gqa_D64_G16_H8_T64": (2, 64, 8, 64, 128, 64),
     "mfma_gqa_D64_T128_H32": (2, 128, 32, 64, 128, 64),
     "generic_G16_H16": (2, 16, 16, 128, 256, 128),  # 16 wave groups: past the MFMA kernel
-    "valu_gqa_G1_H8": (2, 64, 8, 128, 8, 128),
+    "mfma_gqa_G1_H8": (2, 64, 8, 128, 8, 128),      # padded query columns: 1 of 4 used
+    "mfma_gqa_G2_H16": (2, 32, 16, 128, 32, 128),
+    "mfma_gqa_G3_H32_D64": (2, 16, 32, 64, 96, 64),
+    "mfma_gqa_G5_H8": (2, 64, 8, 128, 40, 128),       # 5 of 8 columns
+    "mfma_gqa_G7_H4": (2, 16, 4, 128, 28, 128),       # 28 q / 4 KV heads
+    "mfma_gqa_G10_H8": (2, 16, 8, 128, 80, 128),      # 10 of 16 columns
+    "mfma_gqa_G12_H4": (2, 16, 4, 128, 48, 128),
+    "valu_gqa_G1_H2": (2, 32, 2, 128, 2, 128),
     "valu_gqa_G2_H2": (2, 32, 2, 128, 4, 128),
     "valu_gqa_G4_H2": (2, 16, 2, 128, 8, 128),
     "generic_G3_D64_T8": (2, 8, 2, 64, 6, 64),
