@@ -1,7 +1,8 @@
 // Paged NVFP4 decode attention on MFMA for 1 to 16 query heads per KV head
 // (padded to 4, 8 or 16 query columns: the padding columns hold zero
-// queries and are never written), head_dim 64 or 128, 4 to 32 KV heads,
-// pages a multiple of 16 tokens.
+// queries and are never written) and 1 to 32 KV heads (padded to a multiple
+// of 4: the padding slots load zeros and fetch nothing), head_dim 64 or
+// 128, pages a multiple of 16 tokens.
 //
 // "Accelerating Long-Context and Agentic Inference with NVFP4 KV Cache",
 // NVFP4 KV Decode Attention Kernel Implementation / Figure 3: packed K/V
@@ -74,6 +75,7 @@ constexpr int kWaves = 8;     // waves per workgroup
 template <int KD>
 constexpr int pitch_of() { return KD + 16; }
 constexpr float kNoMax = -1e30f;
+constexpr uint32_t kPastRange = 0x40000000u;  // buffer offset past every tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
                                // maximum exceeds it by more than this (log2
@@ -257,8 +259,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   tg.T = g.T;
   tg.H = g.H;
   tg.tiles_per_page = g.T / kTile;
-  tg.off_data = (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 2));
-  tg.off_scale = (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 16));
+  // KV-head slots past H (H not a multiple of 4 here) read past the
+  // buffer's range: their rows load as zeros and fetch nothing
+  const bool kv_ok = 4 * kg + lg < g.H;
+  tg.off_data = kv_ok ? (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 2)) : kPastRange;
+  tg.off_scale = kv_ok ? (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 16)) : kPastRange;
 
   // transposed-read addresses: lane (q = (lane&15)>>2, j = lane&3) of
   // k-group lg points at row 4x + q, dims 4j.. of KV head lg
@@ -308,8 +313,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 
     // column lr: KV head 4 kg + lr / 4, its query head 4 sub + lr % 4
     const int q_of_kv = 4 * sub + (lr & 3);
-    const bool col_ok = q_of_kv < G;
-    const int head = (4 * kg + (lr >> 2)) * G + (col_ok ? q_of_kv : 0);
+    const int kv_of_col = 4 * kg + (lr >> 2);
+    const bool col_ok = q_of_kv < G && kv_of_col < g.H;
+    const int head = col_ok ? kv_of_col * G + q_of_kv : 0;
     f16x8 qb[KD / 8];   // queries: filled once the first tile is requested
     float qs = 0.f;
 
@@ -562,13 +568,15 @@ hipError_t launch_nkg(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Query subgroups of 4 per KV head for G query heads per KV head (G <= 16):
-// the wave groups of a workgroup are (H/4) x subgroups, 1, 2, 4 or 8 of them.
+// Query subgroups of 4 per KV head for G query heads per KV head (G <= 16),
+// and groups of 4 KV heads for H KV heads (H <= 32; slots past H are
+// padding): the wave groups of a workgroup are their product, 1, 2, 4 or 8.
 int gqa_subgroups(int G) { return G <= 4 ? 1 : G <= 8 ? 2 : 4; }
+int gqa_kv_groups(int H) { return H <= 4 ? 1 : H <= 8 ? 2 : H <= 16 ? 4 : 8; }
 
 template <int KD>
 hipError_t launch_kd(const DecodeArgs& a, hipStream_t stream) {
-  const int nkg = a.g.H / 4, sub = gqa_subgroups(a.hq / a.g.H);
+  const int nkg = gqa_kv_groups(a.g.H), sub = gqa_subgroups(a.hq / a.g.H);
   switch (nkg * 16 + sub) {
     case 1 * 16 + 1: return launch_nkg<KD, 1, 1>(a, stream);
     case 2 * 16 + 1: return launch_nkg<KD, 2, 1>(a, stream);
@@ -585,15 +593,19 @@ hipError_t launch_kd(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool gqa_supported(const Geom& g, int hq, int v_dim);
+
 bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
   if (g.nt != 2 || !(g.D == 64 || g.D == 128) || v_dim != g.D) return false;
   if (g.T % kTile != 0 || g.T > 4096) return false;
-  if (!(g.H == 4 || g.H == 8 || g.H == 16 || g.H == 32)) return false;
+  if (g.H < 1 || g.H > 32) return false;
   if (hq % g.H != 0) return false;
   const int G = hq / g.H;
   if (G < 1 || G > 16) return false;
+  // fewer than 4 KV heads: the shapes the VALU kernel takes stay there
+  if (g.H < 4 && gqa_supported(g, hq, v_dim)) return false;
   // one wave group per (KV-head group, query subgroup)
-  return (g.H / 4) * gqa_subgroups(G) <= kWaves;
+  return gqa_kv_groups(g.H) * gqa_subgroups(G) <= kWaves;
 }
 
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {

@@ -111,6 +111,12 @@ GEOMETRIES = {
     "mfma_gqa_G7_H4": (2, 16, 4, 128, 28, 128),       # 28 q / 4 KV heads
     "mfma_gqa_G10_H8": (2, 16, 8, 128, 80, 128),      # 10 of 16 columns
     "mfma_gqa_G12_H4": (2, 16, 4, 128, 48, 128),
+    "mfma_gqa_H2_G8": (2, 16, 2, 128, 16, 128),       # KV-head slots padded to 4
+    "mfma_gqa_H2_G6_D64": (2, 32, 2, 64, 12, 64),
+    "mfma_gqa_H3_G7": (2, 16, 3, 128, 21, 128),
+    "mfma_gqa_H1_G16": (2, 16, 1, 128, 16, 128),
+    "mfma_gqa_H6_G2": (2, 64, 6, 128, 12, 128),
+    "mfma_gqa_H10_G4": (2, 16, 10, 128, 40, 128),     # 16 slots, 10 KV heads
     "valu_gqa_G1_H2": (2, 32, 2, 128, 2, 128),
     "valu_gqa_G2_H2": (2, 32, 2, 128, 4, 128),
     "valu_gqa_G4_H2": (2, 16, 2, 128, 8, 128),
