@@ -49,8 +49,9 @@
 //            + 1, mod 4, m = 0, 1), whose probabilities sit in lanes
 //            (c, x), (c, y) and are fetched with ds_bpermute.
 //
-// Workgroup: 8 waves = (H/4 groups of 4 KV heads) x (8/(H/4) token
-// streams); stream s takes tiles s, s + NS, ... of each sequence segment.
+// Workgroup: 8 waves = NGT wave groups (groups of 4 KV-head slots x query
+// subgroups of 4) x NS = 8 / NGT token streams; stream s takes tiles s,
+// s + NS, ... of each sequence segment.
 // The balanced split of decode_plan.hpp gives each workgroup a contiguous
 // range of the batch's pages; at the end of each sequence segment the
 // streams are merged through LDS and the partial goes to workspace slot
