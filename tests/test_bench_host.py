@@ -55,3 +55,26 @@ def test_every_leg_has_a_mix_yardstick():
     assert bench.YARDSTICK_KINDS["read"][1] == 1.0
     assert bench.YARDSTICK_KINDS["read4_write1"][1] == 1.25
     assert bench.YARDSTICK_KINDS["read1_write4"][1] == 1.25
+
+
+def test_yardstick_library_rejects_bad_arguments_before_launching():
+    """libkvfp4_yardstick.so loads without a GPU and refuses sizes that are
+    not whole sweeps, unaligned pointers and unknown kinds on the host
+    (hipErrorInvalidValue, 1) before any HIP call."""
+    import ctypes
+    path = os.path.join(os.path.dirname(bench.__file__), "nvfp4_paged_decode_amd",
+                        "libkvfp4_yardstick.so")
+    if not os.path.exists(path):
+        import pytest
+        pytest.skip("libkvfp4_yardstick.so is not built")
+    lib = ctypes.CDLL(path)
+    f = lib.kvfp4_yardstick
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    whole = 1 << 30
+    assert f(0, 16, 16, 16, 0, None) == 1                 # empty
+    assert f(0, 16, 16, 16, whole + 16, None) == 1        # not a whole sweep
+    assert f(1, 16, 8, 16, whole, None) == 1              # unaligned destination
+    assert f(7, 16, 16, 16, whole, None) == 1             # unknown kind
+    assert f(0, None, 16, 16, whole, None) == 1           # read stream without a source
