@@ -645,7 +645,7 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16<->nvfp4 codec (integer thresholds), fp32 attention",
+        "dtype": "bf16<->nvfp4 codec (integer thresholds); attention fp16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded)",
         "config": {"workload": wdesc, "global_scale": args.gs, "cache_flush_between_kernels":
                    "none" if args.no_flush else args.flush_mode + " 1 GiB", "global_batch": wl.batch if wl is not None else None,
