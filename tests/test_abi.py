@@ -267,3 +267,32 @@ def test_rope_codec_needs_16_byte_slots(lib):
     # the plain codec takes the same geometry
     assert lib.kvfp4_quantize_pages(ctypes.byref(g), None, 0, None, None, 0, None, 0, arr,
                                     None) == K.KVFP4_OK
+
+
+@pytest.mark.parametrize("geom,hq,balanced", [
+    ((2, 64, 8, 128), 32, True),      # 4 query heads per KV head
+    ((2, 64, 8, 128), 8, True),       # one query head per KV head: padded columns
+    ((2, 64, 4, 128), 28, True),      # 7 per KV head
+    ((2, 16, 2, 128), 16, True),      # 2 KV heads: padded KV-head slots
+    ((2, 16, 10, 128), 40, True),     # 10 KV heads
+    ((1, 64, 1, 576), 128, True),     # MLA
+    ((2, 16, 16, 128), 256, False),   # 16 x 16: more wave groups than a workgroup has
+    ((2, 64, 4, 256), 16, False),     # head_dim 256
+])
+def test_decode_routing_by_workspace(lib, geom, hq, balanced):
+    """The workspace size tells which plan a shape gets: the balanced
+    kernels hold (workgroups + batch) partial rows and the merge index, the
+    generic kernel batch x heads x splits rows.  Without a GPU the plan
+    assumes 256 compute units."""
+    g = K.Geometry(*geom)
+    batch, hint = 4, 1024
+    v = 512 if geom[0] == 1 else geom[3]
+    n = lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), batch, hq, v, hint)
+    row = hq * (v + 2) * 4
+    index = -(-(2 * batch + 1) * 4 // 16) * 16
+    pages = batch * -(-hint // geom[1])
+    balanced_bytes = (min(256, pages) + batch) * row + index
+    if balanced:
+        assert n == balanced_bytes
+    else:
+        assert n != balanced_bytes and n % row == 0
