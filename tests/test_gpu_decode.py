@@ -142,6 +142,31 @@ def test_decode_geometries(name):
     check(wl, gs, packed, out, lse, what=name)
 
 
+# (nt, T, H, D, Hq, v_dim): the largest page the MFMA and MLA kernels take
+# (4096 tokens: 256 sixteen-token tiles, 128 MLA tiles), and the generic
+# kernel at the same page size
+LARGEST_PAGE = {
+    "mfma_gqa_T4096_H4": (2, 4096, 4, 128, 16, 128),
+    "mfma_gqa_D64_T4096_H8": (2, 4096, 8, 64, 64, 64),
+    "mla_T4096": (1, 4096, 1, 576, 128, 512),
+    "generic_D256_T4096": (2, 4096, 1, 256, 4, 256),
+}
+
+
+@pytest.mark.parametrize("name", list(LARGEST_PAGE))
+def test_decode_largest_page(name):
+    """One token, a partial first tile, exactly one page, one page and a few
+    tokens, and a partial page, at 4096 tokens a page."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = LARGEST_PAGE[name]
+    lens = [1, 17, T, T + 5, 300]
+    wl = W.geometry_case(60 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=name)
+
+
 # (nt, T, H, D, Hq, v_dim) for the balanced kernels
 MANY = {
     "mfma_gqa_D128": (2, 64, 8, 128, 32, 128),
