@@ -195,6 +195,35 @@ def test_decode_more_sequences_than_workgroups(name):
     assert np.all(out[empty] == 0) and np.all(lse[empty] == -np.inf)
 
 
+NO_LSE = {
+    "valu_tiny": lambda: W.tiny(seed=21),
+    "mfma_gqa": lambda: W.llama3_8b(seed=22, batch=3, context=300),
+    "mla": lambda: W.mla(seed=23, batch=2, context=150),
+    "generic_D256": lambda: W.geometry_case(24, nt=2, T=64, H=1, D=256, Hq=4, v_dim=256,
+                                            lens=[0, 1, 70, 200]),
+}
+
+
+@pytest.mark.parametrize("name", list(NO_LSE))
+def test_decode_without_lse(name):
+    """lse is optional: without it the outputs are bit-identical to a call
+    that writes it (empty sequences included)."""
+    require_gpu()
+    wl = NO_LSE[name]()
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out_ref, _ = gpu_decode(wl, dev(packed), gs)
+    B, Hq = wl.batch, wl.num_q_heads
+    hint = int(wl.seq_lens.max())
+    ws_bytes = K.kvfp4_decode_workspace_bytes(wl.geometry, B, Hq, wl.v_dim, hint)
+    ws = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hq, wl.v_dim), 0x7FC0, dtype=torch.int16, device="cuda")
+    K.kvfp4_paged_decode_attention(wl.geometry, dev(packed), gs, dev(wl.q.view(np.int16)),
+                                   dev(wl.block_table), dev(wl.seq_lens), hint,
+                                   wl.softmax_scale, out, None, ws, v_dim=wl.v_dim)
+    assert np.array_equal(host(out).view(np.uint16), out_ref), name
+
+
 def test_decode_unaligned_output():
     """An output buffer that is only 2-byte aligned takes the merge's
     one-column-per-thread path; results are the same."""
