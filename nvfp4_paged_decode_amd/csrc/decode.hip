@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
         if (i < nd) p += qreg[i] * ks[tt][r + 16 * i];
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) p += __shfl_xor(p, off, 16);
-      s[tt] = (t0 + tt < t_end) ? p : -INFINITY;
+      // tokens past the sequence and tokens of an out-of-range page take no
+      // part in the softmax
+      s[tt] = (t0 + tt < t_end && s_slot[tt] >= 0) ? p : -INFINITY;
     }
     float mt = m;
 #pragma unroll

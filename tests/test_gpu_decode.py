@@ -224,6 +224,46 @@ def test_decode_without_lse(name):
     assert np.array_equal(host(out).view(np.uint16), out_ref), name
 
 
+BAD_PAGES = {  # (nt, T, H, D, Hq, v_dim), one per decode kernel
+    "valu_gqa": (2, 16, 2, 128, 4, 128),
+    "mfma_gqa": (2, 64, 8, 128, 32, 128),
+    "mla": (1, 64, 1, 576, 128, 512),
+    "generic_D256": (2, 64, 1, 256, 4, 256),
+}
+
+
+@pytest.mark.parametrize("name", list(BAD_PAGES))
+def test_decode_out_of_range_pages_contribute_nothing(name):
+    """Page-table entries outside [0, pool pages) make their page's tokens
+    take no part: the result equals the oracle on the same sequences with
+    those pages left out (a middle page, a first page, a one-token last
+    page, and a sequence's only page, which leaves it empty)."""
+    require_gpu()
+    import dataclasses
+    nt, T, H, D, Hq, v_dim = BAD_PAGES[name]
+    lens = [3 * T + 5, 2 * T, 4 * T + 1, T, 2 * T + 3]
+    wl = W.geometry_case(110 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    bt_bad = wl.block_table.copy()
+    bt_ref = wl.block_table.copy()
+    lens_ref = wl.seq_lens.copy()
+    # (sequence, page, bad id); the reference drops that page from the row
+    for b, pg, bad in [(0, 1, -1), (1, 0, wl.num_slots), (2, 4, 1 << 30), (3, 0, -5)]:
+        n_pages = -(-int(wl.seq_lens[b]) // T)
+        bt_bad[b, pg] = bad
+        row = [int(s) for j, s in enumerate(wl.block_table[b, :n_pages]) if j != pg]
+        bt_ref[b, :len(row)] = row
+        rows_on_page = min(T, int(wl.seq_lens[b]) - pg * T)
+        lens_ref[b] -= rows_on_page
+    assert list(lens_ref[:4]) == [2 * T + 5, T, 4 * T, 0]
+    wl_bad = dataclasses.replace(wl, block_table=bt_bad)
+    wl_ref = dataclasses.replace(wl, block_table=bt_ref, seq_lens=lens_ref)
+    out, lse = gpu_decode(wl_bad, dev(packed), gs)
+    check(wl_ref, gs, packed, out, lse, what=f"{name} out-of-range pages")
+    assert np.all(out[3] == 0) and np.all(lse[3] == -np.inf)
+
+
 def test_decode_unaligned_output():
     """An output buffer that is only 2-byte aligned takes the merge's
     one-column-per-thread path; results are the same."""
