@@ -264,6 +264,28 @@ def test_decode_out_of_range_pages_contribute_nothing(name):
     assert np.all(out[3] == 0) and np.all(lse[3] == -np.inf)
 
 
+@pytest.mark.parametrize("name", list(BAD_PAGES))
+def test_decode_out_of_range_lengths_are_clamped(name):
+    """A negative length reads as 0 (out = 0, lse = -inf); a length past
+    max_pages_per_seq * T reads as that bound.  The pool is encoded without
+    poisoned rows, so the clamped sequence's last page is data throughout."""
+    require_gpu()
+    import dataclasses
+    nt, T, H, D, Hq, v_dim = BAD_PAGES[name]
+    lens = [3 * T + 5, 2 * T, 4 * T + 1, 40]
+    wl = W.geometry_case(130 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_packed_pages(wl.hot_pool, wl.geometry, gs, np.arange(wl.num_slots))
+    cap = wl.block_table.shape[1] * T
+    assert cap == 5 * T  # sequence 2 uses every entry of its page-table row
+    lens_bad = np.array([-3, 2 * T, cap + 100, 40], np.int32)
+    lens_ref = np.array([0, 2 * T, cap, 40], np.int32)
+    out, lse = gpu_decode(wl, dev(packed), gs, hint=cap + 100, seq_lens=lens_bad)
+    check(dataclasses.replace(wl, seq_lens=lens_ref), gs, packed, out, lse,
+          what=f"{name} clamped lengths")
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+
+
 def test_decode_unaligned_output():
     """An output buffer that is only 2-byte aligned takes the merge's
     one-column-per-thread path; results are the same."""
