@@ -311,7 +311,8 @@ def _valid_pool(rng, g, n_slots, gs):
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp8"])
 def test_gather_bit_exact(geometry, num_tokens, out_dtype):
     """Gathered rows match the oracle bit for bit, bf16 and FP8, including
-    tokens with a bad slot or row (zero rows) and repeated tokens."""
+    tokens with a bad slot (negative or past the pool) or row (zero rows)
+    and repeated tokens."""
     require_gpu()
     g = O.Geometry(*geometry)
     rng = np.random.default_rng(num_tokens + (7 if out_dtype == "fp8" else 0))
@@ -321,6 +322,7 @@ def test_gather_bit_exact(geometry, num_tokens, out_dtype):
     slots = rng.integers(0, n_slots, num_tokens).astype(np.int32)
     page_rows = rng.integers(0, g.page_size, num_tokens).astype(np.int32)
     slots[::17] = -1
+    slots[3::23] = n_slots  # one past the pool
     page_rows[5::19] = g.page_size
     ref = O.gather_dequantize(pool, g, gs, slots, page_rows, out_dtype)
     dt = torch.int16 if out_dtype == "bf16" else torch.uint8
