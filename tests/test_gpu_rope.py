@@ -43,23 +43,29 @@ def test_rope_layouts_bit_exact(geometry, rope_dims, mode):
     n = 3
     gs = [float(np.float32(0.0173)), float(np.float32(2.5))][:g.num_kv_tensors]
     hot = _pages(rng, g, n, gs)
-    src = np.array([2, 0, 1], np.int32)
-    dst = np.array([1, 3, 0], np.int32)
+    # two more pages that must be skipped: a negative source slot, and a
+    # destination one past the pool; the reference encodes the valid three
+    src = np.array([2, 0, 1, -1, 1], np.int32)
+    dst = np.array([1, 3, 0, 2, 4], np.int32)
     pb = RP.packed_page_bytes(g, rope)
     assert K.kvfp4_packed_page_bytes_rope(geometry, (rope_dims, mode)) == pb
     ref = np.zeros((4, pb), np.uint8)
-    RP.quantize_pages(hot, g, rope, n, gs, ref, src, dst)
+    RP.quantize_pages(hot, g, rope, n, gs, ref, src[:n], dst[:n])
     pool = torch.zeros((4, pb), dtype=torch.uint8, device="cuda")
-    K.kvfp4_quantize_pages_rope(geometry, (rope_dims, mode), dev(hot.view(np.int16)), pool, n, gs,
-                                dev(src), dev(dst))
+    K.kvfp4_quantize_pages_rope(geometry, (rope_dims, mode), dev(hot.view(np.int16)), pool, n + 2,
+                                gs, dev(src), dev(dst))
     got = host(pool)
     mism = np.nonzero(got != ref)
     assert mism[0].size == 0, f"{mism[0].size} bytes differ, first at {mism[0][0]},{mism[1][0]}"
     back_ref = np.full((4, *g.row_shape), 0x1234, np.uint16)
-    RP.dequantize_pages(ref, g, rope, n, gs, back_ref, dst, src)
+    # packed slots in, hot slots out; again two skipped pages (a source
+    # past the pool, a negative destination)
+    dsrc = np.array([1, 3, 0, 7, 0], np.int32)
+    ddst = np.array([2, 0, 1, 3, -2], np.int32)
+    RP.dequantize_pages(ref, g, rope, n, gs, back_ref, dsrc[:n], ddst[:n])
     back = torch.full((4, *g.row_shape), 0x1234, dtype=torch.int16, device="cuda")
-    K.kvfp4_dequantize_pages_rope(geometry, (rope_dims, mode), dev(ref), back, n, gs, dev(dst),
-                                  dev(src))
+    K.kvfp4_dequantize_pages_rope(geometry, (rope_dims, mode), dev(ref), back, n + 2, gs,
+                                  dev(dsrc), dev(ddst))
     got_back = host(back).view(np.uint16)
     mism = np.nonzero(got_back != back_ref)
     assert mism[0].size == 0, f"{mism[0].size} values differ, first at {[m[0] for m in mism]}"
