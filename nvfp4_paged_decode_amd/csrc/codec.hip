@@ -61,6 +61,12 @@ __device__ inline void page_range(int num_pages, int& p0, int& p1) {
   p1 = (int)((long long)(blockIdx.x + 1) * num_pages / gridDim.x);
 }
 
+// This workgroup's contiguous run [u0, u1) of num_units work units.
+__device__ inline void unit_range(long long num_units, long long& u0, long long& u1) {
+  u0 = (long long)blockIdx.x * num_units / gridDim.x;
+  u1 = (long long)(blockIdx.x + 1) * num_units / gridDim.x;
+}
+
 __device__ inline int page_slot(const int32_t* slots, int i, int pool_pages) {
   int s = slots ? __builtin_amdgcn_readfirstlane(slots[i]) : i;
   return (s >= 0 && s < pool_pages) ? s : -1;
@@ -417,32 +423,44 @@ __device__ inline void decode8(uint32_t w, const u32x4& row, uint32_t sign_flip,
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     Geom g, const uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ src,
     uint8_t* __restrict__ hot, int hot_pages, const int32_t* __restrict__ dst, int num_pages,
-    float gs0, float gs1) {
+    int parts, float gs0, float gs1) {
   __shared__ DequantLds s;
   build_dequant_table(s, g.nt, gs0, gs1);
   __syncthreads();
   // A lane owns half a block: 4 data bytes + the block's scale byte in,
-  // 16 contiguous output bytes.
+  // 16 contiguous output bytes.  A work unit is one of `parts` equal runs
+  // of a page's half-blocks (the whole page when parts is 1).
   const int hpp = (int)(g.elems() / 8);
   const int bpt = g.blocks_per_tensor();
   const int data_bytes = (int)g.data_bytes();
-  int p0, p1;
-  page_range(num_pages, p0, p1);
-  for (int p = p0; p < p1; ++p) {
+  long long u0, u1;
+  unit_range((long long)num_pages * parts, u0, u1);
+  for (long long un = u0; un < u1; ++un) {
+    const int p = (int)(un / parts), part = (int)(un - (long long)p * parts);
+    const int hlo = (int)((long long)part * hpp / parts);
+    const int hhi = (int)((long long)(part + 1) * hpp / parts);
     const int ss = page_slot(src, p, packed_pages);
     const int ds = page_slot(dst, p, hot_pages);
     if (ss < 0 || ds < 0) continue;
     const uint8_t* in = packed + (long long)ss * g.page_stride();
     uint8_t* out = hot + (long long)ds * g.hot_bytes();
-    auto rin = __builtin_amdgcn_make_buffer_rsrc((void*)in, (short)0, (int)g.packed_bytes(), kRsrcFlags);
+    // the unit's data words, and the scale bytes of its blocks (a block cut
+    // by the unit boundary is read by both units): half-blocks past the
+    // unit fall outside these ranges and read zero without touching memory,
+    // so the loads need no per-lane condition
+    const int slo = hlo >> 1, shi = (hhi + 1) >> 1;
+    auto rdat = __builtin_amdgcn_make_buffer_rsrc((void*)(in + 4LL * hlo), (short)0, 4 * (hhi - hlo),
+                                                  kRsrcFlags);
+    auto rsc = __builtin_amdgcn_make_buffer_rsrc((void*)(in + data_bytes + slo), (short)0, shi - slo,
+                                                 kRsrcFlags);
     auto rout = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)g.hot_bytes(), kRsrcFlags);
-    for (int h0 = 0; h0 < hpp; h0 += kThreads * kDequantUnroll) {
+    for (int h0 = hlo; h0 < hhi; h0 += kThreads * kDequantUnroll) {
       uint32_t dw[kDequantUnroll], code[kDequantUnroll];
 #pragma unroll
       for (int u = 0; u < kDequantUnroll; ++u) {
         const int hb = h0 + u * kThreads + (int)threadIdx.x;
-        dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rin, hb * 4, 0, KVFP4_CODEC_LOAD_AUX);
-        code[u] = hb < hpp ? __builtin_amdgcn_raw_buffer_load_b8(rin, data_bytes + (hb >> 1), 0,
+        dw[u] = __builtin_amdgcn_raw_buffer_load_b32(rdat, (hb - hlo) * 4, 0, KVFP4_CODEC_LOAD_AUX);
+        code[u] = hb < hhi ? __builtin_amdgcn_raw_buffer_load_b8(rsc, (hb >> 1) - slo, 0,
                                                                  KVFP4_CODEC_SCALE_LOAD_AUX)
                            : 0u;
       }
@@ -454,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
         const uint32_t flip = (code[u] & 0x80u) ? 0x08080808u : 0u;  // negative E4M3 scale
         uint32_t o[4];
         decode8(dw[u], row, flip, o);
-        if (hb < hpp)
+        if (hb < hhi)
           __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rout, hb * 16, 0,
                                                  KVFP4_CODEC_STORE_AUX);
       }
@@ -592,15 +610,14 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 }
 
 int grid_for(const Geom& g, int num_pages, long long target_bytes) {
-  // A workgroup takes at most ppw whole pages, ppw = the pages in about
-  // target_bytes of bf16: fewer workgroups than that would leave some with
-  // one page more while the rest wait for them (4800 Llama-3-8B-shaped
+  // Encoder: a workgroup takes at most ppw whole pages, ppw = the pages in
+  // about target_bytes of bf16: fewer workgroups than that would leave some
+  // with one page more while the rest wait for them (4800 Llama-3-8B-shaped
   // pages over 4096 workgroups took 23% longer than over 4800), more would
-  // repeat each workgroup's table build over little data.  Measured: the
-  // encoder wants about 320 KiB (MLA pages one a workgroup encoded 6%
-  // slower than four), the decoder, whose table is cheaper, one page up to
-  // 96 KiB (MLA pages four a workgroup decoded 3% slower than one).  Past
-  // the cap the runs grow, still differing by at most one page.
+  // repeat each workgroup's table build over little data.  Measured: about
+  // 320 KiB (MLA pages one a workgroup encoded 6% slower than four; two or
+  // four workgroups per Llama-3-8B-shaped page were no faster).  Past the
+  // cap the runs grow, still differing by at most one page.
   long long ppw = target_bytes / g.hot_bytes();
   if (ppw < 1) ppw = 1;
   long long grid = ((long long)num_pages + ppw - 1) / ppw;
@@ -644,9 +661,27 @@ hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages
                              int num_pages, const float* gs, hipStream_t stream) {
   if (num_pages == 0) return hipSuccess;
   float gs1 = g.nt > 1 ? gs[1] : gs[0];
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(g, num_pages, 96LL << 10)), dim3(kThreads), 0, stream, g,
+  // Decoder: its table is cheap, so the work unit is about one round of
+  // loads (kThreads x kDequantUnroll half-blocks, 64 KiB of bf16 out): a
+  // larger page is split into that many equal runs, smaller pages are
+  // grouped whole.  Measured on 4096 Llama-3-8B-shaped pages (4 runs a
+  // page): 219-220 us against 243 us with one page a workgroup; runs of
+  // a quarter of that were slower (305-310 us), the table build dominating.
+  const long long hpp = g.elems() / 8;
+  const long long unit = (long long)kThreads * kDequantUnroll;
+  int parts = 1;
+  long long grid;
+  if (hpp >= unit) {
+    parts = (int)((hpp + unit - 1) / unit);
+    grid = (long long)num_pages * parts;
+  } else {
+    const long long ppw = unit / hpp;
+    grid = ((long long)num_pages + ppw - 1) / ppw;
+  }
+  if (grid > KVFP4_CODEC_GRID) grid = KVFP4_CODEC_GRID;
+  hipLaunchKernelGGL(dequantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g,
                      (const uint8_t*)packed, packed_pages, src, (uint8_t*)hot, hot_pages, dst,
-                     num_pages, gs[0], gs1);
+                     num_pages, parts, gs[0], gs1);
   return hipGetLastError();
 }
 

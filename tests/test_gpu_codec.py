@@ -86,9 +86,12 @@ def _block_zoo(rng, gs, n_pages, geometry):
 
 # (1, 3, 1, 16) and (2, 5, 1, 48): 3 and 30 blocks a page, so the last
 # group of four scale bytes is cut by the page end, and pages are 27 and
-# 270 bytes (not dword-aligned)
+# 270 bytes (not dword-aligned).  The decoder splits larger pages into runs
+# of about 4096 half-blocks: 4 a page for (2, 64, 8, 128), 2 of 2304 for
+# (1, 64, 1, 576), 3 of 2880 for (2, 16, 9, 240); smaller pages are grouped.
 @pytest.mark.parametrize("geometry", [(2, 16, 1, 128), (2, 64, 8, 128), (1, 64, 1, 576),
-                                      (2, 8, 3, 48), (1, 3, 1, 16), (2, 5, 1, 48)])
+                                      (2, 8, 3, 48), (1, 3, 1, 16), (2, 5, 1, 48),
+                                      (2, 16, 9, 240)])
 @pytest.mark.parametrize("gs_val", [1.0, 2.0 ** -3, float(np.float32(0.0123456)),
                                     float(np.float32(3.1e-5)), 2.0 ** -110,
                                     float(np.float32(1e30))])
