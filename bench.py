@@ -305,11 +305,44 @@ def _oracle_attend(task):
     return L
 
 
+def cgroup_cpu_quota() -> float | None:
+    """CPUs' worth of time the process's cgroup may use (cpu.max), or None
+    when it is unlimited or not readable."""
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            return int(quota) / int(period)
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+#: Processes the oracle may start on the benchmark's host: the CPU share one
+#: GPU has on the MI355X hosts this runs on (their cores are shared between
+#: the GPUs of the machine).
+CPU_SHARE_PER_GPU = 16
+
+
+def oracle_processes() -> tuple[int, dict]:
+    """Worker count for the oracle: every core the process may run on, up to
+    the cgroup's CPU quota and the one-GPU CPU share; and the host's own
+    figures, reported beside it."""
+    affinity = len(os.sched_getaffinity(0))
+    quota = cgroup_cpu_quota()
+    n = affinity
+    if quota is not None:
+        n = min(n, max(1, int(quota)))
+    n = max(1, min(n, CPU_SHARE_PER_GPU))
+    return n, {"host_logical_cpus": os.cpu_count(), "affinity_cpus": affinity,
+               "cgroup_cpu_quota": quota, "cpu_share_per_gpu": CPU_SHARE_PER_GPU}
+
+
 def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_token: float,
                  step_bytes: float) -> dict:
     """The oracle as it stands, on the host's cores, over a bounded sample of
     the same workload.  A pool of processes (one per core the process may
-    use, at most 16, each with one BLAS thread) encodes chunks of 16 pages,
+    use, within the cgroup quota and the one-GPU share, each with one BLAS
+    thread) encodes chunks of 16 pages,
     decodes them back, and runs decode attention for whole sequences (all
     query heads); the sample sizes come from a short single-process timing
     so that the three legs take about a quarter, a quarter and a half of
@@ -322,7 +355,7 @@ def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_t
     g = O.Geometry(*wl.geometry)
     per_page = codec_bytes(wl.geometry, 1)
     chunk = 16
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores, host = oracle_processes()
     used = wl.used_slots
     n_chunks = used.shape[0] // chunk
     seq_packed = {}
@@ -399,7 +432,7 @@ def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_t
     except OSError:
         pass
     return {"value": round(step_bytes / t_step / 1e9, 6), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "processes": cores, **host,
             "sample": (f"oracle (NumPy fp64) in {cores} processes, one thread each, on {cpu}: "
                        f"encode {n_q} pages ({q_s:.1f} s), decode {n_q} pages ({dq_s:.1f} s), "
                        f"attention for {n_att} sequence(s) ({tokens} tokens, all "

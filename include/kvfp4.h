@@ -209,7 +209,12 @@ int32_t kvfp4_dequantize_pages_rope(const kvfp4_geometry* g, const kvfp4_rope_la
                                     int32_t num_pages, const float* global_scale, void* stream);
 
 /* Workspace bytes kvfp4_paged_decode_attention needs for these sizes on the
- * current device (0 is a valid answer). */
+ * current device (0 is a valid answer); 0 also for sizes that call would
+ * reject.  The workspace holds the split-K partials (o, max, sum) of the
+ * decode kernels before they are merged: "Accelerating Long-Context and
+ * Agentic Inference with NVFP4 KV Cache", Path 3: Decode describes decode
+ * as a memory-read-bound pass over the whole cached context, which only
+ * fills the GPU when a sequence's context is split over many workgroups. */
 size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,
                                     int32_t num_q_heads, int32_t v_dim,
                                     int32_t max_seq_len_hint);
@@ -228,9 +233,11 @@ size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch,
  *   q             bf16 [batch][num_q_heads][head_dim], 16-byte aligned
  *   v_dim         == head_dim when num_kv_tensors == 2; <= head_dim for MLA
  *   block_table   int32 [batch][max_pages_per_seq]
- *   seq_lens      int32 [batch]; each <= max_seq_len_hint and
- *                 <= max_pages_per_seq * T (longer values are clamped)
- *   max_seq_len_hint HOST upper bound on seq_lens (sizes the split-K plan)
+ *   seq_lens      int32 [batch]; values above max_pages_per_seq * T are
+ *                 clamped to it, negative values to 0
+ *   max_seq_len_hint HOST estimate of the longest seq_lens entry; it only
+ *                 sizes the split-K plan (a longer sequence is still
+ *                 attended in full, a wrong hint only costs speed)
  *   out           bf16 [batch][num_q_heads][v_dim]
  *   lse           float [batch][num_q_heads] natural-log LSE, or NULL;
  *                 seq_lens[b] == 0 gives out = 0 and lse = -inf.
@@ -245,10 +252,14 @@ int32_t kvfp4_paged_decode_attention(
     const int32_t* seq_lens, int32_t max_seq_len_hint, float softmax_scale,
     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static text for a status code. */
+/* Static text for a status code.  "KV Cache Compression in TensorRT LLM",
+ * Configuration and Setup of KV Cache Compression: an unsupported
+ * combination is turned away with a clear message, not run. */
 const char* kvfp4_status_string(int32_t status);
 
-/* Detail of the last failure on the calling thread ("" if none). */
+/* Detail of the last failure on the calling thread ("" if none): which
+ * argument was rejected and why (same passage as kvfp4_status_string).
+ * The pointer stays valid until the thread's next call into the library. */
 const char* kvfp4_last_error_message(void);
 
 #ifdef __cplusplus

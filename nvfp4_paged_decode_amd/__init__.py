@@ -145,6 +145,46 @@ def _ptr(t, host_ok: bool = False) -> Optional[int]:
     return t.data_ptr()
 
 
+def _int32(t, name: str, min_numel: int):
+    """Check an index tensor before its pointer is taken: the kernels read
+    int32, so an int64 tensor (torch's default integer type) would be read
+    as pairs of halves."""
+    if t is None:
+        return
+    import torch
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} entries, needs at least {min_numel}")
+
+
+def _check_decode_args(g: "Geometry", q, out, lse, block_table, seq_lens, vd: int) -> None:
+    """Shapes and dtypes of the decode call's tensors, checked before any
+    pointer is taken (the library sees only pointers and sizes)."""
+    import torch
+    if q.dim() != 3 or q.element_size() != 2:
+        raise ValueError("q must be a 3-d tensor [batch, num_q_heads, head_dim] of 2-byte "
+                         f"elements (bf16 bits), got shape {tuple(q.shape)} and {q.dtype}")
+    if int(q.shape[-1]) != g.head_dim:
+        raise ValueError(f"q.shape[-1] = {int(q.shape[-1])} differs from head_dim {g.head_dim}")
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    if out.element_size() != 2:
+        raise ValueError(f"out must hold 2-byte elements (bf16 bits), got {out.dtype}")
+    if out.numel() < B * Hq * vd:
+        raise ValueError(f"out holds {out.numel()} elements, needs {B} x {Hq} x {vd}")
+    if lse is not None:
+        if lse.dtype != torch.float32:
+            raise ValueError(f"lse must be float32, got {lse.dtype}")
+        if lse.numel() < B * Hq:
+            raise ValueError(f"lse holds {lse.numel()} elements, needs {B} x {Hq}")
+    if block_table.dim() != 2:
+        raise ValueError(f"block_table must be 2-d [batch, max_pages], got {tuple(block_table.shape)}")
+    _int32(block_table, "block_table", 1)
+    if int(block_table.shape[0]) < B:
+        raise ValueError(f"block_table has {int(block_table.shape[0])} rows, needs {B}")
+    _int32(seq_lens, "seq_lens", B)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is not None:
         return int(stream)
@@ -178,6 +218,8 @@ def kvfp4_quantize_pages(geometry, hot_pool, packed_pool, num_pages: int, global
     (device memory, or pinned host memory: the offload path)."""
     lib = load_library()
     g = Geometry.of(geometry)
+    _int32(src_slots, "src_slots", int(num_pages))
+    _int32(dst_slots, "dst_slots", int(num_pages))
     _check(lib.kvfp4_quantize_pages(
         ctypes.byref(g), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)), _ptr(src_slots),
         _ptr(packed_pool, host_ok=True), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
@@ -191,6 +233,8 @@ def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, glob
     pinned host memory: the onboard path) into ``hot_pool``."""
     lib = load_library()
     g = Geometry.of(geometry)
+    _int32(src_slots, "src_slots", int(num_pages))
+    _int32(dst_slots, "dst_slots", int(num_pages))
     _check(lib.kvfp4_dequantize_pages(
         ctypes.byref(g), _ptr(packed_pool, host_ok=True),
         _pages(packed_pool, kvfp4_packed_page_bytes(g)),
@@ -208,6 +252,8 @@ def kvfp4_quantize_pages_rope(geometry, rope, hot_pool, packed_pool, num_pages: 
     """kvfp4_quantize_pages into slots of a RoPE layout ``(rope_dims, mode)``."""
     lib = load_library()
     g, r = Geometry.of(geometry), RopeLayout.of(rope)
+    _int32(src_slots, "src_slots", int(num_pages))
+    _int32(dst_slots, "dst_slots", int(num_pages))
     _check(lib.kvfp4_quantize_pages_rope(
         ctypes.byref(g), ctypes.byref(r), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
         _ptr(src_slots), _ptr(packed_pool, host_ok=True),
@@ -221,6 +267,8 @@ def kvfp4_dequantize_pages_rope(geometry, rope, packed_pool, hot_pool, num_pages
     """kvfp4_dequantize_pages from slots of a RoPE layout ``(rope_dims, mode)``."""
     lib = load_library()
     g, r = Geometry.of(geometry), RopeLayout.of(rope)
+    _int32(src_slots, "src_slots", int(num_pages))
+    _int32(dst_slots, "dst_slots", int(num_pages))
     _check(lib.kvfp4_dequantize_pages_rope(
         ctypes.byref(g), ctypes.byref(r), _ptr(packed_pool, host_ok=True),
         _pages(packed_pool, kvfp4_packed_page_bytes_rope(g, r)), _ptr(src_slots), _ptr(hot_pool),
@@ -238,6 +286,8 @@ def kvfp4_append_quantize(geometry, rows, token_slots, token_rows, packed_pool, 
     n = int(token_slots.shape[0])
     if int(token_rows.shape[0]) != n:
         raise ValueError("token_slots and token_rows differ in length")
+    _int32(token_slots, "token_slots", n)
+    _int32(token_rows, "token_rows", n)
     if rows_dtype is None:
         rows_dtype = KVFP4_ROWS_FP8_E4M3 if rows.element_size() == 1 else KVFP4_ROWS_BF16
     width = 1 if rows_dtype == KVFP4_ROWS_FP8_E4M3 else 2
@@ -262,6 +312,8 @@ def kvfp4_gather_dequantize(geometry, packed_pool, token_slots, token_rows, out,
     n = int(token_slots.shape[0])
     if int(token_rows.shape[0]) != n:
         raise ValueError("token_slots and token_rows differ in length")
+    _int32(token_slots, "token_slots", n)
+    _int32(token_rows, "token_rows", n)
     if out_dtype is None:
         out_dtype = KVFP4_ROWS_FP8_E4M3 if out.element_size() == 1 else KVFP4_ROWS_BF16
     width = 1 if out_dtype == KVFP4_ROWS_FP8_E4M3 else 2
@@ -290,8 +342,9 @@ def kvfp4_paged_decode_attention(geometry, packed_pool, global_scale, q, block_t
     bf16 tensor ``[B, Hq, v_dim]``) and, if given, ``lse`` (fp32 ``[B, Hq]``)."""
     lib = load_library()
     g = Geometry.of(geometry)
-    B, Hq = int(q.shape[0]), int(q.shape[1])
     vd = int(v_dim if v_dim is not None else out.shape[-1])
+    _check_decode_args(g, q, out, lse, block_table, seq_lens, vd)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.kvfp4_paged_decode_attention(
         ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),

@@ -666,9 +666,10 @@ hipError_t launch_dequantize(const Geom& g, const void* packed, int packed_pages
   // Decoder: its table is cheap, so the work unit is about one round of
   // loads (kThreads x kDequantUnroll half-blocks, 64 KiB of bf16 out): a
   // larger page is split into that many equal runs, smaller pages are
-  // grouped whole.  Measured on 4096 Llama-3-8B-shaped pages (4 runs a
-  // page): 219-220 us against 243 us with one page a workgroup; runs of
-  // a quarter of that were slower (305-310 us), the table build dominating.
+  // grouped whole.  Measured on 4096 Llama-3-8B-shaped pages in a random
+  // slot order (4 runs a page): 241.5-242 us against 250.5-251.5 us with
+  // one page a workgroup; runs of a quarter of that were slower (305-310
+  // us), the table build dominating.
   const long long hpp = g.elems() / 8;
   const long long unit = (long long)kThreads * kDequantUnroll;
   int parts = 1;

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(kGenThreads) void decode_generic_kernel(DecodeArgs 
   if (L < 0) L = 0;
   const int t_begin = split * a.pages_per_split * g.T;
   int t_end = t_begin + a.pages_per_split * g.T;
-  if (t_end > L) t_end = L;
+  // the plan is sized from the caller's length hint; the last split takes
+  // whatever lies beyond it, so a longer sequence is still attended in full
+  if (t_end > L || split == a.splits - 1) t_end = L;
 
   const long long page_bytes = g.packed_bytes(), data_bytes = g.data_bytes();
   const long long row_data = D / 2, row_scale = D / 16;

@@ -393,10 +393,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
         for (int dt = 0; dt < KD / 16; ++dt) acc[dt] *= alpha;
         m = mn;
       }
+      // P.V multiplies the fp16-rounded probabilities, so the denominator
+      // sums those same values
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+        p[r] = (float)(_Float16)__builtin_amdgcn_exp2f(sv[r] - m);
         l += p[r];
       }
       const uint32_t pw0 = pack_f16(p[0], p[1]), pw1 = pack_f16(p[2], p[3]);

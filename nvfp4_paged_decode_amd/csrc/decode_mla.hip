@@ -312,9 +312,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
       f16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sv[e] - m);
-        l += p;
-        pb[e] = (_Float16)p;
+        // the denominator sums the fp16-rounded values P.V multiplies
+        pb[e] = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m);
+        l += (float)pb[e];
       }
 
       // 4. O^T[dim][head] += V^T P^T over the 32 tokens

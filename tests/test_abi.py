@@ -296,3 +296,86 @@ def test_decode_routing_by_workspace(lib, geom, hq, balanced):
         assert n == balanced_bytes
     else:
         assert n != balanced_bytes and n % row == 0
+
+
+# --- the Python binding's checks, made before any pointer is taken --------
+# CPU tensors stand in for device tensors: every call below is turned away
+# by a shape or dtype check that runs before the pointer check.
+
+def _decode_call(**over):
+    torch = pytest.importorskip("torch")
+    B, Hq, D = 2, 8, 128
+    args = dict(
+        geometry=(2, 64, 2, D), packed_pool=torch.zeros(4, 64, dtype=torch.uint8),
+        global_scale=[1.0, 1.0], q=torch.zeros(B, Hq, D, dtype=torch.int16),
+        block_table=torch.zeros(B, 4, dtype=torch.int32),
+        seq_lens=torch.zeros(B, dtype=torch.int32), max_seq_len_hint=256,
+        softmax_scale=0.1, out=torch.zeros(B, Hq, D, dtype=torch.int16),
+        lse=torch.zeros(B, Hq, dtype=torch.float32), workspace=None, v_dim=D)
+    args.update(over)
+    K.kvfp4_paged_decode_attention(**args)
+
+
+@pytest.mark.parametrize("name,make,msg", [
+    ("block_table", lambda t: t.zeros(2, 4, dtype=t.int64), "int32"),
+    ("block_table", lambda t: t.zeros(8, dtype=t.int32), "2-d"),
+    ("block_table", lambda t: t.zeros(1, 4, dtype=t.int32), "rows"),
+    ("seq_lens", lambda t: t.zeros(2, dtype=t.int64), "int32"),
+    ("seq_lens", lambda t: t.zeros(1, dtype=t.int32), "at least 2"),
+    ("q", lambda t: t.zeros(2, 8, 128, dtype=t.float32), "2-byte"),
+    ("q", lambda t: t.zeros(2, 8, 64, dtype=t.int16), "head_dim"),
+    ("q", lambda t: t.zeros(16, 128, dtype=t.int16), "3-d"),
+    ("out", lambda t: t.zeros(2 * 8 * 128 - 1, dtype=t.int16), "needs"),
+    ("out", lambda t: t.zeros(2, 8, 128, dtype=t.float32), "2-byte"),
+    ("lse", lambda t: t.zeros(2, 7, dtype=t.float32), "needs"),
+    ("lse", lambda t: t.zeros(2, 8, dtype=t.float64), "float32"),
+])
+def test_binding_rejects_decode_tensor(lib, name, make, msg):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match=msg):
+        _decode_call(**{name: make(torch)})
+
+
+@pytest.mark.parametrize("fn", ["kvfp4_quantize_pages", "kvfp4_dequantize_pages"])
+@pytest.mark.parametrize("which,make,msg", [
+    ("src_slots", lambda t: t.arange(4, dtype=t.int64), "int32"),
+    ("dst_slots", lambda t: t.arange(4, dtype=t.int64), "int32"),
+    ("src_slots", lambda t: t.arange(3, dtype=t.int32), "at least 4"),
+    ("dst_slots", lambda t: t.arange(3, dtype=t.int32), "at least 4"),
+])
+def test_binding_rejects_codec_slots(lib, fn, which, make, msg):
+    torch = pytest.importorskip("torch")
+    g = (2, 64, 8, 128)
+    a = torch.zeros(8, 16, dtype=torch.uint8)
+    b = torch.zeros(8, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=msg):
+        getattr(K, fn)(g, a, b, 4, [1.0, 1.0], **{which: make(torch)})
+
+
+@pytest.mark.parametrize("fn", ["kvfp4_quantize_pages_rope", "kvfp4_dequantize_pages_rope"])
+def test_binding_rejects_rope_codec_slots(lib, fn):
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(8, 16, dtype=torch.uint8)
+    b = torch.zeros(8, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="int32"):
+        getattr(K, fn)((2, 64, 8, 128), (64, 1), a, b, 4, [1.0, 1.0],
+                       src_slots=torch.arange(4, dtype=torch.int64))
+
+
+@pytest.mark.parametrize("fn", ["kvfp4_append_quantize", "kvfp4_gather_dequantize"])
+@pytest.mark.parametrize("which", ["token_slots", "token_rows"])
+def test_binding_rejects_token_index_dtype(lib, fn, which):
+    torch = pytest.importorskip("torch")
+    n = 4
+    idx = {"token_slots": torch.zeros(n, dtype=torch.int32),
+           "token_rows": torch.zeros(n, dtype=torch.int32)}
+    idx[which] = torch.zeros(n, dtype=torch.int64)
+    rows = torch.zeros(n, 2, 8, 128, dtype=torch.int16)
+    pool = torch.zeros(8, 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="int32"):
+        if fn == "kvfp4_append_quantize":
+            K.kvfp4_append_quantize((2, 64, 8, 128), rows, idx["token_slots"], idx["token_rows"],
+                                    pool, [1.0, 1.0])
+        else:
+            K.kvfp4_gather_dequantize((2, 64, 8, 128), pool, idx["token_slots"],
+                                      idx["token_rows"], rows, [1.0, 1.0])

@@ -41,6 +41,36 @@ def _small_gqa(seed=9, B=3, H=2, G=4, D=64, T=16, lens=(37, 16, 1)):
                             W.calibrated_scales(hot), perm[:c], int(perm[-1]))
 
 
+def _walked_kv(wl, gs, b):
+    """K/V of sequence b for the textbook reference, built without the
+    oracle's page-table walk or its decode: token j's bf16 row is read from
+    the hot pool at slot block_table[b][j // T], row j % T, quantized with
+    the oracle's row quantizer (pinned by the brute-force tests), and its
+    codes are decoded here from exact E2M1 / E4M3 rationals."""
+    from fractions import Fraction
+    from tests.exact import E2M1, E4M3
+    T, H, D = wl.page_size, wl.num_kv_heads, wl.head_dim
+    L = int(wl.seq_lens[b])
+    out = []
+    for t in range(wl.num_kv_tensors):
+        gsf = Fraction(float(np.float32(gs[t])))
+        rows = np.empty((L, H, D), np.float64)
+        for j in range(L):
+            slot = int(wl.block_table[b][j // T])
+            bits = wl.hot_pool[slot, t, j % T]           # [H, D] bf16 bits
+            data, scales = O.quantize_rows(bits, gs[t])
+            for h in range(H):
+                for d in range(D):
+                    byte = int(data[h, d // 2])
+                    nib = byte & 0xF if d % 2 == 0 else byte >> 4
+                    v = E2M1[nib & 7] * E4M3[int(scales[h, d // 16])] * gsf
+                    rows[j, h, d] = float(-v if nib & 8 else v)
+        out.append(rows)
+    K = out[0]
+    V = K if wl.num_kv_tensors == 1 else out[1]
+    return K, V[..., :wl.v_dim]
+
+
 @pytest.mark.parametrize("gs_kind", ["unit", "calibrated"])
 def test_matches_torch_sdpa_in_float64(gs_kind):
     wl = _small_gqa()
@@ -50,7 +80,7 @@ def test_matches_torch_sdpa_in_float64(gs_kind):
                                   wl.softmax_scale, wl.v_dim)
     G = wl.num_q_heads // wl.num_kv_heads
     for b in range(wl.batch):
-        K, V = _dense_kv(wl, g, packed, gs, b)
+        K, V = _walked_kv(wl, gs, b)
         q = torch.from_numpy(O.bf16_bits_to_f64(wl.q[b]))[None, :, None, :]  # [1, Hq, 1, D]
         k = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, 0)[None]
         v = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0)[None]

@@ -249,3 +249,27 @@ def test_gather_fp8_equals_torch_cast_of_exact_values():
     ref = ref.view(torch.uint8).numpy()
     assert keep.mean() > 0.9 and np.array_equal(f8[keep], ref[keep])
     assert np.all((f8[~keep] & 0x7F) == 0x7E)  # saturated to +-448
+
+
+@pytest.mark.parametrize("gs", [0.7, 1.0 / 3.0, 1.2345e-3, 37.5])
+def test_dequantize_rows_equals_exact_rational_rounding(gs):
+    """Every (code, scale) pair at a non-power-of-two tensor scale: the
+    oracle's bf16 value is the bf16 nearest (ties to even) to the exact
+    rational product e2m1 * e4m3 * gs, found by the brute-force rounding of
+    tests/exact.py."""
+    from fractions import Fraction
+    from tests.exact import E2M1, E4M3, bf16_round_exact
+    gs32 = float(np.float32(gs))
+    gsf = Fraction(gs32)
+    nibs = np.arange(16, dtype=np.int64)
+    codes = np.arange(127, dtype=np.uint8)  # every finite scale code
+    # one 16-value block per scale code holding all 16 nibbles
+    data = np.tile((nibs[0::2] | (nibs[1::2] << 4)).astype(np.uint8), (127, 1))
+    got = O.dequantize_rows(data, codes[:, None], gs32)
+    for c in range(127):
+        for n in range(16):
+            v = E2M1[n & 7] * E4M3[c] * gsf
+            want = bf16_round_exact(-v if n & 8 else v)
+            if v == 0 and n & 8:
+                want = 0x8000  # -0 keeps its sign
+            assert int(got[c, n]) == want, (gs, c, n)
