@@ -65,10 +65,23 @@ constexpr int kPitch = 592;        // fp16 per staged row (296 dwords = 8 mod 32
 constexpr int kRowData = kD / 2, kRowScale = kD / 16;  // packed bytes per row
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kSlack = 8.f;      // lazy-rescale threshold (log2 units)
+constexpr float kHeadroom = 15.f;  // p = 2^(s - m) <= 2^15 stays finite in fp16
+#ifndef KVFP4_MLA_HB1  // 1: 16 heads a wave above 64 heads (eight waves)
+#define KVFP4_MLA_HB1 0
+#endif
+constexpr int kKAhead = 2;         // k-steps of K fragments read ahead of the products
+constexpr int kVAhead = 3;         // dim tiles of V^T fragments read ahead
 
 struct MlaLds {
   _Float16 k[2][kTile][kPitch];  // double-buffered natural latent tiles
+  int vote[8];                   // per wave: a head of its segment needs a second pass
+};
+// With 32 heads a wave the second head block's query fragments sit in LDS
+// (each wave reads only its own): registers hold the first block's queries
+// and the accumulators.
+struct MlaLds2 {
+  MlaLds t;
+  f16x8 q1[4][kKs][64];  // [wave][k-step][lane]
 };
 
 // Swizzle of staged row `row`: 16-byte chunk c sits at chunk c ^ swz(row).
@@ -99,31 +112,66 @@ __device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
   return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Score products of the 32-heads-a-wave layout.  The compiler selects one
+// register form for every MFMA of a kernel; with the 256 output accumulators
+// holding the whole accumulation register file, the score chains must use
+// ordinary VGPRs, so they are issued here with VGPR operands.  A chain's
+// first product takes a zero accumulator; the products of one chain are
+// always four MFMAs apart (four chains interleaved), and mfma_settle pads
+// the last product's result before any other instruction reads it (19 wait
+// states cover the VALU-read latency of an 8-pass XDL product).
+__device__ inline f32x4 mfma_v0(const f16x8& a, const f16x8& b) {
+  f32x4 d;
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ inline void mfma_v(f32x4& c, const f16x8& a, const f16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 __device__ inline f16x4 lds_read_tr(const _Float16* p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(f16x4, r);
 }
 
+// A tile holds kTile x 2 kBlocks = 2304 half-blocks (4 data bytes and the
+// block's scale byte each); thread tid stages half-blocks tid, tid + NT,
+// ...  Half-block i is chunk i % 72 of token row i / 72: its data bytes sit
+// at 4 i in the tile's data rows and its scale byte at i / 2, so a wave's
+// loads cover contiguous bytes, and the 8 lanes of each 16-byte LDS store
+// write 8 consecutive chunks of one row (distinct banks).
+constexpr int kHalf = kTile * 2 * kBlocks;  // half-blocks per tile
 template <int NW>
 struct Prefetch {
-  static constexpr int kPer = (kTile * kBlocks + 64 * NW - 1) / (64 * NW);  // blocks per thread
-  u32x2 d[kPer];
+  // half-blocks per thread (an equal share for 1, 2, 3, 4 and 6 waves;
+  // otherwise the last round is partial)
+  static constexpr int kPer = (kHalf + 64 * NW - 1) / (64 * NW);
+  static constexpr bool kEven = kHalf % (64 * NW) == 0;
+  uint32_t d[kPer];
   uint32_t s[kPer];
 };
 
-template <int NW>
+// HB head blocks of 16 per wave.  With HB = 2 (more than 64 heads) every K
+// and V^T fragment a wave reads from LDS feeds two products, which halves
+// the LDS traffic per flop -- the kernel's bound at 16 heads a wave -- and
+// the wave's 32 heads x 512 dims of fp32 accumulators (256 registers) take
+// the whole accumulation register file, so the kernel runs one wave per
+// SIMD (4 waves, 512 registers each).
+template <int NW, int HB>
 __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   constexpr int NT = 64 * NW;
   constexpr int kPer = Prefetch<NW>::kPer;
+  constexpr int HW = 16 * HB;  // heads per wave
   extern __shared__ __align__(16) unsigned char smem[];
   MlaLds& st = *reinterpret_cast<MlaLds*>(smem);
   const Geom g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;  // head column (or token row), k-group
-  const int head = 16 * wave + col;
-  const bool head_ok = head < a.hq;
   const int w = blockIdx.x, nwg = gridDim.x;
   const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
   const long long page_bytes = g.packed_bytes(), data_bytes = g.data_bytes();
@@ -148,7 +196,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     const int row = 16 * h + 4 * grp + q4;
     tr_off[h] = row * kPitch + 8 * ((j4 >> 1) ^ sw) + 4 * (j4 & 1);
   }
-
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
   note_total(a, w, rng.ptot);
@@ -162,37 +209,44 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;
     note_segment(a, w, b, p_lo, p_hi, npages);
-    const long long t_lo = p_lo * tiles_per_page;
-    long long t_hi = p_hi * tiles_per_page;
-    const long long t_end = (L + kTile - 1) / kTile;
+    // tile indices within the sequence (32-bit: a sequence holds at most
+    // 2^31 tokens); tile t is tile t % tiles_per_page of page t / tiles_per_page
+    const int t_lo = (int)p_lo * tiles_per_page;
+    int t_hi = (int)p_hi * tiles_per_page;
+    const int t_end = (L + kTile - 1) / kTile;
     if (t_hi > t_end) t_hi = t_end;
 
     // page-table entries of pages c0 .. c0+63, one per lane
     const int32_t* bt_row = a.block_table + (long long)b * a.max_pages;
-    long long c0 = -(1LL << 40);
+    int c0 = -(1 << 30);
     int slot_vec = -1;
-    auto slot_of = [&](long long ti) -> int {
-      const long long pg = ti / tiles_per_page;
+    auto slot_of = [&](int pg) -> int {
       if (pg < c0 || pg >= c0 + 64) {
         c0 = pg;
-        slot_vec = (c0 + lane < p_hi) ? bt_row[c0 + lane] : -1;
+        slot_vec = (c0 + lane < (int)p_hi) ? bt_row[c0 + lane] : -1;
       }
-      return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
+      return __builtin_amdgcn_readlane(slot_vec, pg - c0);
     };
-    auto rows_of = [&](int slot, long long ti) -> int {
-      int n = L - (int)(ti * kTile);
+    auto rows_of = [&](int slot, int ti) -> int {
+      int n = L - ti * kTile;
       n = n > kTile ? kTile : n;
       if (slot < 0 || slot >= a.pool_pages) n = 0;
       return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
     };
 
-    // this thread's blocks of a tile: block bi = tid + NT u is row bi % 32,
-    // block bi / 32 of the row; rows past the sequence end read as zero
+    // rows past the sequence end (or a whole tile of a bad page) read as
+    // zero through the buffer resources' bounds
     Prefetch<NW> pre;
-    auto issue = [&](long long ti) -> int {
-      const int slot = slot_of(ti);
+    // the next tile to request, as (page, tile within the page)
+    int nx_pg = (int)p_lo, nx_tip = 0;
+    auto issue = [&](int ti) -> int {
+      const int slot = slot_of(nx_pg);
       const int n = rows_of(slot, ti);
-      const int row0 = (int)(ti % tiles_per_page) * kTile;
+      const int row0 = nx_tip * kTile;
+      if (++nx_tip == tiles_per_page) {
+        nx_tip = 0;
+        ++nx_pg;
+      }
       const uint8_t* page = a.pool + (long long)(n > 0 ? slot : 0) * page_bytes;
       auto rd = __builtin_amdgcn_make_buffer_rsrc((void*)(page + (long long)row0 * kRowData),
                                                   (short)0, n * kRowData, 0x00020000);
@@ -201,38 +255,44 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
           0x00020000);
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int bi = tid + NT * u;
-        if (bi < kTile * kBlocks) {
-          const int t = bi & (kTile - 1), blk = bi >> 5;
-          pre.d[u] = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rd, t * kRowData + 8 * blk, 0, 0));
-          pre.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, t * kRowScale + blk, 0, 0);
-        }
+        // the round's constant part goes in the scalar offset; a half-block
+        // past the tile (partial last round) reads past the buffer's range:
+        // zero, nothing fetched
+        const int hi = tid + NT * u;
+        const bool in = Prefetch<NW>::kEven || hi < kHalf;
+        pre.d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, in ? 4 * tid : 1 << 28, 4 * NT * u, 0);
+        pre.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? tid >> 1 : 1 << 28, NT * u / 2, 0);
       }
       return n;
     };
     auto stage = [&](int buf) {
       _Float16* base = &st.k[buf][0][0];
+      // recomputed per tile (a few integer ops) rather than kept: the empty
+      // asm stops the compiler from hoisting kPer offsets out of the loop,
+      // which it would then spill
+      int tid_l = tid;
+      asm volatile("" : "+v"(tid_l));
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int bi = tid + NT * u;
-        if (bi < kTile * kBlocks) {
-          const int t = bi & (kTile - 1), blk = bi >> 5;
-          const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pre.s[u], 1.0f, false);
-          const _Float16 sb = sp.x;
-          *reinterpret_cast<f16x8*>(base + chunk_at(t, 2 * blk)) = dequant8(pre.d[u].x, sb);
-          *reinterpret_cast<f16x8*>(base + chunk_at(t, 2 * blk + 1)) = dequant8(pre.d[u].y, sb);
-        }
+        const int hi = tid_l + NT * u;
+        if (!Prefetch<NW>::kEven && hi >= kHalf) continue;
+        const int t = hi / (2 * kBlocks), c = hi - t * (2 * kBlocks);
+        const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pre.s[u], 1.0f, false);
+        const _Float16 sb = sp[0];
+        *reinterpret_cast<f16x8*>(base + chunk_at(t, c)) = dequant8(pre.d[u], sb);
       }
     };
 
-    int n_cur = issue(t_lo);
-
-    // queries of this wave's 16 heads (B operand of the scores): lane
-    // (column c, group g) holds dims 32 ks + 8 g .. +8 of head c
-    f16x8 qb[kKs];
-    float qs;
-    {
+    // queries of this wave's heads (B operand of the scores): for head block
+    // hb, lane (column c, group g) holds dims 32 ks + 8 g .. +8 of head
+    // HW wave + 16 hb + c
+    f16x8 qb[kKs];  // head block 0 (head block 1: LDS)
+    float qs[HB];
+    MlaLds2& st2 = *reinterpret_cast<MlaLds2*>(smem);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = HW * wave + 16 * hb + col;
+      const bool head_ok = head < a.hq;
       const uint16_t* qrow = a.q + ((long long)b * a.hq + (head_ok ? head : 0)) * kD + 8 * grp;
       u32x4 raw[kKs];
       uint32_t mb = 0;
@@ -255,75 +315,143 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
       }
       const int shq = head_ok ? sh : -200;  // padding columns: exactly 0
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks)
+      for (int ks = 0; ks < kKs; ++ks) {
+        f16x8 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qb[ks][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] << 16), shq);
-          qb[ks][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] & 0xFFFF0000u), shq);
+          v[2 * e] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] << 16), shq);
+          v[2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[ks][e] & 0xFFFF0000u), shq);
         }
-      qs = ldexpf(base_scale, -sh);
+        if (hb == 0)
+          qb[ks] = v;
+        else
+          st2.q1[wave][ks][lane] = v;
+      }
+      qs[hb] = ldexpf(base_scale, -sh);
     }
 
-    f32x4 acc[kDt];
+    // Softmax without rescaling the accumulators: a column's maximum m is
+    // fixed by its first tile with a valid token, and the probabilities
+    // 2^(s - m) of later tiles are used as they are while s - m stays within
+    // kHeadroom (fp16 holds them).  A later score beyond that makes the
+    // whole workgroup compute the segment again with m = the maximum over
+    // the segment seen in the first pass (a workgroup-wide vote at the end
+    // of the pass), after which no score exceeds m.  The accumulators are
+    // therefore only ever zeroed or written by MFMA.
+    f32x4 acc[HB][kDt];
+    float m[HB], l[HB], mseen[HB];
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m = kNoMax, l = 0.f;
-
+    for (int hb = 0; hb < HB; ++hb) m[hb] = kNoMax;
+    for (;;) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) acc[hb][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      l[hb] = 0.f;
+      mseen[hb] = m[hb];
+    }
+    bool over = false;
+    nx_pg = (int)p_lo;
+    nx_tip = 0;
+    int n_cur = issue(t_lo);
     stage(0);
     __syncthreads();
     int buf = 0;
-    for (long long ti = t_lo; ti < t_hi; ++ti) {
+    for (int ti = t_lo; ti < t_hi; ++ti) {
       const bool more = ti + 1 < t_hi;
       int n_nxt = 0;
       if (more) n_nxt = issue(ti + 1);
       const _Float16* kb = &st.k[buf][0][0];
 
-      // 2. scores S^T[token][head], 16 tokens per half
-      f32x4 sc[2];
+      // 2. scores S^T[token][head] per 16-token half and head block; each
+      //    K fragment read from LDS feeds every head block.  Reads run
+      //    kKAhead k-steps ahead of the products through a small ring, so
+      //    only that many fragments are live (the scheduling barriers keep
+      //    the compiler from hoisting all 36 reads, which spills)
+      f32x4 sc[HB][2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sc[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < HB; ++hb) sc[hb][0] = sc[hb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      {
+        // fragment ring: [0..1] K of the two token halves, [2] head block
+        // 1's queries
+        f16x8 kf[kKAhead + 1][HB + 1];
+        auto kread = [&](int ks, f16x8 (&dst)[HB + 1]) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            dst[tt] = *reinterpret_cast<const f16x8*>(kb + nat_off[tt] + 32 * ks);
+          if (HB == 2) dst[HB] = st2.q1[wave][ks][lane];
+        };
+#pragma unroll
+        for (int ks = 0; ks < kKAhead; ++ks) kread(ks, kf[ks]);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-          const f16x8 ka = *reinterpret_cast<const f16x8*>(kb + nat_off[tt] + 32 * ks);
-          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], sc[tt], 0, 0, 0);
+          if (ks + kKAhead < kKs) kread(ks + kKAhead, kf[(ks + kKAhead) % (kKAhead + 1)]);
+          const int r = ks % (kKAhead + 1);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+              const f16x8& qf = hb == 0 ? qb[ks] : kf[r][HB];
+              if (HB == 1)
+                sc[hb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[r][tt], qf, sc[hb][tt],
+                                                                    0, 0, 0);
+              else if (ks == 0)
+                sc[hb][tt] = mfma_v0(kf[r][tt], qf);
+              else
+                mfma_v(sc[hb][tt], kf[r][tt], qf);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (HB == 2) mfma_settle(sc[0][0], sc[0][1], sc[HB - 1][0], sc[HB - 1][1]);
+      }
+
+      // 3. online softmax of each head column over rows 16 tt + 4 grp + r
+      f16x8 pb[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float sv[8];
+        float mx = kNoMax;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
+          sv[e] = tok < n_cur ? sc[hb][e >> 2][e & 3] * qs[hb] : -INFINITY;
+          mx = fmaxf(mx, sv[e]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (m[hb] == kNoMax)
+          m[hb] = mx;  // first tile with a valid token: nothing accumulated yet
+        else
+          over = over || mx > m[hb] + kHeadroom;
+        mseen[hb] = fmaxf(mseen[hb], mx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // the denominator sums the fp16-rounded values P.V multiplies
+          pb[hb][e] = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m[hb]);
+          l[hb] += (float)pb[hb][e];
         }
       }
 
-      // 3. online softmax of head `col` over rows 16 tt + 4 grp + r
-      float sv[8];
-      float mx = kNoMax;
+      // 4. O^T[dim][head] += V^T P^T over the 32 tokens; each V^T fragment
+      //    feeds every head block (reads kVAhead dim tiles ahead, as above)
+      {
+        f16x8 vf[kVAhead + 1];
+        auto vread = [&](int dt) -> f16x8 {
+          const f16x4 lo = lds_read_tr(kb + tr_off[0] + 16 * dt);
+          const f16x4 hi = lds_read_tr(kb + tr_off[1] + 16 * dt);
+          return (f16x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        };
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
-        sv[e] = tok < n_cur ? sc[e >> 2][e & 3] * qs : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m + kSlack) != 0, 0)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
+        for (int dt = 0; dt < kVAhead; ++dt) vf[dt] = vread(dt);
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) acc[dt] *= alpha;
-        m = mn;
-      }
-      f16x8 pb;
+        for (int dt = 0; dt < kDt; ++dt) {
+          if (dt + kVAhead < kDt) vf[(dt + kVAhead) % (kVAhead + 1)] = vread(dt + kVAhead);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // the denominator sums the fp16-rounded values P.V multiplies
-        pb[e] = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m);
-        l += (float)pb[e];
-      }
-
-      // 4. O^T[dim][head] += V^T P^T over the 32 tokens
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) {
-        const f16x4 lo = lds_read_tr(kb + tr_off[0] + 16 * dt);
-        const f16x4 hi = lds_read_tr(kb + tr_off[1] + 16 * dt);
-        const f16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[dt], 0, 0, 0);
+          for (int hb = 0; hb < HB; ++hb)
+            acc[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt % (kVAhead + 1)], pb[hb],
+                                                                 acc[hb][dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
       // 1. (next tile) staged into the other buffer
@@ -332,31 +460,50 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
       buf ^= 1;
       n_cur = n_nxt;
     }
-
-    // partial for slot (workgroup + sequence): lane holds head `col`,
-    // dims 16 dt + 4 grp + 0..3 in acc[dt]
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (head_ok) {
-      const long long slotp = ((long long)w + b) * a.hq + head;
-      float* dst = a.ws_o + slotp * kDv;
+    // workgroup-wide vote: every wave takes the same branch (the tile loop
+    // has workgroup barriers), and the next pass starts after this barrier,
+    // when every wave is done with both tile buffers
+    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // all lanes vote
+    if (lane == 0) st.vote[wave] = wave_over;
+    __syncthreads();
+    bool again = false;
 #pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * grp) = acc[dt];
-      if (grp == 0) {
-        a.ws_ml[slotp * 2] = m;
-        a.ws_ml[slotp * 2 + 1] = l;
+    for (int i = 0; i < NW; ++i) again = again || st.vote[i] != 0;
+    if (!again) break;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) m[hb] = mseen[hb];
+    }
+
+    // partial for slot (workgroup + sequence): lane holds head column `col`
+    // of each head block, dims 16 dt + 4 grp + 0..3 in acc[hb][dt]
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float lt = l[hb];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const int head = HW * wave + 16 * hb + col;
+      if (head < a.hq) {
+        const long long slotp = ((long long)w + b) * a.hq + head;
+        float* dst = a.ws_o + slotp * kDv;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt)
+          *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * grp) = acc[hb][dt];
+        if (grp == 0) {
+          a.ws_ml[slotp * 2] = m[hb];
+          a.ws_ml[slotp * 2 + 1] = lt;
+        }
       }
     }
   }
 }
 
-template <int NW>
+template <int NW, int HB>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(MlaLds);  // above the 64 KiB default: opt in
+  const size_t lds = HB == 2 ? sizeof(MlaLds2) : sizeof(MlaLds);  // above 64 KiB: opt in
   static std::atomic<unsigned long long> lds_set{0};
-  hipError_t e = allow_lds_once(lds_set, (const void*)decode_mla_kernel<NW>, lds);
+  hipError_t e = allow_lds_once(lds_set, (const void*)decode_mla_kernel<NW, HB>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_mla_kernel<NW>), dim3(a.nwg), dim3(64 * NW), lds, stream, a);
+  hipLaunchKernelGGL((decode_mla_kernel<NW, HB>), dim3(a.nwg), dim3(64 * NW), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -371,15 +518,21 @@ bool mla_supported(const Geom& g, int hq, int v_dim) {
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream) {
   if (!mla_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
   if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
+  // up to 64 heads: 16 a wave (one to four waves); more: 32 a wave (four),
+  // or with KVFP4_MLA_HB1 16 a wave (up to eight)
+#if KVFP4_MLA_HB1
+  if (a.hq > 112) return launch_nw<8, 1>(a, stream);
+  if (a.hq > 96) return launch_nw<7, 1>(a, stream);
+  if (a.hq > 80) return launch_nw<6, 1>(a, stream);
+  if (a.hq > 64) return launch_nw<5, 1>(a, stream);
+#else
+  if (a.hq > 64) return launch_nw<4, 2>(a, stream);
+#endif
   switch ((a.hq + 15) / 16) {
-    case 1: return launch_nw<1>(a, stream);
-    case 2: return launch_nw<2>(a, stream);
-    case 3: return launch_nw<3>(a, stream);
-    case 4: return launch_nw<4>(a, stream);
-    case 5: return launch_nw<5>(a, stream);
-    case 6: return launch_nw<6>(a, stream);
-    case 7: return launch_nw<7>(a, stream);
-    default: return launch_nw<8>(a, stream);
+    case 1: return launch_nw<1, 1>(a, stream);
+    case 2: return launch_nw<2, 1>(a, stream);
+    case 3: return launch_nw<3, 1>(a, stream);
+    default: return launch_nw<4, 1>(a, stream);
   }
 }
 

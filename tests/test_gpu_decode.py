@@ -348,3 +348,27 @@ def test_decode_full_size_sampled(name):
     # every output of the whole batch is finite and the merge produced an lse
     allo = (out.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.isfinite(allo)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("name", list(BAD_PAGES))
+def test_decode_late_dominant_score(name):
+    """A token near the end of a long sequence whose key equals a query row
+    scores far above every token before it (for MLA about 24 nats, past the
+    fp16 headroom of the first tiles' maximum): the kernels' running-maximum
+    updates (rescales, or a second pass over the segment) must give the
+    oracle's result; the head's output is then close to that token's value."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = BAD_PAGES[name]
+    lens = [6 * T + 7, 3 * T, 2 * T + 1]
+    wl = W.geometry_case(150 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    G = Hq // H
+    for b, h in [(0, 0), (2, Hq - 1)]:
+        # three quarters into the second-to-last page: a later tile of its
+        # page than the page's first (each workgroup may own a single page)
+        j = (-(-int(wl.seq_lens[b]) // T) - 2) * T + (3 * T) // 4
+        slot, row = int(wl.block_table[b, j // T]), j % T
+        wl.hot_pool[slot, 0, row, h // G] = wl.q[b, h]  # key row = query row
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=f"{name} late dominant score")
