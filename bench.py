@@ -5,15 +5,23 @@ One step = the whole hot path over one batch of synthetic input resident in
 HBM: encode the batch's bf16 K/V pages into the packed NVFP4 pool
 (kvfp4_quantize_pages), run single-token decode attention over the packed
 pool (kvfp4_paged_decode_attention, dequantizing in-kernel), and decode the
-pages back to bf16 (kvfp4_dequantize_pages).  Default workload: the
+pages back to bf16 (kvfp4_dequantize_pages).  Headline workload: the
 Llama-3-8B-shaped layer (batch 32, 32 q / 8 KV heads, head_dim 128, 8192
-tokens, 64-token pages in a seeded permutation; 4096 pages).
+tokens, 64-token pages in a seeded permutation; 4096 pages); the other four
+workloads are timed the same way and reported under ``workloads``.
 
-Timing: HIP events on the stream the kernels run on, around each kernel;
-between kernels an untimed 1 GiB read evicts the 256 MiB Infinity Cache so
-that bytes come from HBM (a read, so that no dirty lines are left to be
-written back inside the next timed kernel).  `value` is the step's algorithmic bytes divided
-by its kernel time.  Prints one JSON line.
+Timing (steady state): each leg runs K calls back to back on the stream,
+between one pair of HIP events, cycling over three copies of its buffers
+(as a model step cycles over its layers' caches).  A set's bytes were last
+touched two calls earlier, after more than the 256 MiB Infinity Cache of
+other traffic, so they come from HBM; a call also pays for writing back what
+the calls before it left dirty, as it does in a running server.  The
+per-call time is the block's time over K; an untimed 1 GiB read before each
+block writes back what the previous block left dirty.  Also reported, as
+``isolated``:
+single calls after an untimed 1 GiB read that evicts the caches, each
+between its own events.  ``value`` is the step's algorithmic bytes over the
+summed steady-state leg times.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -34,6 +42,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 COPY_CALLS = 4          # 1 GiB device copies timed as the practical ceiling
 COPY_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
+SETS = 3                # buffer copies each leg cycles over
+ISOLATED_CALLS = 10
+HEADLINE = "llama3_8b"
+WORKLOADS = ["tiny", "llama3_8b", "qwen3_8b_long", "cold_pages", "mla"]
 
 
 def parse():
@@ -41,24 +53,24 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama3_8b",
-                   choices=["tiny", "llama3_8b", "qwen3_8b_long", "mla", "cold_pages"])
+    p.add_argument("--workload", default=HEADLINE, choices=WORKLOADS,
+                   help="the workload whose step is the headline")
+    p.add_argument("--only", action="store_true",
+                   help="time only --workload (the other workloads are skipped)")
     p.add_argument("--gs", default="calibrated", choices=["calibrated", "unit"])
-    p.add_argument("--no-flush", action="store_true", help="do not evict caches between kernels")
-    p.add_argument("--flush-mode", default="read", choices=["read", "write"],
-                   help="evict caches by reading (default; leaves no dirty lines to be "
-                        "written back inside the next timed kernel) or writing 1 GiB")
+    p.add_argument("--no-isolated", action="store_true",
+                   help="skip the single-call (cache-evicted) timings")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="approximate host time budget of the oracle sample")
     p.add_argument("--no-copy-yardstick", action="store_true",
-                   help="skip timing a plain 1 GiB device copy (the practical HBM ceiling)")
+                   help="skip timing plain streams (the practical HBM ceilings)")
     p.add_argument("--extras-only", action="store_true",
                    help="time only the paths reported beside the step (no step, no JSON "
                         "metric line); for profiling those kernels on their own")
     p.add_argument("--no-append", action="store_true",
-                   help="skip timing the token-row paths (append-quantize, gather-dequantize), "
-                        "reported beside the step")
+                   help="skip timing the paths reported beside the step (append-quantize, "
+                        "gather-dequantize, host offload, RoPE layouts)")
     return p.parse_args()
 
 
@@ -98,10 +110,11 @@ YARDSTICK_KINDS = {"read": (0, 1.0), "write": (1, 1.0), "read4_write1": (2, 1.25
                    "read1_write4": (3, 1.25)}
 
 
-def stream_yardsticks(torch, src, dst, stream, evict, calls=COPY_CALLS):
+def stream_yardsticks(torch, src, dst, stream, calls=COPY_CALLS):
     """Plain streams of 1 GiB per traffic mix (libkvfp4_yardstick.so), timed
-    like the legs: cache eviction before each call, median after the first.
-    GB/s counts both directions (read 1 GiB + write 256 MiB for read4_write1)."""
+    like the legs: one untimed call, then `calls` back to back between one
+    pair of events.  GB/s counts both directions (read 1 GiB + write 256 MiB
+    for read4_write1)."""
     import ctypes
     lib_path = os.path.join(ROOT, "nvfp4_paged_decode_amd", "libkvfp4_yardstick.so")
     if not os.path.exists(lib_path):
@@ -114,25 +127,33 @@ def stream_yardsticks(torch, src, dst, stream, evict, calls=COPY_CALLS):
     nbytes = src.numel()
     out = {}
     for name, (kind, factor) in YARDSTICK_KINDS.items():
-        times = []
-        for _ in range(calls):
-            evict()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+        def call():
             rc = lib.kvfp4_yardstick(kind, src.data_ptr(), dst.data_ptr(), sink.data_ptr(), nbytes,
                                      ctypes.c_void_p(stream.cuda_stream))
-            e1.record(stream)
             if rc != 0:
                 raise RuntimeError(f"kvfp4_yardstick({name}) failed: {rc}")
-            times.append((e0, e1))
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
+        ms = time_block(torch, stream, [call], calls, 1)
         moved = factor * nbytes
-        out[name] = {"bytes": int(moved), "median_us": round(ms * 1e3, 2),
+        out[name] = {"bytes": int(moved), "avg_us": round(ms * 1e3, 2),
                      "GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
                      "frac_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return out
+
+
+def time_block(torch, stream, calls, k, warmup):
+    """Average ms of one call when `k` calls run back to back, cycling over
+    `calls` (one per buffer set), between one pair of events on `stream`."""
+    n = len(calls)
+    for i in range(warmup):
+        calls[i % n]()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(k):
+        calls[i % n]()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / k
 
 
 def time_append(K, torch, wl, geometry, gs, hot, packed, stream, evict, steps, warmup):
@@ -441,6 +462,162 @@ def cpu_baseline(wl, gs, budget_s: float, step_unit_bytes: dict, dec_bytes_per_t
             "seconds": round(q_s + dq_s + dec_s, 2)}
 
 
+class Legs:
+    """Device buffers and calls of one workload's three legs, over SETS
+    copies of the hot pool, the packed pool and the decoded pool."""
+
+    def __init__(self, K, torch, name, gs_kind):
+        from nvfp4_paged_decode_amd import workloads as W
+        t0 = time.perf_counter()
+        self.name = name
+        if name == "cold_pages":
+            cw = W.cold_pages()
+            self.wl = None
+            self.geometry = cw.geometry
+            self.gs = [float(v) for v in (cw.gs_calibrated if gs_kind == "calibrated"
+                                          else cw.gs_unit)]
+            host_pool = cw.hot_pool
+            self.pages = cw.num_pages
+            src, dst = cw.src_slots, cw.dst_slots
+            self.num_slots = cw.num_pages
+        else:
+            wl = W.FULL[name]()
+            self.wl = wl
+            self.geometry = wl.geometry
+            self.gs = [float(v) for v in (wl.gs_calibrated if gs_kind == "calibrated"
+                                          else wl.gs_unit)]
+            host_pool = wl.hot_pool
+            self.pages = int(wl.used_slots.shape[0])
+            src = dst = wl.used_slots.astype(np.int32)
+            self.num_slots = wl.num_slots
+        self.gen_s = time.perf_counter() - t0
+        dev = torch.device("cuda")
+        self.dev = dev
+        hot0 = torch.from_numpy(host_pool.view(np.int16)).to(dev)
+        self.hot = [hot0] + [hot0.clone() for _ in range(SETS - 1)]
+        self.src = torch.from_numpy(np.ascontiguousarray(src, np.int32)).to(dev)
+        self.dst = torch.from_numpy(np.ascontiguousarray(dst, np.int32)).to(dev)
+        pb = K.kvfp4_packed_page_bytes(self.geometry)
+        self.packed = [torch.zeros((self.num_slots, pb), dtype=torch.uint8, device=dev)
+                       for _ in range(SETS)]
+        self.back = [torch.empty_like(hot0) for _ in range(SETS)]
+        self.K = K
+        G, gs = self.geometry, self.gs
+        self.calls = {
+            "quantize": [lambda r=r: K.kvfp4_quantize_pages(G, self.hot[r], self.packed[r],
+                                                            self.pages, gs, self.src, self.dst)
+                         for r in range(SETS)],
+            "dequantize": [lambda r=r: K.kvfp4_dequantize_pages(G, self.packed[r], self.back[r],
+                                                                self.pages, gs, self.dst,
+                                                                self.src)
+                           for r in range(SETS)],
+        }
+        self.leg_bytes = {"quantize": codec_bytes(G, self.pages),
+                          "dequantize": codec_bytes(G, self.pages)}
+        if self.wl is not None:
+            wl = self.wl
+            self.q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
+            self.bt = torch.from_numpy(wl.block_table).to(dev)
+            self.sl = torch.from_numpy(wl.seq_lens).to(dev)
+            self.hint = int(wl.seq_lens.max())
+            ws_n = K.kvfp4_decode_workspace_bytes(G, wl.batch, wl.num_q_heads, wl.v_dim,
+                                                  self.hint)
+            self.ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+            self.out = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), dtype=torch.int16,
+                                   device=dev)
+            self.lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
+            self.calls["decode"] = [
+                lambda r=r: K.kvfp4_paged_decode_attention(G, self.packed[r], gs, self.q,
+                                                           self.bt, self.sl, self.hint,
+                                                           wl.softmax_scale, self.out, self.lse,
+                                                           self.ws, v_dim=wl.v_dim)
+                for r in range(SETS)]
+            self.db = decode_bytes(wl)
+            self.leg_bytes["decode"] = self.db["bytes"]
+        self.order = [k for k in ("quantize", "decode", "dequantize") if k in self.calls]
+
+    def describe(self) -> str:
+        if self.wl is None:
+            return (f"cold_pages: {self.pages} pages x {self.geometry} (tensors, tokens, heads, "
+                    f"dims); step = encode + decode of every page")
+        wl = self.wl
+        nt, T, H, D = self.geometry
+        return (f"{self.name}: batch {wl.batch}, {wl.num_q_heads} q / {H} KV heads, head_dim "
+                f"{D}, v_dim {wl.v_dim}, context {int(wl.seq_lens.min())}-"
+                f"{int(wl.seq_lens.max())} (sum {int(wl.seq_lens.sum())}), page {T}; step = "
+                f"encode {self.pages} pages + decode attention + decode {self.pages} pages")
+
+    def free(self):
+        for k in list(vars(self)):
+            if k not in ("name", "wl", "geometry", "gs", "pages", "leg_bytes", "db", "gen_s",
+                         "order", "num_slots"):
+                delattr(self, k)
+
+
+def leg_report(legs, name, ms, iso=None, mixes=None, copy=None) -> dict:
+    """Rates of one leg from its per-call time `ms` (and the isolated-call
+    figures `iso`, a list of ms)."""
+    b = legs.leg_bytes[name]
+    gbs = b / (ms * 1e-3) / 1e9
+    r = {"avg_us": round(ms * 1e3, 2), "bytes": b, "GB/s": round(gbs, 1),
+         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if mixes and LEG_MIX[name] in mixes:
+        r["frac_mix_yardstick"] = round(gbs / mixes[LEG_MIX[name]]["GB/s"], 4)
+    if copy is not None:
+        r["frac_copy_yardstick"] = round(gbs / copy["GB/s"], 4)
+    if name == "decode":
+        wl, t = legs.wl, ms * 1e-3
+        r["tokens_per_s"] = round(wl.batch / t, 1)
+        r["context_tokens_per_s"] = round(float(wl.seq_lens.sum()) / t, 1)
+        r["TFLOP/s"] = round(legs.db["flops"] / t / 1e12, 2)
+        r["frac_bf16_mfma_peak"] = round(legs.db["flops"] / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    if iso:
+        r["isolated"] = {"avg_us": round(float(np.mean(iso)) * 1e3, 2),
+                         "median_us": round(float(np.median(iso)) * 1e3, 2),
+                         "min_us": round(float(np.min(iso)) * 1e3, 2),
+                         "frac_hbm_peak": round(b / (float(np.mean(iso)) * 1e-3) / 1e9 /
+                                                HBM_PEAK_GBS, 4)}
+    from nvfp4_paged_decode_amd.profiling import read_traffic
+    traffic = read_traffic(os.path.join(PROFILES, f"counters_{legs.name}.txt"), legs.name, name)
+    if traffic is not None:
+        r["counter_traffic_bytes"] = traffic
+        r["traffic_over_algorithmic"] = round(traffic / b, 4)
+    return r
+
+
+def roofline_of(legs, kern: dict, leg: str) -> dict:
+    """Roofline of one leg: MLA decode against the dense 16-bit MFMA peak (a
+    dense contraction of about 820 flop per cache byte), the rest against
+    HBM."""
+    r = kern[leg]
+    traffic = r.get("counter_traffic_bytes")
+    if leg == "decode" and legs.name == "mla":
+        return {"kernel": leg, "bound": "mfma", "achieved": r["TFLOP/s"],
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": r["frac_bf16_mfma_peak"], "traffic": traffic}
+    return {"kernel": leg, "bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": r["frac_hbm_peak"], "traffic": traffic}
+
+
+def isolated_times(torch, stream, legs, evict, n) -> dict:
+    """Single calls after an untimed cache eviction, each between its own
+    events (the event marker before a call adds a few microseconds)."""
+    out = {}
+    for name in legs.order:
+        evs = []
+        for i in range(n):
+            evict()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            legs.calls[name][i % SETS]()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        out[name] = [a.elapsed_time(b) for a, b in evs]
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,228 +627,123 @@ def main():
 
     import torch
     import nvfp4_paged_decode_amd as K
-    from nvfp4_paged_decode_amd import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     K.load_library()
-
-    t_gen = time.perf_counter()
-    name = args.workload
-    if name == "cold_pages":
-        cw = W.cold_pages()
-        wl = None
-    else:
-        wl = W.FULL[name]()
-    t_gen = time.perf_counter() - t_gen
-
-    dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
-
-    if wl is not None:
-        geometry = wl.geometry
-        gs = [float(v) for v in (wl.gs_calibrated if args.gs == "calibrated" else wl.gs_unit)]
-        hot = torch.from_numpy(wl.hot_pool.view(np.int16)).to(dev)
-        pages = int(wl.used_slots.shape[0])
-        slots = torch.from_numpy(wl.used_slots.astype(np.int32)).to(dev)
-        num_slots = wl.num_slots
-    else:
-        geometry = cw.geometry
-        gs = [float(v) for v in (cw.gs_calibrated if args.gs == "calibrated" else cw.gs_unit)]
-        hot = torch.from_numpy(cw.hot_pool.view(np.int16)).to(dev)
-        pages = cw.num_pages
-        slots = torch.from_numpy(cw.src_slots).to(dev)
-        num_slots = cw.num_pages
-    pbytes = K.kvfp4_packed_page_bytes(geometry)
-    packed = torch.zeros((num_slots, pbytes), dtype=torch.uint8, device=dev)
-    hot_back = torch.empty_like(hot)
-    # fp32 in and out, so that the sum is one read-only reduction (an int32
-    # sum would first widen the whole buffer to int64 in a 2 GiB write)
+    dev = torch.device("cuda")
+    # fp32 in and out, so that the sum is one read-only reduction
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def evict():
-        # touch 1 GiB (4x the 256 MiB Infinity Cache) between timed kernels
-        if args.flush_mode == "read":
-            torch.sum(flush, dim=0, out=flush_sink)
-        else:
-            flush.fill_(1)
+        # read 1 GiB (4x the 256 MiB Infinity Cache); a read leaves no dirty lines
+        torch.sum(flush, dim=0, out=flush_sink)
 
-    if wl is not None:
-        q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
-        bt = torch.from_numpy(wl.block_table).to(dev)
-        sl = torch.from_numpy(wl.seq_lens).to(dev)
-        hint = int(wl.seq_lens.max())
-        ws_n = K.kvfp4_decode_workspace_bytes(geometry, wl.batch, wl.num_q_heads, wl.v_dim, hint)
-        ws = torch.empty(max(ws_n, 4), dtype=torch.uint8, device=dev)
-        out = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), dtype=torch.int16, device=dev)
-        lse = torch.empty((wl.batch, wl.num_q_heads), dtype=torch.float32, device=dev)
-
-    def k_quant():
-        K.kvfp4_quantize_pages(geometry, hot, packed, pages, gs, slots, slots)
-
-    def k_decode():
-        K.kvfp4_paged_decode_attention(geometry, packed, gs, q, bt, sl, hint, wl.softmax_scale,
-                                       out, lse, ws, v_dim=wl.v_dim)
-
-    def k_dequant():
-        K.kvfp4_dequantize_pages(geometry, packed, hot_back, pages, gs, slots, slots)
-
-    legs = [("quantize", k_quant)]
-    if wl is not None:
-        legs.append(("decode", k_decode))
-    legs.append(("dequantize", k_dequant))
-
-    def run(n_steps, timed):
-        ev = {k: [] for k, _ in legs}
-        for _ in range(n_steps):
-            for k, fn in legs:
-                if not args.no_flush:
-                    evict()
-                if timed:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    fn()
-                    e1.record(stream)
-                    ev[k].append((e0, e1))
-                else:
-                    fn()
-        return ev
-
-    def run_extras():
-        """The "next" paths, timed beside the step (never part of it)."""
-        ev = (lambda: None) if args.no_flush else evict
-        return {
-            "token_rows": time_append(K, torch, wl, geometry, gs, hot, packed, stream, ev,
-                                      args.steps, args.warmup),
-            "host_offload": time_offload(K, torch, wl, geometry, gs, hot, stream,
-                                         min(args.steps, 10), min(args.warmup, 2)),
-            "rope_layouts": time_rope_layouts(K, torch, wl, geometry, gs, hot, stream, ev,
-                                              min(args.steps, 10), min(args.warmup, 2)),
-        }
-
+    name = args.workload
     if args.extras_only:
-        if wl is None:
+        legs = Legs(K, torch, name, args.gs)
+        if legs.wl is None:
             print("--extras-only needs a decode workload", file=sys.stderr)
             sys.exit(2)
-        k_quant()  # the packed pool the gathers read
+        legs.calls["quantize"][0]()  # the packed pool the gathers read
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "extras-only", "workload": name, **run_extras()}), flush=True)
+        print(json.dumps({"mode": "extras-only", "workload": name,
+                          **run_extras(K, torch, legs, stream, evict, args)}), flush=True)
         return
 
-    copy = None
-    mixes = None
+    copy = mixes = None
     if not args.no_copy_yardstick:
-        # a plain device-to-device copy of 1 GiB: reads 1 GiB and writes 1 GiB
         src_c = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst_c = torch.empty_like(src_c)
-        times = []
-        for i in range(COPY_CALLS):
-            evict()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dst_c.copy_(src_c)
-            e1.record(stream)
-            times.append((e0, e1))
-        torch.cuda.synchronize()
-        ms_c = float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
-        copy = {"bytes": 2 * COPY_BYTES, "median_us": round(ms_c * 1e3, 2),
+        ms_c = time_block(torch, stream, [lambda: dst_c.copy_(src_c)], COPY_CALLS, 1)
+        copy = {"bytes": 2 * COPY_BYTES, "avg_us": round(ms_c * 1e3, 2),
                 "GB/s": round(2 * COPY_BYTES / (ms_c * 1e-3) / 1e9, 1)}
-        mixes = stream_yardsticks(torch, src_c, dst_c, stream, evict)
+        mixes = stream_yardsticks(torch, src_c, dst_c, stream)
         del src_c, dst_c
 
-    run(args.warmup, False)
+    # ---- the headline workload: K timed steps ---------------------------
+    legs = Legs(K, torch, name, args.gs)
+    for leg in legs.order:  # warm-up steps, untimed
+        for i in range(args.warmup):
+            legs.calls[leg][i % SETS]()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev = run(args.steps, True)
+    evs = {}
+    for leg in legs.order:
+        # the previous block's dirty lines are written back during this
+        # untimed read, not inside the next leg's first calls
+        evict()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            legs.calls[leg][i % SETS]()
+        e1.record(stream)
+        evs[leg] = (e0, e1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {k: [a.elapsed_time(b) for a, b in v] for k, v in ev.items()}
-    avg = {k: float(np.mean(v)) for k, v in ms.items()}
-    med = {k: float(np.median(v)) for k, v in ms.items()}
-    mn = {k: float(np.min(v)) for k, v in ms.items()}
-    step_ms = float(sum(avg.values()))
-
-    # warm figures (labelled as such, never the reported value): the same
-    # calls back to back with no eviction, so inputs may sit in the caches
-    warm = {}
-    if not args.no_flush:
-        ev_w = {k: [] for k, _ in legs}
-        for _ in range(min(args.steps, 5)):
-            for k, fn in legs:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                ev_w[k].append((e0, e1))
-        torch.cuda.synchronize()
-        warm = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev_w.items()}
-
-    cb = codec_bytes(geometry, pages)
-    leg_bytes = {"quantize": cb, "dequantize": cb}
-    kern = {}
-    if wl is not None:
-        db = decode_bytes(wl)
-        leg_bytes["decode"] = db["bytes"]
-    for k in leg_bytes:
-        gbs = leg_bytes[k] / (avg[k] * 1e-3) / 1e9
-        kern[k] = {"avg_us": round(avg[k] * 1e3, 2), "median_us": round(med[k] * 1e3, 2),
-                   "min_us": round(mn[k] * 1e3, 2),
-                   "bytes": leg_bytes[k], "GB/s": round(gbs, 1),
-                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-        if copy is not None:
-            kern[k]["frac_copy_yardstick"] = round(gbs / copy["GB/s"], 4)
-        if mixes and LEG_MIX[k] in mixes:
-            kern[k]["frac_mix_yardstick"] = round(gbs / mixes[LEG_MIX[k]]["GB/s"], 4)
-        if k in warm:
-            kern[k]["warm_avg_us_no_eviction"] = round(warm[k] * 1e3, 2)
-    if wl is not None:
-        t = avg["decode"] * 1e-3
-        kern["decode"]["tokens_per_s"] = round(wl.batch / t, 1)
-        kern["decode"]["context_tokens_per_s"] = round(float(wl.seq_lens.sum()) / t, 1)
-        kern["decode"]["TFLOP/s"] = round(db["flops"] / t / 1e12, 2)
-        kern["decode"]["frac_bf16_mfma_peak"] = round(db["flops"] / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
-    step_bytes = sum(leg_bytes.values())
+    ms = {k: a.elapsed_time(b) / args.steps for k, (a, b) in evs.items()}
+    iso = {} if args.no_isolated else isolated_times(torch, stream, legs, evict,
+                                                     min(args.steps, ISOLATED_CALLS))
+    kern = {k: leg_report(legs, k, ms[k], iso.get(k), mixes, copy) for k in legs.order}
+    step_ms = float(sum(ms.values()))
+    step_bytes = sum(legs.leg_bytes.values())
     value = step_bytes / (step_ms * 1e-3) / 1e9
-    dom = max(avg, key=avg.get)
-    from nvfp4_paged_decode_amd.profiling import read_traffic
-    traffic = read_traffic(os.path.join(PROFILES, f"counters_{name}.txt"), name, dom)
-    if dom == "decode" and name == "mla":
-        # 128 query heads over one latent: a dense bf16 contraction (about
-        # 820 flop per cache byte), bound by MFMA throughput, not HBM
-        roof = {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["TFLOP/s"],
-                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": kern[dom]["frac_bf16_mfma_peak"], "traffic": traffic}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB/s"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
-                "traffic": traffic}
+    dom = max(ms, key=ms.get)
+    roof = roofline_of(legs, kern, dom)
 
-    if wl is not None:
-        nt, T, H, D = geometry
-        wdesc = (f"{name}: batch {wl.batch}, {wl.num_q_heads} q / {H} KV heads, head_dim {D}, "
-                 f"v_dim {wl.v_dim}, context {int(wl.seq_lens.min())}-{int(wl.seq_lens.max())} "
-                 f"(sum {int(wl.seq_lens.sum())}), page {T}; step = encode {pages} pages + "
-                 f"decode attention + decode {pages} pages")
-    else:
-        wdesc = f"cold_pages: {pages} pages x {geometry}; step = encode + decode of every page"
-
-    extras = run_extras() if wl is not None and not args.no_append else {}
-    append = extras.get("token_rows")
-    offload = extras.get("host_offload")
-    rope = extras.get("rope_layouts")
-
+    extras = {}
+    if legs.wl is not None and not args.no_append:
+        extras = run_extras(K, torch, legs, stream, evict, args)
     cpu = None
-    if wl is not None and not args.no_cpu_baseline:
+    if legs.wl is not None and not args.no_cpu_baseline:
         try:
-            cpu = cpu_baseline(wl, gs, args.cpu_seconds, leg_bytes,
-                               db["bytes"] / float(wl.seq_lens.sum()), step_bytes)
+            cpu = cpu_baseline(legs.wl, legs.gs, args.cpu_seconds, legs.leg_bytes,
+                               legs.db["bytes"] / float(legs.wl.seq_lens.sum()), step_bytes)
         except Exception as e:  # the GPU figure stands on its own
             cpu = {"error": repr(e)}
+    wdesc = legs.describe()
+    wl = legs.wl
+    gen_s = legs.gen_s
+    legs.free()
+    del legs
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads, timed the same way ------------------------
+    others = {}
+    if not args.only:
+        for other in WORKLOADS:
+            if other == name:
+                continue
+            lo = Legs(K, torch, other, args.gs)
+            ms_o = {}
+            for leg in lo.order:
+                evict()
+                ms_o[leg] = time_block(torch, stream, lo.calls[leg], args.steps, args.warmup)
+            iso_o = {} if args.no_isolated else isolated_times(torch, stream, lo, evict,
+                                                               min(args.steps, ISOLATED_CALLS))
+            k_o = {k: leg_report(lo, k, ms_o[k], iso_o.get(k), mixes, copy) for k in lo.order}
+            d = {"workload": lo.describe(), "legs": k_o,
+                 "step_GB/s": round(sum(lo.leg_bytes.values()) /
+                                    (sum(ms_o.values()) * 1e-3) / 1e9, 1)}
+            if "decode" in k_o:
+                d["roofline_decode"] = roofline_of(lo, k_o, "decode")
+            d["roofline_quantize"] = roofline_of(lo, k_o, "quantize")
+            d["roofline_dequantize"] = roofline_of(lo, k_o, "dequantize")
+            others[other] = d
+            gen_s += lo.gen_s
+            lo.free()
+            del lo
+            torch.cuda.empty_cache()
+
+    def summary(leg):
+        r = kern.get(leg)
+        if r is None:
+            return None
+        return {"avg_us": r["avg_us"], "GB/s": r["GB/s"], "frac_hbm_peak": r["frac_hbm_peak"]}
 
     line = {
         "metric": "NVFP4-KV decode attn effective HBM GB/s (% peak) + page quant/dequant GB/s",
@@ -680,22 +752,42 @@ def main():
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16<->nvfp4 codec (integer thresholds); attention fp16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded)",
-        "config": {"workload": wdesc, "global_scale": args.gs, "cache_flush_between_kernels":
-                   "none" if args.no_flush else args.flush_mode + " 1 GiB", "global_batch": wl.batch if wl is not None else None,
+        "config": {"workload": wdesc, "global_scale": args.gs,
+                   "value": "the step's algorithmic bytes (encode + decode attention + decode "
+                            "of the batch) over the summed steady-state leg times; per-leg "
+                            "rates below",
+                   "timing": f"steady state: {args.steps} calls per leg back to back over "
+                             f"{SETS} buffer copies, one event pair per leg",
+                   "global_batch": wl.batch if wl is not None else None,
                    "seq_len": int(wl.seq_lens.max()) if wl is not None else None,
                    "parallelism": "single GPU"},
+        "decode_attention": summary("decode"),
+        "page_quantize": summary("quantize"),
+        "page_dequantize": summary("dequantize"),
         "kernels": kern,
-        "copy_yardstick": copy,
-        "stream_yardsticks": mixes,
-        "token_rows": append,
-        "host_offload": offload,
-        "rope_layouts": rope,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "workloads": others,
+        "copy_yardstick": copy,
+        "stream_yardsticks": mixes,
+        **extras,
         "wall_s_timed_region": round(wall, 3),
-        "gen_s": round(t_gen, 1),
+        "gen_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def run_extras(K, torch, legs, stream, evict, args) -> dict:
+    """The "next" paths, timed beside the step (never part of it)."""
+    wl, G, gs = legs.wl, legs.geometry, legs.gs
+    return {
+        "token_rows": time_append(K, torch, wl, G, gs, legs.hot[0], legs.packed[0], stream,
+                                  evict, args.steps, args.warmup),
+        "host_offload": time_offload(K, torch, wl, G, gs, legs.hot[0], stream,
+                                     min(args.steps, 10), min(args.warmup, 2)),
+        "rope_layouts": time_rope_layouts(K, torch, wl, G, gs, legs.hot[0], stream, evict,
+                                          min(args.steps, 10), min(args.warmup, 2)),
+    }
 
 
 if __name__ == "__main__":

@@ -43,6 +43,8 @@
 //     transposed copy is made.
 // The wave's unnormalized partial (O, max, sum) goes to workspace slot
 // (workgroup + sequence); merge_balanced_kernel combines them.
+#include <type_traits>
+
 #include "common.hpp"
 #include "decode_plan.hpp"
 
@@ -69,8 +71,20 @@ constexpr float kHeadroom = 15.f;  // p = 2^(s - m) <= 2^15 stays finite in fp16
 #ifndef KVFP4_MLA_HB1  // 1: 16 heads a wave above 64 heads (eight waves)
 #define KVFP4_MLA_HB1 0
 #endif
-constexpr int kKAhead = 2;         // k-steps of K fragments read ahead of the products
-constexpr int kVAhead = 3;         // dim tiles of V^T fragments read ahead
+#ifndef KVFP4_MLA_KA
+#define KVFP4_MLA_KA 2
+#endif
+#ifndef KVFP4_MLA_VA
+#define KVFP4_MLA_VA 3
+#endif
+#ifndef KVFP4_MLA_PVSB  // 1: a scheduling barrier after each P.V dim tile
+#define KVFP4_MLA_PVSB 1
+#endif
+#ifndef KVFP4_MLA_PVSPLIT  // 1: P.V of head block 0, then of head block 1
+#define KVFP4_MLA_PVSPLIT 0
+#endif
+constexpr int kKAhead = KVFP4_MLA_KA;  // k-steps of K fragments read ahead of the products
+constexpr int kVAhead = KVFP4_MLA_VA;  // dim tiles of V^T fragments read ahead
 
 struct MlaLds {
   _Float16 k[2][kTile][kPitch];  // double-buffered natural latent tiles
@@ -122,14 +136,14 @@ __device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
 // states cover the VALU-read latency of an 8-pass XDL product).
 __device__ inline f32x4 mfma_v0(const f16x8& a, const f16x8& b) {
   f32x4 d;
-  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 __device__ inline void mfma_v(f32x4& c, const f16x8& a, const f16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
 __device__ inline void mfma_settle(f32x4& a, f32x4& b, f32x4& c, f32x4& d) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
 __device__ inline f16x4 lds_read_tr(const _Float16* p) {
@@ -196,6 +210,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     const int row = 16 * h + 4 * grp + q4;
     tr_off[h] = row * kPitch + 8 * ((j4 >> 1) ^ sw) + 4 * (j4 & 1);
   }
+  // LDS element offset of each of this thread's staging rounds (see
+  // stage_piece below)
+  int st_off[Prefetch<NW>::kPer];
+#pragma unroll
+  for (int u = 0; u < Prefetch<NW>::kPer; ++u) {
+    const unsigned hi = tid + NT * u, t = hi / (2 * kBlocks);
+    st_off[u] = chunk_at((int)t, (int)(hi - t * (2 * kBlocks)));
+  }
+
   BalancedRange rng;
   balanced_range(a, w, nwg, rng);
   note_total(a, w, rng.ptot);
@@ -216,36 +239,45 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     const int t_end = (L + kTile - 1) / kTile;
     if (t_hi > t_end) t_hi = t_end;
 
-    // page-table entries of pages c0 .. c0+63, one per lane
-    const int32_t* bt_row = a.block_table + (long long)b * a.max_pages;
-    int c0 = -(1 << 30);
-    int slot_vec = -1;
-    auto slot_of = [&](int pg) -> int {
-      if (pg < c0 || pg >= c0 + 64) {
-        c0 = pg;
-        slot_vec = (c0 + lane < (int)p_hi) ? bt_row[c0 + lane] : -1;
-      }
-      return __builtin_amdgcn_readlane(slot_vec, pg - c0);
+    // Page-table entries are read with scalar loads (a uniform address in
+    // the constant address space): their wait is then on the scalar/LDS
+    // counter, not on the vector-memory counter that also tracks the tile
+    // loads, so reading an entry never waits for tiles in flight.  A page's
+    // entry is requested one request ahead of its use.
+    typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+    const ConstI32 bt_row = (ConstI32)(a.block_table + (long long)b * a.max_pages);
+    auto slot_load = [&](int pg) -> int {  // -1 past the segment
+      const int e = bt_row[pg < (int)p_hi ? pg : (int)p_hi - 1];
+      return pg < (int)p_hi ? e : -1;
     };
     auto rows_of = [&](int slot, int ti) -> int {
       int n = L - ti * kTile;
       n = n > kTile ? kTile : n;
       if (slot < 0 || slot >= a.pool_pages) n = 0;
-      return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
+      return n < 0 ? 0 : n;
     };
 
-    // rows past the sequence end (or a whole tile of a bad page) read as
-    // zero through the buffer resources' bounds
-    Prefetch<NW> pre;
-    // the next tile to request, as (page, tile within the page)
-    int nx_pg = (int)p_lo, nx_tip = 0;
-    auto issue = [&](int ti) -> int {
-      const int slot = slot_of(nx_pg);
+    // Packed bytes of tile t are requested two tiles ahead, into one of two
+    // register sets, and staged into LDS (dequantized) while tile t - 1 is
+    // being scored; rows past the sequence end (or a whole tile of a bad
+    // page) read as zero through the buffer resources' bounds.
+    Prefetch<NW> pre[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) pre[i].d[u] = pre[i].s[u] = 0u;
+    // the next tile to request, as (page, tile within the page), and the
+    // page's slot; tiles past the segment get slot -1 (no rows: the loads
+    // read zero and fetch nothing), so the request is made every tile
+    int nx_pg = (int)p_lo, nx_tip = 0, nx_slot = -1;
+    auto issue = [&](Prefetch<NW>& pf, int ti) -> int {
+      const int slot = nx_slot;
       const int n = rows_of(slot, ti);
       const int row0 = nx_tip * kTile;
       if (++nx_tip == tiles_per_page) {
         nx_tip = 0;
         ++nx_pg;
+        nx_slot = slot_load(nx_pg);
       }
       const uint8_t* page = a.pool + (long long)(n > 0 ? slot : 0) * page_bytes;
       auto rd = __builtin_amdgcn_make_buffer_rsrc((void*)(page + (long long)row0 * kRowData),
@@ -260,27 +292,39 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
         // zero, nothing fetched
         const int hi = tid + NT * u;
         const bool in = Prefetch<NW>::kEven || hi < kHalf;
-        pre.d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, in ? 4 * tid : 1 << 28, 4 * NT * u, 0);
-        pre.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? tid >> 1 : 1 << 28, NT * u / 2, 0);
+        pf.d[u] = __builtin_amdgcn_raw_buffer_load_b32(rd, in ? 4 * tid : 1 << 28, 4 * NT * u, 0);
+        pf.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, in ? tid >> 1 : 1 << 28, NT * u / 2, 0);
       }
       return n;
     };
-    auto stage = [&](int buf) {
-      _Float16* base = &st.k[buf][0][0];
-      // recomputed per tile (a few integer ops) rather than kept: the empty
-      // asm stops the compiler from hoisting kPer offsets out of the loop,
-      // which it would then spill
-      int tid_l = tid;
-      asm volatile("" : "+v"(tid_l));
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int hi = tid_l + NT * u;
-        if (!Prefetch<NW>::kEven && hi >= kHalf) continue;
-        const int t = hi / (2 * kBlocks), c = hi - t * (2 * kBlocks);
-        const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pre.s[u], 1.0f, false);
-        const _Float16 sb = sp[0];
-        *reinterpret_cast<f16x8*>(base + chunk_at(t, c)) = dequant8(pre.d[u], sb);
+    // Staging of half-block round u of the tile held in pf into LDS buffer
+    // buf.  Round u of this thread is chunk c of row t with (t, c) =
+    // divmod(tid + NT u, 72): its LDS offset is computed once per
+    // workgroup (st_off).  The work of one round is split into pieces 0..5
+    // so that the score loop can spread it between its MFMAs: 0 the block
+    // scale, 1..4 a pair of codes each, 5 the 16-byte store.
+    struct Stager {
+      _Float16 sb;
+      f16x8 v;
+    };
+    auto stager_start = [&]() -> Stager { return Stager{}; };
+    auto stage_piece = [&](const Prefetch<NW>& pf, int u, int piece, int buf, Stager& g) {
+      if (!Prefetch<NW>::kEven && tid + NT * u >= kHalf) return;
+      if (piece == 0) {
+        const f16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pf.s[u], 1.0f, false);
+        g.sb = sp[0];
+      } else if (piece <= 4) {
+        const f16x2 s2 = {g.sb, g.sb};
+        const f16x2 h = fp4x2(pf.d[u], piece - 1) * s2;
+        g.v[2 * (piece - 1)] = h.x;
+        g.v[2 * (piece - 1) + 1] = h.y;
+      } else {
+        *reinterpret_cast<f16x8*>(&st.k[buf][0][0] + st_off[u]) = g.v;
       }
+    };
+    auto stage_one = [&](const Prefetch<NW>& pf, int u, int buf, Stager& g) {
+#pragma unroll
+      for (int piece = 0; piece < 6; ++piece) stage_piece(pf, u, piece, buf, g);
     };
 
     // queries of this wave's heads (B operand of the scores): for head block
@@ -330,44 +374,54 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
       qs[hb] = ldexpf(base_scale, -sh);
     }
 
-    // Softmax without rescaling the accumulators: a column's maximum m is
-    // fixed by its first tile with a valid token, and the probabilities
-    // 2^(s - m) of later tiles are used as they are while s - m stays within
-    // kHeadroom (fp16 holds them).  A later score beyond that makes the
-    // whole workgroup compute the segment again with m = the maximum over
-    // the segment seen in the first pass (a workgroup-wide vote at the end
-    // of the pass), after which no score exceeds m.  The accumulators are
-    // therefore only ever zeroed or written by MFMA.
+    // Softmax without rescaling the accumulators.  Pass 0: a column's
+    // maximum m is fixed by its first tile with a valid token, and the
+    // probabilities 2^(s - m) of later tiles are used as they are; fp16
+    // holds them up to 65504, and a larger one becomes inf, which makes the
+    // column's sum l non-finite.  If any column of the workgroup ends the
+    // pass so, pass 1 computes only the scores and the maximum of every
+    // column over the segment, and pass 2 repeats pass 0 with that maximum,
+    // where no probability exceeds 1.  The accumulators are therefore only
+    // ever zeroed or written by MFMA.
     f32x4 acc[HB][kDt];
-    float m[HB], l[HB], mseen[HB];
+    float m[HB], l[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) m[hb] = kNoMax;
-    for (;;) {
+    for (int mode = 0;;) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) acc[hb][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       l[hb] = 0.f;
-      mseen[hb] = m[hb];
+      if (mode == 1) m[hb] = kNoMax;
     }
-    bool over = false;
     nx_pg = (int)p_lo;
     nx_tip = 0;
-    int n_cur = issue(t_lo);
-    stage(0);
+    nx_slot = slot_load(nx_pg);
+    int n_cur = issue(pre[0], t_lo);
+    int n_nxt = issue(pre[1], t_lo + 1);
+    {
+      Stager g = stager_start();
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) stage_one(pre[0], u, 0, g);
+    }
     __syncthreads();
-    int buf = 0;
-    for (int ti = t_lo; ti < t_hi; ++ti) {
-      const bool more = ti + 1 < t_hi;
-      int n_nxt = 0;
-      if (more) n_nxt = issue(ti + 1);
-      const _Float16* kb = &st.k[buf][0][0];
 
-      // 2. scores S^T[token][head] per 16-token half and head block; each
-      //    K fragment read from LDS feeds every head block.  Reads run
-      //    kKAhead k-steps ahead of the products through a small ring, so
-      //    only that many fragments are live (the scheduling barriers keep
-      //    the compiler from hoisting all 36 reads, which spills)
+    // One tile: `nextp` holds the next tile's bytes (staged into the other
+    // buffer during the score products), `freep` receives the tile after it.
+    auto tile = [&](int ti, Prefetch<NW>& nextp, Prefetch<NW>& freep, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;  // LDS buffer of this tile
+      const int n_nn = issue(freep, ti + 2);
+      const _Float16* kb = &st.k[buf][0][0];
+      Stager g = stager_start();
+
+      // scores S^T[token][head] per 16-token half and head block; each K
+      // fragment read from LDS feeds every head block.  Reads run kKAhead
+      // k-steps ahead of the products through a small ring; the next tile's
+      // staging is spread over the k-steps (a round of half-blocks every
+      // k-step or two), so its VALU work runs while the MFMAs do; the
+      // scheduling barriers keep that interleave and stop the compiler from
+      // hoisting all 36 reads, which spills.
       f32x4 sc[HB][2];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) sc[hb][0] = sc[hb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -387,91 +441,165 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
         for (int ks = 0; ks < kKs; ++ks) {
           if (ks + kKAhead < kKs) kread(ks + kKAhead, kf[(ks + kKAhead) % (kKAhead + 1)]);
           const int r = ks % (kKAhead + 1);
+          if constexpr (HB == 2 && kPer * 2 == kKs) {
+            // one staging round every two k-steps, its six pieces placed
+            // after the first six of the eight products, each MFMA and its
+            // piece in a scheduling group of their own (the VALU piece then
+            // issues while the MFMA runs)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
+            for (int i = 0; i < 4; ++i) {
+              const int tt = i >> 1, hb = i & 1;
               const f16x8& qf = hb == 0 ? qb[ks] : kf[r][HB];
-              if (HB == 1)
-                sc[hb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[r][tt], qf, sc[hb][tt],
-                                                                    0, 0, 0);
-              else if (ks == 0)
+              if (ks == 0)
                 sc[hb][tt] = mfma_v0(kf[r][tt], qf);
               else
                 mfma_v(sc[hb][tt], kf[r][tt], qf);
+              const int piece = 4 * (ks & 1) + i;
+              if (piece < 6) stage_piece(nextp, ks >> 1, piece, buf ^ 1, g);
+              __builtin_amdgcn_sched_barrier(0);
             }
-          __builtin_amdgcn_sched_barrier(0);
+          } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int hb = 0; hb < HB; ++hb) {
+                const f16x8& qf = hb == 0 ? qb[ks] : kf[r][HB];
+                if (HB == 1)
+                  sc[hb][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[r][tt], qf, sc[hb][tt],
+                                                                      0, 0, 0);
+                else if (ks == 0)
+                  sc[hb][tt] = mfma_v0(kf[r][tt], qf);
+                else
+                  mfma_v(sc[hb][tt], kf[r][tt], qf);
+              }
+            // rounds [ks kPer / kKs, (ks + 1) kPer / kKs) of the next tile
+#pragma unroll
+            for (int u = ks * kPer / kKs; u < (ks + 1) * kPer / kKs; ++u)
+              stage_one(nextp, u, buf ^ 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         if (HB == 2) mfma_settle(sc[0][0], sc[0][1], sc[HB - 1][0], sc[HB - 1][1]);
       }
 
-      // 3. online softmax of each head column over rows 16 tt + 4 grp + r
-      f16x8 pb[HB];
+      // softmax of each head column over rows 16 tt + 4 grp + r.  A column
+      // maximum is needed on every tile of pass 1, and in passes 0 and 2 on
+      // the tiles until a column has seen a valid token (rare: first).
+      const bool full = n_cur >= kTile;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        float sv[8];
-        float mx = kNoMax;
+        if (mode == 1 || __builtin_amdgcn_ballot_w64(m[hb] == kNoMax) != 0) {
+          float mx = kNoMax;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
-          sv[e] = tok < n_cur ? sc[hb][e >> 2][e & 3] * qs[hb] : -INFINITY;
-          mx = fmaxf(mx, sv[e]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (m[hb] == kNoMax)
-          m[hb] = mx;  // first tile with a valid token: nothing accumulated yet
-        else
-          over = over || mx > m[hb] + kHeadroom;
-        mseen[hb] = fmaxf(mseen[hb], mx);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // the denominator sums the fp16-rounded values P.V multiplies
-          pb[hb][e] = (_Float16)__builtin_amdgcn_exp2f(sv[e] - m[hb]);
-          l[hb] += (float)pb[hb][e];
+          for (int e = 0; e < 8; ++e) {
+            const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
+            if (tok < n_cur) mx = fmaxf(mx, sc[hb][e >> 2][e & 3] * qs[hb]);
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          m[hb] = (mode == 1 || m[hb] == kNoMax) ? fmaxf(m[hb], mx) : m[hb];
         }
       }
 
-      // 4. O^T[dim][head] += V^T P^T over the 32 tokens; each V^T fragment
-      //    feeds every head block (reads kVAhead dim tiles ahead, as above)
-      {
+      // P.V: O^T[dim][head] += V^T P^T over the 32 tokens, head block 0 then
+      // head block 1 (each V^T fragment is read once per head block; LDS has
+      // the bandwidth), so that head block 1's probabilities are computed
+      // between head block 0's products, beside its MFMAs.  Fragments are
+      // read kVAhead dim tiles ahead.
+      if (mode != 1) {
+        f16x8 pb[HB];
+        const f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+        // probabilities e, e + 1 of head block hb: 2^(s - m) rounded to fp16
+        auto probs = [&](int hb, int e, bool partial) {
+          float x0 = fmaf(sc[hb][e >> 2][e & 3], qs[hb], -m[hb]);
+          float x1 = fmaf(sc[hb][e >> 2][(e & 3) + 1], qs[hb], -m[hb]);
+          if (partial) {
+            const int tok = 16 * (e >> 2) + 4 * grp + (e & 3);
+            x0 = tok < n_cur ? x0 : -INFINITY;
+            x1 = tok + 1 < n_cur ? x1 : -INFINITY;
+          }
+          const f16x2 p2 = {(_Float16)__builtin_amdgcn_exp2f(x0),
+                            (_Float16)__builtin_amdgcn_exp2f(x1)};
+          pb[hb][e] = p2.x;
+          pb[hb][e + 1] = p2.y;
+          // the denominator sums the fp16-rounded values P.V multiplies
+          l[hb] = __builtin_amdgcn_fdot2(p2, one2, l[hb], false);
+        };
+        // (a uniform branch: the masking of rows past the sequence end only
+        // on the sequence's last tile)
+        if (full) {
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) probs(hb, e, false);
+        } else {
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) probs(hb, e, true);
+        }
         f16x8 vf[kVAhead + 1];
         auto vread = [&](int dt) -> f16x8 {
           const f16x4 lo = lds_read_tr(kb + tr_off[0] + 16 * dt);
           const f16x4 hi = lds_read_tr(kb + tr_off[1] + 16 * dt);
           return (f16x8){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         };
+        if (KVFP4_MLA_PVSPLIT) {
 #pragma unroll
-        for (int dt = 0; dt < kVAhead; ++dt) vf[dt] = vread(dt);
+          for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          if (dt + kVAhead < kDt) vf[(dt + kVAhead) % (kVAhead + 1)] = vread(dt + kVAhead);
+            for (int dt = 0; dt < kVAhead; ++dt) vf[dt] = vread(dt);
 #pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-            acc[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt % (kVAhead + 1)], pb[hb],
-                                                                 acc[hb][dt], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+            for (int dt = 0; dt < kDt; ++dt) {
+              if (dt + kVAhead < kDt) vf[(dt + kVAhead) % (kVAhead + 1)] = vread(dt + kVAhead);
+              acc[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  vf[dt % (kVAhead + 1)], pb[hb], acc[hb][dt], 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < kVAhead; ++dt) vf[dt] = vread(dt);
+#pragma unroll
+          for (int dt = 0; dt < kDt; ++dt) {
+            if (dt + kVAhead < kDt) vf[(dt + kVAhead) % (kVAhead + 1)] = vread(dt + kVAhead);
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+              acc[hb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  vf[dt % (kVAhead + 1)], pb[hb], acc[hb][dt], 0, 0, 0);
+            if (KVFP4_MLA_PVSB) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-
-      // 1. (next tile) staged into the other buffer
-      if (more) stage(buf ^ 1);
+      // every wave is done with this tile's buffer, and the next tile is
+      // staged in the other
       __syncthreads();
-      buf ^= 1;
       n_cur = n_nxt;
+      n_nxt = n_nn;
+    };
+    for (int ti = t_lo; ti < t_hi; ti += 2) {
+      tile(ti, pre[1], pre[0], std::integral_constant<int, 0>{});
+      if (ti + 1 < t_hi) tile(ti + 1, pre[0], pre[1], std::integral_constant<int, 1>{});
     }
-    // workgroup-wide vote: every wave takes the same branch (the tile loop
-    // has workgroup barriers), and the next pass starts after this barrier,
-    // when every wave is done with both tile buffers
-    const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;  // all lanes vote
-    if (lane == 0) st.vote[wave] = wave_over;
+    if (mode == 1) {
+      mode = 2;
+      continue;
+    }
+    if (mode == 2) break;
+    // pass 0 done: a workgroup-wide vote on whether any column overflowed
+    // (every wave takes the same branch; the next pass starts after this
+    // barrier, when every wave is done with both tile buffers)
+    bool bad = false;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) bad = bad || !(fabsf(l[hb]) <= 3.0e38f);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;  // all lanes vote
+    if (lane == 0) st.vote[wave] = wave_bad;
     __syncthreads();
     bool again = false;
 #pragma unroll
     for (int i = 0; i < NW; ++i) again = again || st.vote[i] != 0;
     if (!again) break;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) m[hb] = mseen[hb];
+    mode = 1;
     }
 
     // partial for slot (workgroup + sequence): lane holds head column `col`

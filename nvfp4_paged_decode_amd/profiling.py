@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the kernels of this library.
 
-Two commands, each printing a short text summary (to stdout or --out):
+Three commands, each printing a short text summary (to stdout or --out):
 
   python -m nvfp4_paged_decode_amd.profiling stats DIR [--command TEXT]
       per-kernel dispatch count and average/min/max duration from a
@@ -16,6 +16,12 @@ Two commands, each printing a short text summary (to stdout or --out):
       summary ends with one `traffic` line per benchmark leg, which bench.py
       reads back together with the digest of that leg's kernel sources the
       counters were taken on (a figure for other sources is not reported).
+
+  python -m nvfp4_paged_decode_amd.profiling pmc DIR [DIR ...] [--command TEXT]
+      per-kernel wave occupancy and issue picture from `rocprofv3 --pmc`
+      runs of the PMC_PASSES counter sets: shares of wave-cycles waiting,
+      issuing, on VALU and on LDS, MFMA-busy share of all SIMDs, and LDS
+      cycles lost to bank conflicts.
 """
 
 from __future__ import annotations
@@ -141,6 +147,81 @@ def counters(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> 
     return out
 
 
+#: Counter passes for the occupancy / issue picture of each kernel.  One
+#: rocprofv3 --pmc run per pass (the SQ block collects at most 8 counters in
+#: a run, GRBM 2).
+PMC_PASSES = (
+    ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+     "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+    ("SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_LDS",
+     "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_ACTIVE_INST_VMEM", "SQ_INST_CYCLES_VMEM_RD",
+     "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"),
+)
+
+#: SIMDs of an MI355X (256 CUs x 4), the denominator of MFMA busy cycles,
+#: and its XCDs: rocprofv3 sums GRBM_GUI_ACTIVE over the 8 XCDs, so the
+#: kernel's own cycle count is that sum over 8
+SIMDS = 1024
+XCDS = 8
+
+
+def _all_counters(d: str) -> dict[str, dict[str, list[float]]]:
+    """kernel -> counter -> per-dispatch values, from one --pmc run."""
+    per: dict = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        per[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def pmc(dirs: list[str], kernels_prefix=("decode_", "merge_", "quantize_", "dequantize_")):
+    """Per-kernel averages of the PMC_PASSES counters (one directory per
+    pass) and the fractions derived from them:
+
+    wait%   SQ_WAIT_ANY / SQ_WAVE_CYCLES  (wave-cycles spent waiting on anything)
+    issue%  SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES  (wave-cycles issuing)
+    valu%   SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES
+    lds%    SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES
+    mfma%   SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024
+            SIMDs): MFMA pipes busy, as a share of every SIMD over the
+            kernel's cycles
+    bank%   SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS  (LDS cycles lost to
+            bank conflicts per LDS-active cycle)
+    """
+    merged: dict = collections.defaultdict(dict)
+    for d in dirs:
+        for k, cs in _all_counters(d).items():
+            for c, vals in cs.items():
+                merged[k].setdefault(c, vals)
+    out = [f"{'kernel':<40} {'disp':>4} {'wait%':>6} {'issue%':>6} {'valu%':>6} {'lds%':>6} "
+           f"{'mfma%':>6} {'bank%':>6} {'waves':>8} {'gui_cyc':>9}"]
+
+    def avg(cs, c):
+        v = cs.get(c)
+        return sum(v) / len(v) if v else None
+
+    def pct(a, b):
+        return f"{100.0 * a / b:6.1f}" if a is not None and b else f"{'-':>6}"
+
+    raw = []
+    for k in sorted(merged):
+        if not k.startswith(kernels_prefix):
+            continue
+        cs = merged[k]
+        wc = avg(cs, "SQ_WAVE_CYCLES")
+        gui = avg(cs, "GRBM_GUI_ACTIVE")
+        n = max(len(v) for v in cs.values())
+        mfma_den = gui / XCDS * SIMDS if gui else None
+        out.append(f"{k[:40]:<40} {n:>4} {pct(avg(cs, 'SQ_WAIT_ANY'), wc)} "
+                   f"{pct(avg(cs, 'SQ_ACTIVE_INST_ANY'), wc)} "
+                   f"{pct(avg(cs, 'SQ_ACTIVE_INST_VALU'), wc)} "
+                   f"{pct(avg(cs, 'SQ_ACTIVE_INST_LDS'), wc)} "
+                   f"{pct(avg(cs, 'SQ_VALU_MFMA_BUSY_CYCLES'), mfma_den)} "
+                   f"{pct(avg(cs, 'SQ_LDS_BANK_CONFLICT'), avg(cs, 'SQ_ACTIVE_INST_LDS'))} "
+                   f"{(avg(cs, 'SQ_WAVES') or 0):>8.0f} {(gui or 0):>9.0f}")
+        raw.append(f"raw {k}: " + " ".join(f"{c}={avg(cs, c):.0f}" for c in sorted(cs)))
+    return out + [""] + raw
+
+
 def read_traffic(path: str, workload: str, leg: str) -> int | None:
     """Total HBM bytes per call of `leg`, if `path` holds a figure taken on
     the current kernel sources for this workload; else None."""
@@ -166,11 +247,18 @@ def main(argv=None):
     c.add_argument("--write", required=True)
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--workload", required=True)
-    for q in (s, c):
+    m = sub.add_parser("pmc")
+    m.add_argument("dirs", nargs="+", help="one rocprofv3 --pmc output directory per pass")
+    for q in (s, c, m):
         q.add_argument("--command", default="", help="the command(s) that produced DIR")
         q.add_argument("--out")
     a = p.parse_args(argv)
-    lines = stats(a.dir) if a.cmd == "stats" else counters(a.fetch, a.write, a.copy_bytes, a.workload)
+    if a.cmd == "stats":
+        lines = stats(a.dir)
+    elif a.cmd == "pmc":
+        lines = pmc(a.dirs)
+    else:
+        lines = counters(a.fetch, a.write, a.copy_bytes, a.workload)
     head = [f"# {l}" for l in a.command.splitlines() if l.strip()]
     text = "\n".join(head + [""] + lines if head else lines) + "\n"
     if a.out:

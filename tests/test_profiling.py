@@ -61,3 +61,29 @@ def test_names_outside_the_library_namespace_are_kept():
     n = P.short_name("void (anonymous namespace)::read4_write1_kernel<8>(unsigned int const*)")
     assert n == "read4_write1_kernel<8>"
     assert P.leg_of(n) is None
+
+
+def test_pmc_summary_fractions(tmp_path):
+    """The pmc summary merges passes per kernel and derives its shares from
+    the averaged counters (GRBM_GUI_ACTIVE is the sum over 8 XCDs)."""
+    k = "void kvfp4::(anonymous namespace)::decode_mla_kernel<4, 2>(kvfp4::DecodeArgs)"
+    a = tmp_path / "a"
+    b = tmp_path / "b"
+    for d, rows in ((a, [("SQ_WAVE_CYCLES", 1000), ("SQ_WAIT_ANY", 600),
+                         ("SQ_ACTIVE_INST_ANY", 250), ("SQ_VALU_MFMA_BUSY_CYCLES", 4096),
+                         ("GRBM_GUI_ACTIVE", 80)]),
+                    (b, [("SQ_ACTIVE_INST_LDS", 200), ("SQ_LDS_BANK_CONFLICT", 50),
+                         ("GRBM_GUI_ACTIVE", 80)])):
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for c, v in rows:
+                w.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+    lines = P.pmc([str(a), str(b)])
+    row = next(l for l in lines if l.startswith("decode_mla_kernel<4, 2>"))
+    cols = row.split()
+    # kernel name has a space: "decode_mla_kernel<4," "2>"
+    wait, issue, valu, lds, mfma, bank = cols[3:9]
+    assert float(wait) == 60.0 and float(issue) == 25.0 and valu == "-"
+    assert float(lds) == 20.0 and float(mfma) == 40.0 and float(bank) == 25.0
