@@ -252,6 +252,27 @@ int32_t kvfp4_paged_decode_attention(
     const int32_t* seq_lens, int32_t max_seq_len_hint, float softmax_scale,
     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvfp4_paged_decode_attention without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, layouts
+ * and results otherwise (the same kernels and split-K plan, bit-identical
+ * outputs).  The split-K partials go to a scratch array of 96 MiB that the
+ * library holds on every device it runs on (allocated with its code
+ * object, kept until the process ends); this call allocates nothing.
+ * Sizes whose kvfp4_decode_workspace_bytes() exceeds 96 MiB are rejected
+ * with KVFP4_ERR_WORKSPACE before anything is launched (the MLA shape of
+ * batch 64 x 128 heads needs 84 MiB; Llama- and Qwen-shaped batches of 32
+ * need under 5 MiB).  Every call on a device shares that device's scratch:
+ * calls that overlap in time on one device (concurrent streams, or threads
+ * without ordering) race on it and must not be issued; calls ordered on one
+ * stream are fine.  The scratch needs no clearing between calls. */
+int32_t kvfp4_paged_decode_attention_noalloc(
+    const kvfp4_geometry* g, const void* packed_pool, int32_t packed_pool_pages,
+    const float* global_scale, const void* q, int32_t batch, int32_t num_q_heads,
+    int32_t v_dim, const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* seq_lens, int32_t max_seq_len_hint, float softmax_scale,
+    void* out, float* lse, void* stream);
+
 /* Static text for a status code.  "KV Cache Compression in TensorRT LLM",
  * Configuration and Setup of KV Cache Compression: an unsupported
  * combination is turned away with a clear message, not run. */

@@ -32,7 +32,8 @@ EXPORTS = (
     "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_gather_dequantize",
     "kvfp4_packed_page_bytes_rope", "kvfp4_quantize_pages_rope", "kvfp4_dequantize_pages_rope",
     "kvfp4_decode_workspace_bytes",
-    "kvfp4_paged_decode_attention", "kvfp4_status_string", "kvfp4_last_error_message",
+    "kvfp4_paged_decode_attention", "kvfp4_paged_decode_attention_noalloc",
+    "kvfp4_status_string", "kvfp4_last_error_message",
 )
 
 
@@ -115,6 +116,9 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_paged_decode_attention.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32, P, I32,
                                                  F, P, P, P, SZ, P]
     lib.kvfp4_paged_decode_attention.restype = I32
+    lib.kvfp4_paged_decode_attention_noalloc.argtypes = [G, P, I32, P, P, I32, I32, I32, P, I32,
+                                                         P, I32, F, P, P, P]
+    lib.kvfp4_paged_decode_attention_noalloc.restype = I32
     lib.kvfp4_status_string.argtypes = [I32]
     lib.kvfp4_status_string.restype = ctypes.c_char_p
     lib.kvfp4_last_error_message.argtypes = []
@@ -351,3 +355,22 @@ def kvfp4_paged_decode_attention(geometry, packed_pool, global_scale, q, block_t
         _scales(global_scale, g.num_kv_tensors), _ptr(q), B, Hq, vd, _ptr(block_table),
         int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len_hint), float(softmax_scale),
         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvfp4_paged_decode_attention_noalloc(geometry, packed_pool, global_scale, q, block_table,
+                                         seq_lens, max_seq_len_hint: int, softmax_scale: float,
+                                         out, lse=None, v_dim: Optional[int] = None,
+                                         stream=None) -> None:
+    """kvfp4_paged_decode_attention with the library's own scratch instead
+    of a workspace (for callers that cannot allocate; see the header for the
+    size limit and the rule that calls on one device must not overlap)."""
+    lib = load_library()
+    g = Geometry.of(geometry)
+    vd = int(v_dim if v_dim is not None else out.shape[-1])
+    _check_decode_args(g, q, out, lse, block_table, seq_lens, vd)
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    _check(lib.kvfp4_paged_decode_attention_noalloc(
+        ctypes.byref(g), _ptr(packed_pool), _pages(packed_pool, kvfp4_packed_page_bytes(g)),
+        _scales(global_scale, g.num_kv_tensors), _ptr(q), B, Hq, vd, _ptr(block_table),
+        int(block_table.shape[1]), _ptr(seq_lens), int(max_seq_len_hint), float(softmax_scale),
+        _ptr(out), _ptr(lse), _stream(stream)))

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 #include "kvfp4.h"
@@ -79,6 +80,44 @@ int device_cus() {
   }
   g_cus[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Split-K scratch of the allocation-free decode entry point (one copy per
+// device, allocated with the library's code object and held until the
+// process ends).  In host code `scratch` names a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(96) << 20;
+std::atomic<void*> g_scratch_addr[64];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the
+// first call there (with that device current) and kept.
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64)
+    return fail(KVFP4_ERR_UNSUPPORTED, "device %d: the scratch table covers devices 0-63", dev);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(KVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVFP4_OK;
 }
 
 int32_t check_codec(const kvfp4_geometry* g, const void* from, int32_t from_pages,
@@ -338,6 +377,25 @@ size_t kvfp4_decode_workspace_bytes(const kvfp4_geometry* g, int32_t batch, int3
       .workspace_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of one decode call: on the caller's workspace
+// (`workspace`, `workspace_bytes`), or with `scratch` set on the library's
+// scratch array (the allocation-free entry point; the workspace arguments
+// are then ignored).
+int32_t decode_call(const kvfp4_geometry* g, const void* packed_pool, int32_t packed_pool_pages,
+                    const float* global_scale, const void* q, int32_t batch,
+                    int32_t num_q_heads, int32_t v_dim, const int32_t* block_table,
+                    int32_t max_pages_per_seq, const int32_t* seq_lens,
+                    int32_t max_seq_len_hint, float softmax_scale, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, bool scratch, void* stream);
+
+}  // namespace
+
+extern "C" {
+
 int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed_pool,
                                      int32_t packed_pool_pages, const float* global_scale,
                                      const void* q, int32_t batch, int32_t num_q_heads,
@@ -346,6 +404,33 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
                                      int32_t max_seq_len_hint, float softmax_scale, void* out,
                                      float* lse, void* workspace, size_t workspace_bytes,
                                      void* stream) {
+  return decode_call(g, packed_pool, packed_pool_pages, global_scale, q, batch, num_q_heads,
+                     v_dim, block_table, max_pages_per_seq, seq_lens, max_seq_len_hint,
+                     softmax_scale, out, lse, workspace, workspace_bytes, false, stream);
+}
+
+int32_t kvfp4_paged_decode_attention_noalloc(const kvfp4_geometry* g, const void* packed_pool,
+                                             int32_t packed_pool_pages, const float* global_scale,
+                                             const void* q, int32_t batch, int32_t num_q_heads,
+                                             int32_t v_dim, const int32_t* block_table,
+                                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                             int32_t max_seq_len_hint, float softmax_scale,
+                                             void* out, float* lse, void* stream) {
+  return decode_call(g, packed_pool, packed_pool_pages, global_scale, q, batch, num_q_heads,
+                     v_dim, block_table, max_pages_per_seq, seq_lens, max_seq_len_hint,
+                     softmax_scale, out, lse, nullptr, 0, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t decode_call(const kvfp4_geometry* g, const void* packed_pool, int32_t packed_pool_pages,
+                    const float* global_scale, const void* q, int32_t batch,
+                    int32_t num_q_heads, int32_t v_dim, const int32_t* block_table,
+                    int32_t max_pages_per_seq, const int32_t* seq_lens,
+                    int32_t max_seq_len_hint, float softmax_scale, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, bool scratch, void* stream) {
   int32_t st = check_decode_shape(g, batch, num_q_heads, v_dim, max_seq_len_hint);
   if (st) return st;
   if (batch == 0) return ok();
@@ -364,6 +449,18 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
   kvfp4::Geom geom = to_geom(g);
   kvfp4::DecodePlan plan =
       kvfp4::plan_decode(geom, batch, num_q_heads, v_dim, max_seq_len_hint, device_cus());
+  if (scratch) {
+    if (plan.workspace_bytes > kScratchBytes)
+      return fail(KVFP4_ERR_WORKSPACE,
+                  "these sizes need %zu bytes of split-K scratch, more than the %zu bytes the "
+                  "allocation-free entry point holds; call kvfp4_paged_decode_attention with "
+                  "a workspace instead", plan.workspace_bytes, kScratchBytes);
+    if (((uintptr_t)q & 15) != 0)
+      return fail(KVFP4_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    int32_t sst = scratch_address(&workspace);
+    if (sst) return sst;
+    workspace_bytes = kScratchBytes;
+  }
   if (workspace_bytes < plan.workspace_bytes || (plan.workspace_bytes > 0 && !workspace))
     return fail(KVFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
                 plan.workspace_bytes);
@@ -399,6 +496,10 @@ int32_t kvfp4_paged_decode_attention(const kvfp4_geometry* g, const void* packed
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 const char* kvfp4_status_string(int32_t status) {
   switch (status) {

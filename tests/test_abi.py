@@ -379,3 +379,18 @@ def test_binding_rejects_token_index_dtype(lib, fn, which):
         else:
             K.kvfp4_gather_dequantize((2, 64, 8, 128), pool, idx["token_slots"],
                                       idx["token_rows"], rows, [1.0, 1.0])
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Sizes whose split-K workspace exceeds the allocation-free entry
+    point's 96 MiB scratch are rejected before anything is launched (the
+    pointers below are never dereferenced)."""
+    g = K.Geometry(1, 64, 1, 576)
+    need = lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 4096, 128, 512, 16384)
+    assert need > 96 << 20
+    gs = (ctypes.c_float * 1)(1.0)
+    st = lib.kvfp4_paged_decode_attention_noalloc(
+        ctypes.byref(g), FAKE, 8, gs, FAKE, 4096, 128, 512, FAKE + 0x100, 256, FAKE + 0x200,
+        16384, 0.04, FAKE + 0x300, None, None)
+    assert st == K.KVFP4_ERR_WORKSPACE
+    assert "allocation-free" in lib.kvfp4_last_error_message().decode()
