@@ -177,9 +177,10 @@ __device__ inline u32x4 load_q8(const uint16_t* row, int i) {
   return *reinterpret_cast<const u32x4*>(row + 8 * i);
 }
 
-// Issues the loads of one lane's share of tile `ti` of a sequence; rows
-// past the sequence end (or a whole tile of a bad page) come back as zero
-// from the buffer resources' bounds, and are never fetched.
+// Issues the loads of one lane's share of a tile of a sequence; rows past
+// the sequence end (or a whole tile of a bad page, or a request past the
+// stream's last tile) come back as zero from the buffer resources' bounds,
+// and are never fetched.
 struct TileGeom {
   const uint8_t* pool;
   long long page_bytes;
@@ -187,16 +188,16 @@ struct TileGeom {
   uint32_t off_data, off_scale;  // this lane's row offsets in a tile
 };
 
-__device__ inline int tile_rows(const TileGeom& tg, int slot, long long ti) {
-  int n = tg.L - (int)(ti * kTile);
+__device__ inline int tile_rows(const TileGeom& tg, int slot, int ti) {
+  int n = tg.L - ti * kTile;
   n = n > kTile ? kTile : n;
   if (slot < 0 || slot >= tg.pool_pages) n = 0;
   return __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n);
 }
 
 template <int KD>
-__device__ inline void load_tile(Packed<KD>& p, const TileGeom& tg, int slot, long long ti, int n) {
-  const int row0 = (int)(ti % tg.tiles_per_page) * kTile;
+__device__ inline void load_tile(Packed<KD>& p, const TileGeom& tg, int slot, int tip, int n) {
+  const int row0 = tip * kTile;  // tip: the tile's index within its page
   const int rowb = tg.H * (KD / 2), rows = tg.H * (KD / 16);
   const uint8_t* page = tg.pool + (long long)(n > 0 ? slot : 0) * tg.page_bytes;
   const uint8_t* kd = page + (long long)row0 * rowb;
@@ -307,9 +308,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     if (p_lo >= p_hi) continue;
     note_segment(a, w, b, p_lo, p_hi, npages);
     tg.L = L;
-    const long long t_lo = p_lo * tg.tiles_per_page;
-    long long t_hi = p_hi * tg.tiles_per_page;
-    const long long t_end = (L + kTile - 1) / kTile;
+    // tile indices within the sequence (32-bit: a sequence holds at most
+    // 2^31 tokens)
+    const int t_lo = (int)p_lo * tg.tiles_per_page;
+    int t_hi = (int)p_hi * tg.tiles_per_page;
+    const int t_end = (L + kTile - 1) / kTile;
     if (t_hi > t_end) t_hi = t_end;
 
     // column lr: KV head 4 kg + lr / 4, its query head 4 sub + lr % 4
@@ -325,17 +328,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     for (int dt = 0; dt < KD / 16; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m = kNoMax, l = 0.f;
 
-    // page-table entries of pages c0 .. c0+63, one per lane
-    const int32_t* bt_row = a.block_table + (long long)b * a.max_pages;
-    long long c0 = -(1LL << 40);  // no window loaded yet
-    int slot_vec = -1;
-    auto slot_of = [&](long long ti) -> int {
-      const long long pg = ti / tg.tiles_per_page;
-      if (pg < c0 || pg >= c0 + 64) {
-        c0 = pg;
-        slot_vec = (c0 + lane < p_hi) ? bt_row[c0 + lane] : -1;
-      }
-      return __builtin_amdgcn_readlane(slot_vec, (int)(pg - c0));
+    // Page-table entries are read with scalar loads (a uniform address in
+    // the constant address space): their wait is on the scalar/LDS
+    // counter, so reading an entry never waits for the vector-memory loads
+    // of tiles in flight.  Each tile's entry is requested a tile ahead.
+    typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+    const ConstI32 bt_row = (ConstI32)(a.block_table + (long long)b * a.max_pages);
+    const int tpp = tg.tiles_per_page;
+    const bool tpp_pow2 = (tpp & (tpp - 1)) == 0;
+    const int tpp_sh = __builtin_ctz((unsigned)tpp);
+    auto page_of = [&](int t) -> int { return tpp_pow2 ? t >> tpp_sh : t / tpp; };
+    auto slot_load = [&](int pg) -> int {  // -1 past the segment
+      const int e = bt_row[pg < (int)p_hi ? pg : (int)p_hi - 1];
+      return pg < (int)p_hi ? e : -1;
     };
 
     // One tile of the stream, in two phases: (a) V rows to LDS and the
@@ -432,12 +437,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    auto issue = [&](Packed& p, int& n, long long t) {
-      if (t < t_hi) {
-        const int sl = slot_of(t);
-        n = tile_rows(tg, sl, t);
-        load_tile(p, tg, sl, t, n);
-      }
+    // the loads of tile t of the sequence from slot sl (-1: no tile; the
+    // loads then read zero and fetch nothing, so a request needs no branch)
+    auto issue = [&](Packed& p, int& n, int t, int sl) {
+      n = tile_rows(tg, sl, t);
+      load_tile(p, tg, sl, t - page_of(t) * tpp, n);
     };
     // queries of this wave's 16 heads as the block-diagonal B operand, one
     // pass: the largest magnitude (from the bf16 bit patterns) sets a power
@@ -486,23 +490,36 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     // starts kg tiles later and wraps round), so the block-scale lines the
     // groups share are fetched by one group and found in L2 by the next,
     // instead of being missed by all of them at once.
-    const long long first_t = t_lo + s;
-    const int nk = first_t < t_hi ? (int)((t_hi - first_t + NS - 1) / NS) : 0;
+    const int first_t = t_lo + s;
+    const int nk = first_t < t_hi ? (t_hi - first_t + NS - 1) / NS : 0;
     const int rot = (KVFP4_GQA_ROT && nk > 0) ? gt % nk : 0;
-    auto tile_at = [&](int k) -> long long {
+    auto tile_at = [&](int k) -> int {  // k-th tile of the walk (k < nk)
       int kk = k + rot;
       if (kk >= nk) kk -= nk;
-      return first_t + (long long)kk * NS;
+      return first_t + kk * NS;
     };
-    Packed cur, nxt;
-    int n_cur = 0, n_nxt = 0;
-    if (nk > 0) issue(cur, n_cur, tile_at(0));  // requested before the queries are prepared
+    // slot of the k-th tile of the walk, -1 past its end (the entry read is
+    // always in bounds)
+    auto slot_for = [&](int k) -> int {
+      const int sl = slot_load(page_of(tile_at(k < nk ? k : 0)));
+      return k < nk ? sl : -1;
+    };
+    // two register sets, the loop unrolled by two so that each keeps its
+    // role (tile k in one, tile k + 1 requested into the other)
+    Packed pk0, pk1;
+    int n0 = 0, n1 = 0;
+    int sl_next = slot_for(0);
+    issue(pk0, n0, tile_at(0), sl_next);  // requested before the queries are prepared
+    sl_next = slot_for(1);
     load_queries();
-    for (int k = 0; k < nk; ++k) {
-      if (k + 1 < nk) issue(nxt, n_nxt, tile_at(k + 1));
+    auto step = [&](int k, Packed& cur, int& n_cur, Packed& nxt, int& n_nxt) {
+      issue(nxt, n_nxt, tile_at(k + 1 < nk ? k + 1 : 0), sl_next);
+      sl_next = slot_for(k + 2);
       phase_b(phase_a(cur), n_cur);
-      cur = nxt;
-      n_cur = n_nxt;
+    };
+    for (int k = 0; k < nk; k += 2) {
+      step(k, pk0, n0, pk1, n1);
+      if (k + 1 < nk) step(k + 1, pk1, n1, pk0, n0);
     }
 
     // merge the NS streams of each KV-head group, then write the partial
