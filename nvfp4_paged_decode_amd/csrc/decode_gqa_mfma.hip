@@ -94,6 +94,9 @@ constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
 #ifndef KVFP4_GQA_SPLIT
 #define KVFP4_GQA_SPLIT 1
 #endif
+#ifndef KVFP4_GQA_BALANCE  // priority to the SIMD's lagging wave
+#define KVFP4_GQA_BALANCE 1
+#endif
 #ifndef KVFP4_GQA_AUX  // cache-policy bits of the K/V loads
 #define KVFP4_GQA_AUX 0
 #endif
@@ -111,10 +114,15 @@ struct MergeLds {
   float o[kWaves][16][merge_pitch_of<KD>()];  // per wave: 16 query heads x KD dims
   float ml[kWaves][16][2];   // running max and sum per query head
 };
+// Staging or merge area, then one progress counter per wave.
 template <int KD>
-constexpr size_t lds_bytes() {
+constexpr size_t area_bytes() {
   return sizeof(StageLds<KD>) > sizeof(MergeLds<KD>) ? sizeof(StageLds<KD>)
                                                      : sizeof(MergeLds<KD>);
+}
+template <int KD>
+constexpr size_t lds_bytes() {
+  return area_bytes<KD>() + kWaves * sizeof(int);
 }
 
 // One lane's packed share of a tile: its K row and V row (KD/2 bytes each)
@@ -244,6 +252,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   extern __shared__ __align__(16) unsigned char smem[];
   StageLds<KD>& st = *reinterpret_cast<StageLds<KD>*>(smem);
   MergeLds<KD>& mg = *reinterpret_cast<MergeLds<KD>*>(smem);
+  int* progress = reinterpret_cast<int*>(smem + area_bytes<KD>());  // [kWaves]
   const Geom g = a.g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -253,6 +262,27 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   const bool diag = (lr >> 2) == lg;          // column lr's KV head is group lg
   const int w = blockIdx.x, nwg = gridDim.x;
   const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
+
+  // The 8 waves sit two to a SIMD (waves w and w ^ 4), and a SIMD issues
+  // for its older ready wave first, which leaves the younger one about a
+  // quarter slower; with a fixed split of the tiles the workgroup then
+  // waits for it.  So each wave publishes its count of finished tiles and
+  // runs at raised priority while it trails its SIMD partner: both finish
+  // together and the tile split (and the result) stays fixed.  The counter
+  // is a hint: a stale or unset value only costs balance.
+  int tiles_done = 0;
+  if (KVFP4_GQA_BALANCE && lane == 0) progress[wave] = 0;
+  auto balance = [&]() {
+    ++tiles_done;
+    if (lane == 0)
+      __hip_atomic_store(&progress[wave], tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int other = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(&progress[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (tiles_done < other)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
 
   TileGeom tg;
   tg.pool = a.pool;
@@ -516,6 +546,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       issue(nxt, n_nxt, tile_at(k + 1 < nk ? k + 1 : 0), sl_next);
       sl_next = slot_for(k + 2);
       phase_b(phase_a(cur), n_cur);
+      if constexpr (KVFP4_GQA_BALANCE) balance();
     };
     for (int k = 0; k < nk; k += 2) {
       step(k, pk0, n0, pk1, n1);
