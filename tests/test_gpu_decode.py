@@ -7,6 +7,7 @@ import pytest
 import nvfp4_paged_decode_amd as K
 from nvfp4_paged_decode_amd import workloads as W
 from oracle import nvfp4 as O
+from tests import oracle_pool as P
 from tests.gpu_common import (assert_attention_close, dev, host, oracle_attention,
                               oracle_packed_pages, poison_unread, require_gpu, torch)
 
@@ -307,47 +308,34 @@ def test_decode_unaligned_output():
 
 
 FULL = {
-    "llama3_8b": (lambda: W.llama3_8b(), [0, 13, 31]),
-    "qwen3_8b_long": (lambda: W.qwen3_8b_long(), None),  # longest and shortest sequence
-    "mla": (lambda: W.mla(), [0, 37, 63]),
+    "llama3_8b": lambda: W.llama3_8b(),
+    "qwen3_8b_long": lambda: W.qwen3_8b_long(),
+    "mla": lambda: W.mla(),
 }
 
 
-@pytest.mark.parametrize("name", ["llama3_8b", "qwen3_8b_long", "mla"])
-def test_decode_full_size_sampled(name):
-    """Full-size workloads in the bench's launch configuration.  The pool is
-    encoded on the GPU; the sampled sequences' pages are then overwritten
-    with oracle-encoded bytes, so every compared output depends on oracle
-    inputs only."""
+@pytest.mark.parametrize("name", list(FULL))
+def test_decode_full_size_all_outputs(name):
+    """Full-size workloads in the bench's launch configuration, every output
+    of every sequence and query head: the whole pool is encoded by the
+    oracle (process pool), bytes no decode may read are poisoned, the GPU
+    decodes the batch in one call, and the oracle computes every
+    (sequence, head) result in the pool."""
     require_gpu()
-    wl = FULL[name][0]()
+    wl = FULL[name]()
     gs = wl.gs_calibrated
-    if name == "qwen3_8b_long":
-        sample = [int(np.argmax(wl.seq_lens)), int(np.argmin(wl.seq_lens))]
-    else:
-        sample = FULL[name][1]
     g = O.Geometry(*wl.geometry)
-    hot_d = dev(wl.hot_pool.view(np.int16))
-    packed_d = torch.empty((wl.num_slots, O.packed_page_bytes(g)), dtype=torch.uint8,
-                           device="cuda")
-    K.kvfp4_quantize_pages(wl.geometry, hot_d, packed_d, wl.num_slots, gs)
-    del hot_d
-    T = wl.page_size
-    slots = sorted({int(s) for b in sample
-                    for s in wl.block_table[b, :-(-int(wl.seq_lens[b]) // T)]})
-    ref_pages = oracle_packed_pages(wl.hot_pool, wl.geometry, gs, slots)
-    host_pool = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
-    host_pool[slots] = ref_pages
-    spare = np.setdiff1d(np.arange(wl.num_slots), wl.used_slots)
-    poison_unread(host_pool, wl, np.random.default_rng(3))  # tails + spare slots
-    touched = np.union1d(np.asarray(slots), spare)
-    packed_d[torch.from_numpy(touched).cuda()] = dev(host_pool[touched])
-    out, lse = gpu_decode(wl, packed_d, gs)
-    check(wl, gs, host_pool, out, lse, batch_indices=sample,
-          head_indices=None, what=f"{name} full size")
-    # every output of the whole batch is finite and the merge produced an lse
-    allo = (out.astype(np.uint32) << 16).view(np.float32)
-    assert np.all(np.isfinite(allo)) and np.all(np.isfinite(lse))
+    with P.make_pool() as pool:
+        packed = np.zeros((wl.num_slots, O.packed_page_bytes(g)), np.uint8)
+        packed[wl.used_slots] = P.encode_pages(pool, wl.hot_pool, wl.geometry, gs,
+                                               wl.used_slots)
+        poison_unread(packed, wl, np.random.default_rng(3))
+        out, lse = gpu_decode(wl, dev(packed), gs)
+        ref, ref_lse = P.decode_attention_all(pool, packed, wl, gs)
+    assert_attention_close(out, ref, f"{name} full size")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)), f"{name}: lse finiteness"
+    assert np.all(np.abs(lse[fin] - ref_lse[fin]) <= 1e-3 + 1e-3 * np.abs(ref_lse[fin])), name
 
 
 @pytest.mark.parametrize("name", list(BAD_PAGES))
