@@ -16,37 +16,50 @@
 // Why MFMA with 4 query heads.  On VALU every cached value costs one FMA
 // per query head (4 per value) on top of its dequantization, which keeps
 // the VALU busy for longer than HBM takes to deliver the bytes.  Here a
-// wave takes 4 KV heads at once and places them block-diagonally in one
-// v_mfma_f32_16x16x32_f16: the 32-long contraction is 4 KV heads x 8
-// values, and the 16 output columns are those 4 KV heads x their 4 query
-// heads, so every output column is a real query head.
+// wave takes 4 KV heads at once: one v_mfma_f32_16x16x32_f16 multiplies 16
+// (token, KV head) rows of K by the 16 query columns of those 4 KV heads,
+// and each lane keeps the quarter of the products whose row and column
+// share a KV head (the MFMA has compute to spare; the other three quarters
+// are discarded).
+//
+// Load layout.  A tile's K (and V) rows of the wave's 4 KV heads are read in
+// 4 rounds of 4 tokens; in round j, lane (4a + b) + 16p takes quarter p of
+// the row of token 4j + a, KV-head slot b, which is exactly its A operand
+// (row 4a + b, k-group p).  Each load instruction therefore covers 4 whole
+// token rows of the 4 KV heads, i.e. whole 128-byte lines, so the loads are
+// non-temporal (streaming) without any line being fetched twice; a row-per-
+// lane layout spreads each line over 4 instructions and streams about 30 %
+// slower.
 //
 // 16-bit format.  E2M1 x E4M3 has at most 6 significant bits and lies in
 // [2^-10, 2688]: exact in fp16 (normal range), so the dequantized values
 // are exact; gfx950 converts E2M1 codes exactly to fp16 pairs
-// (v_cvt_scalef32_pk_f16_fp4 with scale 1.0) and one v_pk_mul_f16 applies
-// the block scale to two values.  Queries (bf16) are scaled per head by a
-// power of two so that their largest magnitude sits just under 2^15, then
-// converted to fp16: bf16's 8-bit significands fit fp16's 11, so the only
-// loss is for elements 2^-39 of the head's largest or smaller.  The power
-// of two is undone on the fp32 scores.  Probabilities are rounded to fp16
-// (11 significant bits) for the P.V product.
+// (v_cvt_scalef32_pk_f16_fp4 with scale 1.0; its scale operand applies
+// only a power of two, so it cannot take the E4M3 scale) and one
+// v_pk_mul_f16 applies the block scale to two values.  Queries (bf16) are
+// scaled per head by a power of two so that their largest magnitude sits
+// just under 2^15, then converted to fp16: bf16's 8-bit significands fit
+// fp16's 11, so the only loss is for elements 2^-39 of the head's largest
+// or smaller.  The power of two is undone on the fp32 scores.
+// Probabilities are rounded to fp16 (11 significant bits) for the P.V
+// product.
 //
 // Per 16-token tile of a wave (4 KV heads):
-//   scores   S^T = K Q^T: A = K, lane (token t, KV head g) dequantizes its
-//            own row (head_dim / 2 bytes), 8 values per k-step; B = Q^T block-diagonal
-//            (lane (column c, group g) holds query c's 8 values when g is
-//            c's KV head, else 0), kept in registers per sequence.  Lane
-//            (c, g) receives rows 4g..4g+3 of column c.
+//   scores   round j: A = K rows (token 4j + r/4, KV-head slot r%4), B = the
+//            dense query operand (lane (column c, k-group p) holds quarter p
+//            of column c's query row, kept in registers per sequence).
+//            Lane (c, x) keeps row block c/4 of its column: the score of
+//            token 4j + x, for j = 0..3.
 //   softmax  online per column, running max shared by the column's 4
 //            lanes; the accumulators are rescaled only when a tile's
 //            maximum exceeds the running one by more than 2^8.
-//   P.V      O^T = V^T P^T.  V rows are dequantized by the same lanes and
-//            staged in LDS in their natural [KV head][token][dim] order;
-//            ds_read_b64_tr_b16 reads them transposed (4 tokens of one dim
-//            per lane).  Two products per 16 dims: the k-group of KV head
-//            g takes tokens 4x..4x+3 and 4y..4y+3 (x, y = g + 2m, g + 2m
-//            + 1, mod 4, m = 0, 1), whose probabilities sit in lanes
+//   P.V      O^T = V^T P^T.  V rows are dequantized by the lanes that load
+//            them and staged in LDS per KV head, token 4j + a at row 4a + j
+//            (so that lane (c, x) holds the probabilities of rows
+//            4x..4x+3); ds_read_b64_tr_b16 reads them transposed (4 rows
+//            of one dim per lane).  Two products per 16 dims: the k-group
+//            of KV head g takes rows 4x..4x+3 and 4y..4y+3 (x, y = g + 2m,
+//            g + 2m + 1, mod 4, m = 0, 1), whose probabilities sit in lanes
 //            (c, x), (c, y) and are fetched with ds_bpermute.
 //
 // Workgroup: 8 waves = NGT wave groups (groups of 4 KV-head slots x query
@@ -97,13 +110,21 @@ constexpr float kSlack = 8.f;  // the running max is raised only when a tile's
 #ifndef KVFP4_GQA_BALANCE  // priority to the SIMD's lagging wave
 #define KVFP4_GQA_BALANCE 1
 #endif
-#ifndef KVFP4_GQA_AUX  // cache-policy bits of the K/V loads
-#define KVFP4_GQA_AUX 0
+#ifndef KVFP4_GQA_SETS  // register sets of tiles (2: one in flight, 3: two)
+#define KVFP4_GQA_SETS 2
+#endif
+#ifndef KVFP4_GQA_AUX  // cache-policy bits of the K/V data loads: non-temporal
+#define KVFP4_GQA_AUX 2
 #endif
 
+// fp16 between the staged rows of consecutive KV heads: 16 rows plus 16 fp16
+// (8 banks), so the 8 lanes of a 16-byte write that differ in KV head only
+// hit distinct banks
+template <int KD>
+constexpr int head_stride_of() { return kTile * pitch_of<KD>() + 16; }
 template <int KD>
 struct StageLds {
-  _Float16 v[kWaves][4][kTile][pitch_of<KD>()];  // per wave: 4 KV heads x 16 tokens
+  _Float16 v[kWaves][4 * head_stride_of<KD>()];  // per wave: 4 KV heads x 16 tokens
 };
 // floats per merge row: rows 4 banks apart, so the 8 lanes of a 16-byte
 // access hit distinct banks
@@ -125,12 +146,23 @@ constexpr size_t lds_bytes() {
   return area_bytes<KD>() + kWaves * sizeof(int);
 }
 
-// One lane's packed share of a tile: its K row and V row (KD/2 bytes each)
-// and their KD/16 scale bytes each.
+// One lane's packed share of a tile: in each of the 4 load rounds j (tokens
+// 4j..4j+3), a quarter of one K row and of one V row (KD/8 bytes each) and
+// the scale bytes of that quarter (KD/64 each).
+template <int KD>
+struct ChunkOf;
+template <>
+struct ChunkOf<128> {
+  typedef u32x4 type;
+};
+template <>
+struct ChunkOf<64> {
+  typedef u32x2 type;
+};
 template <int KD>
 struct Packed {
-  u32x4 k[KD / 32], v[KD / 32];
-  uint32_t ks[KD / 64], vs[KD / 64];
+  typename ChunkOf<KD>::type k[4], v[4];
+  uint32_t ks[4], vs[4];
 };
 
 __device__ inline f16x2 fp4x2(uint32_t w, int sel) {
@@ -142,17 +174,7 @@ __device__ inline f16x2 fp4x2(uint32_t w, int sel) {
   }
 }
 
-// The KD/16 block scales of a row (E4M3 bytes) as fp16 pairs (exact).
-template <int KD>
-__device__ inline void scales_row(const uint32_t (&s)[KD / 64], f16x2 (&o)[KD / 32]) {
-#pragma unroll
-  for (int i = 0; i < KD / 64; ++i) {
-    o[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[i], 1.0f, false);
-    o[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s[i], 1.0f, true);
-  }
-}
-
-// 8 values of dword w (dims 8i..8i+7 of a row) times their block scale.
+// 8 values of dword w (8 consecutive dims of a row) times their block scale.
 __device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
   const f16x2 s2 = {sb, sb};
   const f16x2 a = fp4x2(w, 0) * s2, b = fp4x2(w, 1) * s2;
@@ -160,10 +182,8 @@ __device__ inline f16x8 dequant8(uint32_t w, _Float16 sb) {
   return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-template <int N>
-__device__ inline _Float16 block_scale(const f16x2 (&s)[N], int blk) {
-  return (blk & 1) ? s[blk >> 1].y : s[blk >> 1].x;
-}
+__device__ inline _Float16 sp0(f16x2 s) { return s[0]; }
+__device__ inline _Float16 sp1(f16x2 s) { return s[1]; }
 
 __device__ inline uint32_t bperm(uint32_t v, int src_lane) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
@@ -193,7 +213,8 @@ struct TileGeom {
   const uint8_t* pool;
   long long page_bytes;
   int pool_pages, T, H, L, tiles_per_page;
-  uint32_t off_data, off_scale;  // this lane's row offsets in a tile
+  uint32_t off_data, off_scale;  // this lane's offsets in a tile, round 0
+  uint32_t js_data, js_scale;    // advance per load round (4 token rows)
 };
 
 __device__ inline int tile_rows(const TileGeom& tg, int slot, int ti) {
@@ -216,21 +237,26 @@ __device__ inline void load_tile(Packed<KD>& p, const TileGeom& tg, int slot, in
   auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)vd, (short)0, n * rowb, 0x00020000);
   auto rks = __builtin_amdgcn_make_buffer_rsrc((void*)kss, (short)0, n * rows, 0x00020000);
   auto rvs = __builtin_amdgcn_make_buffer_rsrc((void*)vss, (short)0, n * rows, 0x00020000);
+  // round j: every load instruction covers 4 whole token rows of the wave
+  // group's KV heads (whole cache lines), so the data loads can be
+  // non-temporal without a line being fetched twice
 #pragma unroll
-  for (int j = 0; j < KD / 32; ++j) {
-    p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
-    p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tg.off_data + 16 * j, 0, KVFP4_GQA_AUX));
-  }
-  if constexpr (KD == 128) {
-    const u32x2 ks = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rks, tg.off_scale, 0, KVFP4_GQA_AUX));
-    const u32x2 vs = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, tg.off_scale, 0, KVFP4_GQA_AUX));
-    p.ks[0] = ks.x;
-    p.ks[1] = ks.y;
-    p.vs[0] = vs.x;
-    p.vs[1] = vs.y;
-  } else {
-    p.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, tg.off_scale, 0, KVFP4_GQA_AUX);
-    p.vs[0] = __builtin_amdgcn_raw_buffer_load_b32(rvs, tg.off_scale, 0, KVFP4_GQA_AUX);
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (KD == 128) {
+      p.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rk, tg.off_data, j * tg.js_data, KVFP4_GQA_AUX));
+      p.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rv, tg.off_data, j * tg.js_data, KVFP4_GQA_AUX));
+      p.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, tg.off_scale, j * tg.js_scale, 0);
+      p.vs[j] = __builtin_amdgcn_raw_buffer_load_b16(rvs, tg.off_scale, j * tg.js_scale, 0);
+    } else {
+      p.k[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rk, tg.off_data, j * tg.js_data, KVFP4_GQA_AUX));
+      p.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rv, tg.off_data, j * tg.js_data, KVFP4_GQA_AUX));
+      p.ks[j] = __builtin_amdgcn_raw_buffer_load_b8(rks, tg.off_scale, j * tg.js_scale, 0);
+      p.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(rvs, tg.off_scale, j * tg.js_scale, 0);
+    }
   }
 }
 
@@ -260,6 +286,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   const int kg = gt % NKG, sub = gt / NKG;
   const int lr = lane & 15, lg = lane >> 4;   // MFMA row/column, k-group
   const bool diag = (lr >> 2) == lg;          // column lr's KV head is group lg
+  // load rounds: lane (4 la + lb) + 16 lg takes quarter lg of the K/V rows of
+  // token 4j + la, KV-head slot lb
+  const int la = lr >> 2, lb = lr & 3;
   const int w = blockIdx.x, nwg = gridDim.x;
   const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
 
@@ -293,13 +322,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   tg.tiles_per_page = g.T / kTile;
   // KV-head slots past H (H not a multiple of 4 here) read past the
   // buffer's range: their rows load as zeros and fetch nothing
-  const bool kv_ok = 4 * kg + lg < g.H;
-  tg.off_data = kv_ok ? (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 2)) : kPastRange;
-  tg.off_scale = kv_ok ? (uint32_t)((lr * g.H + 4 * kg + lg) * (KD / 16)) : kPastRange;
+  const bool kv_ok = 4 * kg + lb < g.H;
+  tg.off_data = kv_ok ? (uint32_t)((la * g.H + 4 * kg + lb) * (KD / 2) + lg * (KD / 8)) : kPastRange;
+  tg.off_scale = kv_ok ? (uint32_t)((la * g.H + 4 * kg + lb) * (KD / 16) + lg * (KD / 64)) : kPastRange;
+  tg.js_data = (uint32_t)(4 * g.H * (KD / 2));
+  tg.js_scale = (uint32_t)(4 * g.H * (KD / 16));
 
   // transposed-read addresses: lane (q = (lane&15)>>2, j = lane&3) of
   // k-group lg points at row 4x + q, dims 4j.. of KV head lg
-  _Float16* vw = &st.v[wave][lg][0][0];
+  constexpr int kHead = head_stride_of<KD>();
+  _Float16* vw = &st.v[wave][lg * kHead];
   const int q4 = (lr >> 2), j4 = lr & 3;
   const _Float16* tr_base[2][2];
 #pragma unroll
@@ -350,7 +382,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     const int kv_of_col = 4 * kg + (lr >> 2);
     const bool col_ok = q_of_kv < G && kv_of_col < g.H;
     const int head = col_ok ? kv_of_col * G + q_of_kv : 0;
-    f16x8 qb[KD / 8];   // queries: filled once the first tile is requested
+    f16x8 qb[KD / 32];  // queries: filled once the first tile is requested
     float qs = 0.f;
 
     f32x4 acc[KD / 16];
@@ -377,37 +409,46 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     // scores -- after which the tile's registers are free -- and (b)
     // softmax and P.V from LDS.
     auto phase_a = [&](const Packed& cur) -> f32x4 {
-      // V rows -> LDS (natural layout, 16-byte chunks swizzled by row bit 2)
+      // V rows -> LDS: round j's token 4j + la goes to row 4 la + j of KV
+      // head lb (16-byte chunks swizzled by row bit 2, which is la & 1), so
+      // that lane (column, x) holds the probabilities of rows 4x..4x+3
       {
-        f16x2 vsc[KD / 32];
-        scales_row<KD>(cur.vs, vsc);
-        _Float16* dst = vw + lr * kPitch;
-        const int sw = KVFP4_GQA_SWZ ? (lr >> 2) & 1 : 0;
+        const int sw = KVFP4_GQA_SWZ ? la & 1 : 0;
+        _Float16* vh = &st.v[wave][lb * kHead];
 #pragma unroll
-        for (int j = 0; j < KD / 32; ++j)
+        for (int j = 0; j < 4; ++j) {
+          const f16x2 vsc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.vs[j], 1.0f, false);
+          _Float16* dst = vh + (4 * la + j) * kPitch;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<f16x8*>(dst + 8 * ((4 * j + e) ^ sw)) =
-                dequant8(cur.v[j][e], block_scale(vsc, (4 * j + e) >> 1));
-      }
-
-      // scores S^T[token][column], two independent accumulation chains
-      f32x4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-      {
-        f16x2 ksc[KD / 32];
-        scales_row<KD>(cur.ks, ksc);
-#pragma unroll
-        for (int ks = 0; ks < KD / 8; ks += 2) {
-          const f16x8 ka0 = dequant8(cur.k[ks >> 2][ks & 3], block_scale(ksc, ks >> 1));
-          sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka0, qb[ks], sc0, 0, 0, 0);
-          const f16x8 ka1 = dequant8(cur.k[ks >> 2][(ks & 3) + 1], block_scale(ksc, ks >> 1));
-          if (KVFP4_GQA_SPLIT)
-            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka1, qb[ks + 1], sc1, 0, 0, 0);
-          else
-            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka1, qb[ks + 1], sc0, 0, 0, 0);
+          for (int e = 0; e < KD / 32; ++e)
+            *reinterpret_cast<f16x8*>(dst + 8 * (((KD / 32) * lg + e) ^ sw)) =
+                dequant8(cur.v[j][e], (KD == 128 && e >= 2) ? sp1(vsc) : sp0(vsc));
         }
       }
-      return sc0 + sc1;
+
+      // scores: round j's product has rows (token 4j + row/4, KV-head slot
+      // row%4) and columns (query heads); a lane keeps the one entry of its
+      // column whose row has the column's KV head, row block lr / 4 (a dense
+      // query operand: the products of other KV heads are discarded)
+      f32x4 d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      f16x2 ksc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ksc[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cur.ks[j], 1.0f, false);
+#pragma unroll
+      for (int ks = 0; ks < KD / 32; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x8 ka = dequant8(cur.k[j][ks], (KD == 128 && ks >= 2) ? sp1(ksc[j]) : sp0(ksc[j]));
+          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[ks], d[j], 0, 0, 0);
+        }
+      f32x4 sc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sc[j] = la == 0 ? d[j].x : la == 1 ? d[j].y : la == 2 ? d[j].z : d[j].w;
+      return sc;
     };
     auto phase_b = [&](const f32x4 sc, int n_cur) {
       // online softmax of column lr over rows 4 lg + r
@@ -415,7 +456,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       float mx = kNoMax;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[r] = (4 * lg + r < n_cur) ? sc[r] * qs : -INFINITY;
+        sv[r] = (4 * r + lg < n_cur) ? sc[r] * qs : -INFINITY;  // token 4r + lg
         mx = fmaxf(mx, sv[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -473,49 +514,46 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       n = tile_rows(tg, sl, t);
       load_tile(p, tg, sl, t - page_of(t) * tpp, n);
     };
-    // queries of this wave's 16 heads as the block-diagonal B operand, one
-    // pass: the largest magnitude (from the bf16 bit patterns) sets a power
-    // of two that puts it in [2^14, 2^15); lanes off the diagonal scale by
-    // 2^-200, which makes their operand exactly 0
+    // queries of this wave's 16 columns as the dense B operand: lane
+    // (column lr, k-group lg) holds quarter lg of its column's query row,
+    // 8 values per product.  The column's largest magnitude (from the bf16
+    // bit patterns, over its 4 lanes) sets a power of two that puts it in
+    // [2^14, 2^15).
     auto load_queries = [&]() {
-      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * KD;
-      u32x4 raw[KD / 8];
-      uint32_t mb = 0;
-      // only the diagonal lane of a column uses its row (the others hold
-      // zeros), so only it loads: a quarter of the requests
+      const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * KD + lg * (KD / 4);
+      u32x4 raw[KD / 32];
 #pragma unroll
-      for (int i = 0; i < KD / 8; ++i) raw[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (diag && col_ok) {
+      for (int i = 0; i < KD / 32; ++i) raw[i] = (u32x4){0u, 0u, 0u, 0u};
+      if (col_ok) {
 #pragma unroll
-        for (int i = 0; i < KD / 8; ++i) raw[i] = load_q8(qrow, i);
+        for (int i = 0; i < KD / 32; ++i) raw[i] = load_q8(qrow, i);
       }
+      uint32_t mb = 0;
 #pragma unroll
-      for (int i = 0; i < KD / 8; ++i)
+      for (int i = 0; i < KD / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           mb = max(mb, raw[i][e] & 0x7FFFu);
           mb = max(mb, (raw[i][e] >> 16) & 0x7FFFu);
         }
+      mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16));
+      mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
       int sh = 0;
       if (mb != 0) {
         int e;
         frexpf(__uint_as_float(mb << 16), &e);  // amax < 2^e
         sh = 15 - e;
       }
-      const int shq = diag ? sh : -200;
 #pragma unroll
-      for (int i = 0; i < KD / 8; ++i)
+      for (int i = 0; i < KD / 32; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[i][e] << 16), shq);
-          qb[i][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[i][e] & 0xFFFF0000u), shq);
+          qb[i][2 * e] = (_Float16)ldexpf(__uint_as_float(raw[i][e] << 16), sh);
+          qb[i][2 * e + 1] = (_Float16)ldexpf(__uint_as_float(raw[i][e] & 0xFFFF0000u), sh);
         }
-      // score scale of column lr: its shift lives in lane (lr, lr / 4)
-      const int sh_c = __shfl(sh, lr + 16 * (lr >> 2));
-      qs = ldexpf(base_scale, -sh_c);
+      qs = ldexpf(base_scale, -sh);
     };
 
-    // Two tiles in flight: tile k+1 is requested before tile k is computed.
     // The KV-head groups walk the stream's tiles in rotated orders (group kg
     // starts kg tiles later and wraps round), so the block-scale lines the
     // groups share are fetched by one group and found in L2 by the next,
@@ -534,23 +572,44 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       const int sl = slot_load(page_of(tile_at(k < nk ? k : 0)));
       return k < nk ? sl : -1;
     };
-    // two register sets, the loop unrolled by two so that each keeps its
-    // role (tile k in one, tile k + 1 requested into the other)
-    Packed pk0, pk1;
-    int n0 = 0, n1 = 0;
+    // register sets in static roles, the loop unrolled by their number:
+    // tile k + kSets - 1 is requested into the set whose tile was computed
+    // last, then tile k is computed.  The odd last tiles run after the loop,
+    // so that round it every set is requested on every path and each wait
+    // leaves the later tiles' loads in flight.
+    constexpr int kSets = KVFP4_GQA_SETS;
+    static_assert(kSets == 2 || kSets == 3, "2 or 3 register sets");
+    Packed pk0, pk1, pk2;
+    int n0 = 0, n1 = 0, n2 = 0;
     int sl_next = slot_for(0);
     issue(pk0, n0, tile_at(0), sl_next);  // requested before the queries are prepared
     sl_next = slot_for(1);
+    if constexpr (kSets == 3) {
+      issue(pk1, n1, tile_at(1 < nk ? 1 : 0), sl_next);
+      sl_next = slot_for(2);
+    }
     load_queries();
     auto step = [&](int k, Packed& cur, int& n_cur, Packed& nxt, int& n_nxt) {
-      issue(nxt, n_nxt, tile_at(k + 1 < nk ? k + 1 : 0), sl_next);
-      sl_next = slot_for(k + 2);
+      const int kn = k + kSets - 1;
+      issue(nxt, n_nxt, tile_at(kn < nk ? kn : 0), sl_next);
+      sl_next = slot_for(kn + 1);
       phase_b(phase_a(cur), n_cur);
       if constexpr (KVFP4_GQA_BALANCE) balance();
     };
-    for (int k = 0; k < nk; k += 2) {
-      step(k, pk0, n0, pk1, n1);
+    if constexpr (kSets == 3) {
+      int k = 0;
+      for (; k + 3 <= nk; k += 3) {
+        step(k, pk0, n0, pk2, n2);
+        step(k + 1, pk1, n1, pk0, n0);
+        step(k + 2, pk2, n2, pk1, n1);
+      }
+      if (k < nk) step(k, pk0, n0, pk2, n2);
       if (k + 1 < nk) step(k + 1, pk1, n1, pk0, n0);
+    } else {
+      for (int k = 0; k < nk; k += 2) {
+        step(k, pk0, n0, pk1, n1);
+        if (k + 1 < nk) step(k + 1, pk1, n1, pk0, n0);
+      }
     }
 
     // merge the NS streams of each KV-head group, then write the partial
