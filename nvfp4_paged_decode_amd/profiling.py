@@ -7,12 +7,13 @@ Three commands, each printing a short text summary (to stdout or --out):
       `rocprofv3 --kernel-trace --stats --output-format csv -d DIR` run.
 
   python -m nvfp4_paged_decode_amd.profiling counters --fetch DIR --write DIR
-          --workload NAME --copy-bytes N [--command TEXT]
+          --workload NAME [--yardstick-bytes N] [--command TEXT]
       HBM traffic per dispatch from two `rocprofv3 --pmc` runs (FETCH_SIZE,
       then WRITE_SIZE; both counters report KiB per dispatch).  Each counter
-      is scaled by what it reads for the plain device-to-device copies the
-      benchmark runs (`--copy-bytes` bytes read and as many written, summed
-      over every copy dispatch), so the result is in true bytes.  The
+      is scaled by what it reads for the benchmark's plain streams, which
+      nothing else launches: FETCH_SIZE by the read stream (N bytes read per
+      dispatch), WRITE_SIZE by the write stream (N bytes written), averaged
+      over their dispatches, so the result is in true bytes.  The
       summary ends with one `traffic` line per benchmark leg, which bench.py
       reads back together with the digest of that leg's kernel sources the
       counters were taken on (a figure for other sources is not reported).
@@ -116,16 +117,24 @@ def _counter(d: str, counter: str) -> dict[str, list[float]]:
     return per
 
 
-def counters(fetch_dir: str, write_dir: str, copy_bytes: int, workload: str) -> list[str]:
+#: The benchmark's plain streams (libkvfp4_yardstick.so): each dispatch of
+#: READ_STREAM reads, and each of WRITE_STREAM writes, the yardstick size.
+READ_STREAM, WRITE_STREAM = "read_kernel<8>", "write_kernel<4>"
+
+
+def counters(fetch_dir: str, write_dir: str, yardstick_bytes: int, workload: str) -> list[str]:
     fetch = _counter(fetch_dir, "FETCH_SIZE")
     write = _counter(write_dir, "WRITE_SIZE")
-    if "copyBuffer" not in fetch or "copyBuffer" not in write:
-        raise SystemExit("no copy dispatches to calibrate against")
-    f_cal = copy_bytes / (1024.0 * sum(fetch["copyBuffer"]))
-    w_cal = copy_bytes / (1024.0 * sum(write["copyBuffer"]))
-    out = [f"calibration: {len(fetch['copyBuffer'])} copy dispatches moving {copy_bytes} B read "
-           f"+ {copy_bytes} B written read FETCH_SIZE {sum(fetch['copyBuffer']):.0f} KiB, "
-           f"WRITE_SIZE {sum(write['copyBuffer']):.0f} KiB",
+    if READ_STREAM not in fetch or WRITE_STREAM not in write:
+        raise SystemExit("no read / write stream dispatches to calibrate against")
+    f_kib = sum(fetch[READ_STREAM]) / len(fetch[READ_STREAM])
+    w_kib = sum(write[WRITE_STREAM]) / len(write[WRITE_STREAM])
+    f_cal = yardstick_bytes / (1024.0 * f_kib)
+    w_cal = yardstick_bytes / (1024.0 * w_kib)
+    out = [f"calibration: {READ_STREAM} reads {yardstick_bytes} B per dispatch, FETCH_SIZE "
+           f"{f_kib:.0f} KiB ({len(fetch[READ_STREAM])} dispatches); {WRITE_STREAM} writes "
+           f"{yardstick_bytes} B per dispatch, WRITE_SIZE {w_kib:.0f} KiB "
+           f"({len(write[WRITE_STREAM])} dispatches)",
            f"scale: fetch x{f_cal:.4f}, write x{w_cal:.4f} (bytes per counter KiB / 1024)",
            "",
            f"{'kernel':<44} {'disp':>5} {'FETCH_KiB':>12} {'WRITE_KiB':>12} {'read_B':>14} {'written_B':>14}"]
@@ -245,7 +254,7 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
-    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--yardstick-bytes", type=int, default=1 << 30)
     c.add_argument("--workload", required=True)
     m = sub.add_parser("pmc")
     m.add_argument("dirs", nargs="+", help="one rocprofv3 --pmc output directory per pass")
@@ -258,7 +267,7 @@ def main(argv=None):
     elif a.cmd == "pmc":
         lines = pmc(a.dirs)
     else:
-        lines = counters(a.fetch, a.write, a.copy_bytes, a.workload)
+        lines = counters(a.fetch, a.write, a.yardstick_bytes, a.workload)
     head = [f"# {l}" for l in a.command.splitlines() if l.strip()]
     text = "\n".join(head + [""] + lines if head else lines) + "\n"
     if a.out:

@@ -1,4 +1,4 @@
-"""Host-side checks of the rocprofv3 summary helpers: the copy calibration
+"""Host-side checks of the rocprofv3 summary helpers: the stream calibration
 of FETCH_SIZE / WRITE_SIZE and the per-leg source digest that bench.py
 requires before it reports a traffic figure."""
 
@@ -17,15 +17,21 @@ def _write_counters(d, counter, rows):
             w.writerow({"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
 
 
-def test_counters_scale_by_copy_and_sum_legs(tmp_path):
+def test_counters_scale_by_streams_and_sum_legs(tmp_path):
+    rd = "void (anonymous namespace)::read_kernel<8>(unsigned int __vector(4) const*, unsigned long, unsigned int*)"
+    wr = "void (anonymous namespace)::write_kernel<4>(unsigned int __vector(4)*, unsigned long)"
     copy = "void copyBuffer(char*, char const*)"
-    # the copy of 1 MiB reads 512 KiB on FETCH_SIZE (x2 scale) and 1024 KiB written
+    # the 1 MiB read stream reads 512 KiB on FETCH_SIZE (x2 scale), the 1 MiB
+    # write stream 1024 KiB on WRITE_SIZE (x1); copies (which torch also
+    # launches for its own clones) play no part
     _write_counters(tmp_path / "f", "FETCH_SIZE", [
-        (copy, 512), ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 100),
+        (rd, 512), (rd, 512), (wr, 3), (copy, 99999),
+        ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 100),
         ("void kvfp4::(anonymous namespace)::decode_gqa_mfma_kernel<2>(int)", 30),
         ("kvfp4::(anonymous namespace)::merge_balanced_kernel<true>(int)", 10)])
     _write_counters(tmp_path / "w", "WRITE_SIZE", [
-        (copy, 1024), ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 50),
+        (rd, 0), (wr, 1024), (wr, 1024), (copy, 99999),
+        ("kvfp4::(anonymous namespace)::quantize_kernel(kvfp4::Geom)", 50),
         ("void kvfp4::(anonymous namespace)::decode_gqa_mfma_kernel<2>(int)", 1),
         ("kvfp4::(anonymous namespace)::merge_balanced_kernel<true>(int)", 2)])
     lines = P.counters(str(tmp_path / "f"), str(tmp_path / "w"), 1 << 20, "wl")
