@@ -140,12 +140,31 @@ def stream_yardsticks(torch, src, dst, stream, calls=COPY_CALLS):
     return out
 
 
+#: Untimed warm-up lasts at least this long as well as at least W steps, so
+#: that a timed block never starts from a GPU that idled through the seconds
+#: of host-side input generation.
+WARM_SECONDS = 0.25
+
+
+def warm_up(torch, step, min_calls):
+    """Run step() at least min_calls times and for at least WARM_SECONDS of
+    wall time, synchronizing at the end."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_calls or time.perf_counter() - t0 < WARM_SECONDS:
+        step(i)
+        i += 1
+        if i >= min_calls:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_block(torch, stream, calls, k, warmup):
     """Average ms of one call when `k` calls run back to back, cycling over
-    `calls` (one per buffer set), between one pair of events on `stream`."""
+    `calls` (one per buffer set), between one pair of events on `stream`;
+    before them at least `warmup` calls and WARM_SECONDS of them, untimed."""
     n = len(calls)
-    for i in range(warmup):
-        calls[i % n]()
+    warm_up(torch, lambda i: calls[i % n](), warmup)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -642,6 +661,12 @@ def main():
         # read 1 GiB (4x the 256 MiB Infinity Cache); a read leaves no dirty lines
         torch.sum(flush, dim=0, out=flush_sink)
 
+    # the reduction's first launch loads its code object, which held up the
+    # first timed block behind it (a decode block measured 74 instead of
+    # 61 us per call); launch it once, untimed
+    evict()
+    torch.cuda.synchronize()
+
     name = args.workload
     if args.extras_only:
         legs = Legs(K, torch, name, args.gs)
@@ -666,10 +691,12 @@ def main():
 
     # ---- the headline workload: K timed steps ---------------------------
     legs = Legs(K, torch, name, args.gs)
-    for leg in legs.order:  # warm-up steps, untimed
-        for i in range(args.warmup):
+
+    def warm_step(i):  # one untimed step: every leg once
+        for leg in legs.order:
             legs.calls[leg][i % SETS]()
-    torch.cuda.synchronize()
+
+    warm_up(torch, warm_step, args.warmup)
     t0 = time.perf_counter()
     evs = {}
     for leg in legs.order:
