@@ -16,26 +16,33 @@
 // are scaled per head by a power of two that puts their largest magnitude
 // in [2^14, 2^15) before the fp16 conversion (bf16 significands fit fp16's),
 // and the power of two is undone on the fp32 scores.  Probabilities are
-// rounded to fp16 for P.V.
+// rounded to fp16 for P.V, and the sums add those rounded values.
 //
-// Workgroup: NW = ceil(heads / 16) waves (two per SIMD at 128 heads), one
-// CU, all query heads of a page range (the balanced split of
-// decode_plan.hpp); wave w owns heads [16w, 16w + 16), so its output
-// accumulators (16 heads x 512 dims) fit the accumulation registers.
+// Workgroup: one CU, all query heads of a page range (the balanced split of
+// decode_plan.hpp).  Above 64 heads a wave owns 32 heads (two head blocks of
+// 16): its 32 heads x 512 dims of fp32 accumulators take the whole
+// accumulation register file, so the workgroup is 4 waves, one per SIMD;
+// every K and V^T fragment a wave reads from LDS then feeds both head
+// blocks, which halves the LDS reads per flop (the bound at 16 heads a
+// wave).  Up to 64 heads a wave owns 16.
 // Per 32-token tile:
 //  1. the workgroup dequantizes the tile once into LDS in its natural
 //     [token][576] layout (16-byte chunks XOR-swizzled by token bit 2,
 //     which keeps the row reads, the transposed reads and the staging
-//     writes free of bank conflicts); tiles are double-buffered, the next
-//     tile's bytes are requested before the current tile's products and
-//     staged after them;
+//     writes free of bank conflicts); tiles are double-buffered, packed
+//     bytes are requested two tiles ahead, and the staging work is spread
+//     between the score products;
 //  2. scores S^T = K Q^T per 16 tokens: A = latent rows read from LDS (16
-//     bytes per lane), B = the wave's queries, held in registers per
-//     sequence; lane (column c, group g) receives rows 4g..4g+3 of head c;
-//  3. online softmax per head (a lane's accumulators all belong to its own
-//     head column, so rescaling needs no exchange; the running maximum is
-//     only raised when a tile's maximum exceeds it by more than 2^8 in
-//     exp2 units, which keeps rescales rare and probabilities below 2^8);
+//     bytes per lane), B = the wave's queries (the first head block's in
+//     registers, the second's in LDS); lane (column c, group g) receives
+//     rows 4g..4g+3 of head c.  These products use ordinary VGPRs (issued
+//     through inline asm), since the accumulators fill the accumulation
+//     registers;
+//  3. softmax without rescaling: a column's maximum is fixed by its first
+//     tile and later probabilities 2^(s - m) are used as they are (fp16
+//     holds them up to 65504); if any column's sum ends a segment
+//     non-finite, the workgroup votes for a second pass that finds every
+//     column's maximum and a third that repeats the first with it;
 //  4. O^T += V^T P^T over all 32 tokens at once: the B operand is exactly
 //     the lane's own 8 probabilities (rows 4g..4g+3 of both 16-token
 //     halves), and the A operand (V^T) comes from the same natural tile
