@@ -239,7 +239,7 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
   const int h = threadIdx.x >> 6;  // wave = KV head
   const int lane = threadIdx.x & 63;
   const int s = lane >> 3, c = lane & 7;
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = split_index(blockIdx.x, nwg);  // position in the split
   const float qscale = a.softmax_scale * a.gs_k * kLog2e;
 
   BalancedRange rng;

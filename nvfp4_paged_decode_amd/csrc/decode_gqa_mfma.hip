@@ -289,7 +289,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   // load rounds: lane (4 la + lb) + 16 lg takes quarter lg of the K/V rows of
   // token 4j + la, KV-head slot lb
   const int la = lr >> 2, lb = lr & 3;
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = split_index(blockIdx.x, nwg);  // position in the split
   const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
 
   // The 8 waves sit two to a SIMD (waves w and w ^ 4), and a SIMD issues

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;  // head column (or token row), k-group
-  const int w = blockIdx.x, nwg = gridDim.x;
+  const int nwg = gridDim.x, w = split_index(blockIdx.x, nwg);  // position in the split
   const float base_scale = a.softmax_scale * a.gs_k * kLog2e;
   const long long page_bytes = g.packed_bytes(), data_bytes = g.data_bytes();
   const int tiles_per_page = g.T / kTile;

@@ -31,6 +31,18 @@ __device__ inline long long range_begin(long long ptot, int w, int nwg) {
   return (long long)w * ptot / nwg;
 }
 
+// Workgroups are dispatched to the 8 XCDs (each with its own L2) round
+// robin: workgroup b runs on XCD b % 8.  The balanced split is numbered so
+// that each XCD holds a contiguous block of it; neighbours in the split,
+// which hold pages of the same sequences (its query rows, page-table lines
+// and scale lines), then share an L2.  A bijection of [0, n).
+constexpr int kXcds = 8;
+__device__ inline int split_index(int b, int n) {
+  const int x = b % kXcds, k = b / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Wave-uniform copies (values every lane already agrees on), so that the
 // compiler keeps them in scalar registers and can build buffer resources
 // and branch on them without per-lane loops.
