@@ -261,8 +261,8 @@ int32_t kvfp4_paged_decode_attention(
  * object, kept until the process ends); this call allocates nothing.
  * Sizes whose kvfp4_decode_workspace_bytes() exceeds 96 MiB are rejected
  * with KVFP4_ERR_WORKSPACE before anything is launched (the MLA shape of
- * batch 64 x 128 heads needs 84 MiB; Llama- and Qwen-shaped batches of 32
- * need under 5 MiB).  Every call on a device shares that device's scratch:
+ * batch 64 x 128 heads needs about 41 MiB; Llama- and Qwen-shaped batches
+ * of 32 need under 3 MiB).  Every call on a device shares that device's scratch:
  * calls that overlap in time on one device (concurrent streams, or threads
  * without ordering) race on it and must not be issued; calls ordered on one
  * stream are fine.  The scratch needs no clearing between calls. */

@@ -489,8 +489,13 @@ int32_t decode_call(const kvfp4_geometry* g, const void* packed_pool, int32_t pa
   a.nwg = plan.nwg;
   size_t partials = plan.kernel == 0 ? (size_t)batch * num_q_heads * plan.splits
                                      : (size_t)(plan.nwg + batch) * num_q_heads;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = a.ws_o + partials * v_dim;
+  if (plan.kernel == 0) {  // generic kernel: fp32 partial outputs
+    a.ws_o = (float*)workspace;
+    a.ws_ml = a.ws_o + partials * v_dim;
+  } else {  // balanced kernels: fp16 partial outputs (v_dim is even)
+    a.ws_oh = (uint16_t*)workspace;
+    a.ws_ml = reinterpret_cast<float*>(a.ws_oh + partials * v_dim);
+  }
   a.ws_idx = reinterpret_cast<int32_t*>(a.ws_ml + partials * 2);
   hipError_t e = kvfp4::launch_decode(plan, a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

@@ -59,6 +59,22 @@ __device__ inline uint32_t gt_threshold(double M, bool strict) {
   return strict ? bf16_bits_directed(M, false) : bf16_bits_directed(M, true) - 1u;
 }
 
+// 4 floats as fp16 (round to nearest even), packed for one 8-byte store,
+// and back.  The unpack works on the two 32-bit words with shifts: a
+// bit_cast of a vector element (w.y) to a 2 x fp16 vector compiled to a
+// copy of the low pair here.
+__device__ inline u32x2 pack_f16x4(f32x4 v) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 lo = {(_Float16)v.x, (_Float16)v.y}, hi = {(_Float16)v.z, (_Float16)v.w};
+  return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+__device__ inline uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ inline float f16_value(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ inline f32x4 unpack_f16x4(u32x2 w) {
+  return (f32x4){f16_value((uint16_t)(w.x & 0xFFFFu)), f16_value((uint16_t)(w.x >> 16)),
+                 f16_value((uint16_t)(w.y & 0xFFFFu)), f16_value((uint16_t)(w.y >> 16))};
+}
+
 // OCP E4M3FN value of a scale byte (NaN for 0x7F / 0xFF), as fp32 (exact).
 __device__ inline float e4m3_to_float(uint32_t code) {
   uint32_t e = (code >> 3) & 0xF, m = code & 7;
@@ -172,7 +188,10 @@ struct DecodeArgs {
   int splits;
   int pages_per_split;
   int nwg;
-  float* ws_o;           // partial outputs, v_dim floats each
+  float* ws_o;           // generic kernel: partial outputs, v_dim floats each
+  // balanced kernels: partial outputs divided by their sum, v_dim fp16 each
+  // (a weighted average of value rows: |o / l| <= 2688, which fp16 holds)
+  uint16_t* ws_oh;
   float* ws_ml;          // partial (max, sum), scores in log2 units
   // Balanced kernels: the first and last workgroup whose range holds pages
   // of sequence b ([batch][2], written for every sequence with pages), then

@@ -225,13 +225,17 @@ constexpr int kBalMergeWide = 128, kBalMergeNarrow = 256;
 // Merge for the balanced kernels: sequence b's partials sit in slots w + b
 // for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
 // (recorded by the decode kernel with the batch's page count).  One
-// workgroup per (head, sequence), two dependent rounds of global reads:
-// the sequence's length and slot range, then every partial at once.
-// Slots are split over G thread groups (G = threads / (v_dim / 4) when
-// v_dim is small, else 1); a group folds its slots with a running maximum,
-// kMergeBatch of them per round of loads, and the groups combine through
-// LDS.  VEC (v_dim % 4 == 0, 16-byte aligned partials, 8-byte aligned
-// out): a thread owns 4 columns; otherwise one column per thread, G = 1.
+// workgroup per (head, sequence), two rounds of global reads: the
+// sequence's length, slot range and the batch's page count together, then
+// every partial at once.  Loads are unconditional, from slot and column
+// indices clamped into range, and whether a slot holds a partial is decided
+// after they are all issued: loads under a condition become branches that
+// wait for each load before the next.  Slots are split over G thread
+// groups (G = threads / (v_dim / 4) when v_dim is small, else 1); a group
+// folds its slots with a running maximum, kMergeBatch of them per round of
+// loads, and the groups combine through LDS.  VEC (v_dim % 4 == 0, 16-byte
+// aligned partials, 8-byte aligned out): a thread owns 4 columns;
+// otherwise one column per thread, G = 1.
 template <bool VEC, int K4, int kMergeThreads>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
   static_assert(!VEC || K4 * 4 * kMergeThreads >= 512, "v_dim up to 512");
@@ -239,20 +243,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
   __shared__ float s_m[kMergeThreads], s_l[kMergeThreads];
   __shared__ f32x4 s_acc[kMergeThreads];
   const long long row = (long long)b * a.hq + head;
-  const int L = clamped_len(a, b);
   const int nwg = a.nwg;
+  // first round: all three requested before any is used
+  const int L = clamped_len(a, b);
   int w_lo = a.ws_idx[2 * b], w_hi = a.ws_idx[2 * b + 1];
   const long long ptot = a.ws_idx[2 * a.batch];
-  if (L == 0) {
-    for (int c = tid; c < a.v_dim; c += kMergeThreads) a.out[row * a.v_dim + c] = 0;
-    if (tid == 0 && a.lse) a.lse[row] = -INFINITY;
-    return;
-  }
-  // the decode kernel wrote both for every sequence with pages; clamp anyway
+  // the decode kernel wrote the range for every sequence with pages (and
+  // nothing for the others, nor anything at all for a batch without pages:
+  // those get an empty range, so a zero output and lse -inf); clamp anyway
   w_lo = w_lo < 0 ? 0 : (w_lo > nwg - 1 ? nwg - 1 : w_lo);
   w_hi = w_hi < w_lo ? w_lo : (w_hi > nwg - 1 ? nwg - 1 : w_hi);
-  auto holds = [&](int v) {  // slot v + b holds a partial: v's range is not empty
-    return (long long)v * ptot / nwg < (long long)(v + 1) * ptot / nwg;
+  if (L == 0 || ptot <= 0) w_hi = w_lo - 1;
+  // slot v + b holds a partial when v's page range is not empty, which
+  // every range is when the batch has at least one page per workgroup
+  const bool all_hold = ptot >= nwg;
+  auto holds = [&](int v) {
+    return all_hold || (long long)v * ptot / nwg < (long long)(v + 1) * ptot / nwg;
   };
 
   const int D4 = a.v_dim / 4;
@@ -269,47 +275,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
 #pragma unroll
   for (int k = 0; k < K1; ++k) o1[k] = 0.f;
   float mg = -INFINITY, lg = 0.f;
-  if (grp < G) {
-    for (int v0 = w_lo + grp; v0 <= w_hi; v0 += G * kMergeBatch) {
-      // every load of this round is issued before any is used
+  {
+    for (int v0 = w_lo + grp; grp < G && v0 <= w_hi; v0 += G * kMergeBatch) {
       float mv[kMergeBatch], lv[kMergeBatch];
-      f32x4 ov4[kMergeBatch][K4];
-      float ov1[kMergeBatch][K1];
+      u32x2 raw4[kMergeBatch][K4];
+      uint16_t raw1[kMergeBatch][K1];
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) {
-        const int v = v0 + i * G;
-        const bool ok = v <= w_hi && holds(v);
-        const long long sp = ((long long)v + b) * a.hq + head;
-        mv[i] = ok ? a.ws_ml[sp * 2] : -INFINITY;
-        lv[i] = ok ? a.ws_ml[sp * 2 + 1] : 0.f;
-        const float* src = a.ws_o + sp * a.v_dim;
+        const int v = v0 + i * G, vc = v <= w_hi ? v : w_hi;  // in range
+        const long long sp = ((long long)vc + b) * a.hq + head;
+        mv[i] = a.ws_ml[sp * 2];
+        lv[i] = a.ws_ml[sp * 2 + 1];
+        const uint16_t* src = a.ws_oh + sp * a.v_dim;  // o / l in fp16
         if (VEC) {
 #pragma unroll
           for (int k = 0; k < K4; ++k) {
             const int c = d4 + k * kMergeThreads;
-            ov4[i][k] = (ok && c < D4) ? *reinterpret_cast<const f32x4*>(src + 4 * c)
-                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+            raw4[i][k] = *reinterpret_cast<const u32x2*>(src + 4 * (c < D4 ? c : D4 - 1));
           }
         } else {
 #pragma unroll
           for (int k = 0; k < K1; ++k) {
             const int c = tid + k * kMergeThreads;
-            ov1[i][k] = (ok && c < a.v_dim) ? src[c] : 0.f;
+            raw1[i][k] = src[c < a.v_dim ? c : a.v_dim - 1];
           }
         }
       }
 #pragma unroll
       for (int i = 0; i < kMergeBatch; ++i) {
-        if (mv[i] == -INFINITY) continue;  // no partial in this slot
+        const int v = v0 + i * G;
+        if (v > w_hi || !holds(v) || mv[i] == -INFINITY) continue;  // no partial here
         const float mn = fmaxf(mg, mv[i]);
-        const float so = exp2f(mg - mn), sn = exp2f(mv[i] - mn);  // exp2(-inf) = 0
-        lg = lg * so + lv[i] * sn;
+        // slot weight exp2(m_i - mn) l_i: the stored output is o_i / l_i
+        const float so = exp2f(mg - mn), sn = exp2f(mv[i] - mn) * lv[i];  // exp2(-inf) = 0
+        lg = lg * so + sn;
         if (VEC) {
 #pragma unroll
-          for (int k = 0; k < K4; ++k) o4[k] = o4[k] * so + ov4[i][k] * sn;
+          for (int k = 0; k < K4; ++k) {
+            const int c = d4 + k * kMergeThreads;
+            const f32x4 x = c < D4 ? unpack_f16x4(raw4[i][k]) : (f32x4){0.f, 0.f, 0.f, 0.f};
+            o4[k] = o4[k] * so + x * sn;
+          }
         } else {
 #pragma unroll
-          for (int k = 0; k < K1; ++k) o1[k] = o1[k] * so + ov1[i][k] * sn;
+          for (int k = 0; k < K1; ++k) {
+            const int c = tid + k * kMergeThreads;
+            const float x = c < a.v_dim ? f16_value(raw1[i][k]) : 0.f;
+            o1[k] = o1[k] * so + x * sn;
+          }
         }
         mg = mn;
       }
@@ -387,9 +400,11 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
     p.nwg = (int)(nwg > 0 ? nwg : 1);
     p.splits = 0;
     p.pages_per_split = 0;
-    // partials, then the merge's index ([batch][2] + the page count, padded)
-    p.workspace_bytes = (size_t)(p.nwg + batch) * hq * (size_t)(v_dim + 2) * sizeof(float) +
-                        (((size_t)2 * batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
+    // partial outputs (fp16), their (max, sum) (fp32), then the merge's
+    // index ([batch][2] + the page count, padded)
+    p.workspace_bytes =
+        (size_t)(p.nwg + batch) * hq * ((size_t)v_dim * sizeof(uint16_t) + 2 * sizeof(float)) +
+        (((size_t)2 * batch + 1) * sizeof(int32_t) + 15) / 16 * 16;
     return p;
   }
   p.kernel = 0;
@@ -434,7 +449,7 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   if (plan.kernel == 0) {
     hipLaunchKernelGGL(merge_kernel, dim3(a.hq, a.batch), dim3(kMergeThreads), 0, stream, a);
   } else {
-    const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_o & 15) == 0 &&
+    const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_oh & 15) == 0 &&
                      ((uintptr_t)a.out & 7) == 0;
     // the balanced kernels have v_dim <= 512: one f32x4 column block a thread
     if (a.v_dim <= 128) {

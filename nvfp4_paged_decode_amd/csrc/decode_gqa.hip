@@ -330,11 +330,13 @@ __global__ __launch_bounds__(512) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         const long long head = (long long)h * G + i;
-        float* o = a.ws_o + (slotp * a.hq + head) * kD + c * 16;
+        // the partial output divided by its sum, in fp16
+        uint16_t* o = a.ws_oh + (slotp * a.hq + head) * kD + c * 16;
+        const float il = st.l[i] > 0.f ? 1.f / st.l[i] : 0.f;
 #pragma unroll
         for (int d = 0; d < 16; d += 4)
-          *reinterpret_cast<float4*>(o + d) =
-              make_float4(st.acc[i][d], st.acc[i][d + 1], st.acc[i][d + 2], st.acc[i][d + 3]);
+          *reinterpret_cast<u32x2*>(o + d) = pack_f16x4(
+              (f32x4){st.acc[i][d], st.acc[i][d + 1], st.acc[i][d + 2], st.acc[i][d + 3]} * il);
         if (c == 0) {
           a.ws_ml[(slotp * a.hq + head) * 2] = st.m[i];
           a.ws_ml[(slotp * a.hq + head) * 2 + 1] = st.l[i];

@@ -638,6 +638,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
       }
       const long long slotp = ((long long)w + b) * a.hq + head;
       const int d0 = s * DW + lg * DL;
+      // the partial output divided by its sum, in fp16
+      const float il = Ls > 0.f ? 1.f / Ls : 0.f;
       if (col_ok) {
         if constexpr (DL % 4 == 0) {
 #pragma unroll
@@ -646,7 +648,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
 #pragma unroll
             for (int u = 0; u < NS; ++u)
               o += *reinterpret_cast<const f32x4*>(&mg.o[gt * NS + u][lr][d0 + i]) * wt[u];
-            *reinterpret_cast<f32x4*>(a.ws_o + slotp * KD + d0 + i) = o;
+            *reinterpret_cast<u32x2*>(a.ws_oh + slotp * KD + d0 + i) = pack_f16x4(o * il);
           }
         } else {
 #pragma unroll
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
             float o = 0.f;
 #pragma unroll
             for (int u = 0; u < NS; ++u) o += mg.o[gt * NS + u][lr][d0 + i] * wt[u];
-            a.ws_o[slotp * KD + d0 + i] = o;
+            a.ws_oh[slotp * KD + d0 + i] = f16_bits(o * il);
           }
         }
         if (s == 0 && lg == 0) {
@@ -720,7 +722,7 @@ bool gqa_mfma_supported(const Geom& g, int hq, int v_dim) {
 
 hipError_t launch_decode_gqa_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (!gqa_mfma_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
-  if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
+  if (((uintptr_t)a.ws_oh & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
   return a.g.D == 64 ? launch_kd<64>(a, stream) : launch_kd<128>(a, stream);
 }
 

@@ -105,6 +105,17 @@ struct MlaLds2 {
   f16x8 q1[4][kKs][64];  // [wave][k-step][lane]
 };
 
+// Partial-output staging (after a segment's passes, in the tile buffers):
+// each wave 16 rows of kCh fp32 dims at a time, pitch kCh + 4 (the widest
+// power-of-two chunk whose NW waves' rows fit).
+template <int NW>
+struct OutStage {
+  static constexpr int kBuf = (int)sizeof(_Float16) * 2 * kTile * kPitch;
+  static constexpr int fits(int ch) { return NW * 16 * (ch + 4) * 4 <= kBuf; }
+  static constexpr int kCh = fits(512) ? 512 : fits(256) ? 256 : 128;
+  static_assert(fits(kCh), "staging rows fit the tile buffers");
+};
+
 // Swizzle of staged row `row`: 16-byte chunk c sits at chunk c ^ swz(row).
 // LDS has 32 banks of 4 bytes; with the pitch at 8 banks mod 32, rows r
 // and r + 4 would collide for 16-byte accesses of 8 lanes, which the flip
@@ -609,26 +620,59 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
     mode = 1;
     }
 
-    // partial for slot (workgroup + sequence): lane holds head column `col`
-    // of each head block, dims 16 dt + 4 grp + 0..3 in acc[hb][dt]
+    // Partial for slot (workgroup + sequence), divided by its sum, in fp16.
+    // Lane (col, grp) holds head `col` of each head block, dims 16 dt +
+    // 4 grp + 0..3 in acc[hb][dt].  The accumulators go through LDS (each
+    // wave its own rows of the free tile buffers, kOutCh dims of 16 heads at
+    // a time) so that every global store writes 16 bytes of one head row and
+    // whole lines, and so that the accumulators are only stored, never
+    // operands of vector ALU work, which keeps them in the accumulation
+    // registers through the tile loop.
+    constexpr int kOutCh = OutStage<NW>::kCh, kOutPitch = kOutCh + 4;
+    __syncthreads();  // every wave is done with the tile buffers
+    float* const ob = reinterpret_cast<float*>(smem) + wave * (16 * kOutPitch);
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       float lt = l[hb];
       lt += __shfl_xor(lt, 16);
       lt += __shfl_xor(lt, 32);
-      const int head = HW * wave + 16 * hb + col;
-      if (head < a.hq) {
-        const long long slotp = ((long long)w + b) * a.hq + head;
-        float* dst = a.ws_o + slotp * kDv;
+      const float il = lt > 0.f ? 1.f / lt : 0.f;  // lane col: head col's
+      const int head0 = HW * wave + 16 * hb;
+      if (grp == 0 && head0 + col < a.hq) {
+        const long long slotp = ((long long)w + b) * a.hq + head0 + col;
+        a.ws_ml[slotp * 2] = m[hb];
+        a.ws_ml[slotp * 2 + 1] = lt;
+      }
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt)
-          *reinterpret_cast<f32x4*>(dst + 16 * dt + 4 * grp) = acc[hb][dt];
-        if (grp == 0) {
-          a.ws_ml[slotp * 2] = m[hb];
-          a.ws_ml[slotp * 2 + 1] = lt;
+      for (int ch = 0; ch < kDv / kOutCh; ++ch) {
+#pragma unroll
+        for (int dt = 0; dt < kOutCh / 16; ++dt)
+          *reinterpret_cast<f32x4*>(ob + col * kOutPitch + 16 * dt + 4 * grp) =
+              acc[hb][ch * (kOutCh / 16) + dt];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane: 8 dims of row (16 heads x kOutCh dims, kOutCh / 8 lanes a row)
+        constexpr int kLanesRow = kOutCh / 8, kRowsIt = 64 / kLanesRow;
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += kRowsIt) {
+          const int r = r0 + lane / kLanesRow, c8 = 8 * (lane % kLanesRow);
+          const float ilr = __shfl(il, r);
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(ob + r * kOutPitch + c8);
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(ob + r * kOutPitch + c8 + 4);
+          if (head0 + r < a.hq) {
+            const long long slotp = ((long long)w + b) * a.hq + head0 + r;
+            const u32x2 h0 = pack_f16x4(x0 * ilr), h1 = pack_f16x4(x1 * ilr);
+            *reinterpret_cast<u32x4*>(a.ws_oh + slotp * kDv + ch * kOutCh + c8) =
+                (u32x4){h0.x, h0.y, h1.x, h1.y};
+          }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
+    __syncthreads();  // the tile buffers hold the next segment's tiles again
   }
 }
 
@@ -652,7 +696,7 @@ bool mla_supported(const Geom& g, int hq, int v_dim) {
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream) {
   if (!mla_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
-  if (((uintptr_t)a.ws_o & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
+  if (((uintptr_t)a.ws_oh & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
   // up to 64 heads: 16 a wave (one to four waves); more: 32 a wave (four),
   // or with KVFP4_MLA_HB1 16 a wave (up to eight)
 #if KVFP4_MLA_HB1

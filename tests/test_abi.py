@@ -200,10 +200,11 @@ def test_decode_rejects_invalid_arguments(lib, case, code):
 def test_decode_workspace_size(lib):
     g = K.Geometry(2, 64, 8, 128)
     n = lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 32, 32, 128, 8192)
-    # partials (m, l, 128 dims) for (workgroups + batch) x 32 heads, then the
-    # merge index (first/last workgroup per sequence and the page count)
+    # partials (128 fp16 dims, fp32 m and l) for (workgroups + batch) x 32
+    # heads, then the merge index (first/last workgroup per sequence and the
+    # page count)
     index = -(-(2 * 32 + 1) * 4 // 16) * 16
-    assert n > index and (n - index) % (32 * 130 * 4) == 0
+    assert n > index and (n - index) % (32 * (128 * 2 + 2 * 4)) == 0
     assert lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 32, 30, 128, 8192) == 0
     assert lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), 0, 32, 128, 8192) == 0
 
@@ -281,21 +282,21 @@ def test_rope_codec_needs_16_byte_slots(lib):
 ])
 def test_decode_routing_by_workspace(lib, geom, hq, balanced):
     """The workspace size tells which plan a shape gets: the balanced
-    kernels hold (workgroups + batch) partial rows and the merge index, the
-    generic kernel batch x heads x splits rows.  Without a GPU the plan
-    assumes 256 compute units."""
+    kernels hold (workgroups + batch) partial rows (fp16 outputs, fp32 max
+    and sum) and the merge index, the generic kernel batch x heads x splits
+    rows of fp32.  Without a GPU the plan assumes 256 compute units."""
     g = K.Geometry(*geom)
     batch, hint = 4, 1024
     v = 512 if geom[0] == 1 else geom[3]
     n = lib.kvfp4_decode_workspace_bytes(ctypes.byref(g), batch, hq, v, hint)
-    row = hq * (v + 2) * 4
+    row = hq * (v * 2 + 2 * 4)
     index = -(-(2 * batch + 1) * 4 // 16) * 16
     pages = batch * -(-hint // geom[1])
     balanced_bytes = (min(256, pages) + batch) * row + index
     if balanced:
         assert n == balanced_bytes
     else:
-        assert n != balanced_bytes and n % row == 0
+        assert n != balanced_bytes and n % (hq * (v + 2) * 4) == 0
 
 
 # --- the Python binding's checks, made before any pointer is taken --------
