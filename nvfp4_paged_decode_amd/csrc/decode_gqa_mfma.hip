@@ -154,15 +154,20 @@ struct ChunkOf;
 template <>
 struct ChunkOf<128> {
   typedef u32x4 type;
+  typedef uint16_t scale;
 };
 template <>
 struct ChunkOf<64> {
   typedef u32x2 type;
+  typedef uint8_t scale;
 };
+// The scale bytes are kept at their loaded width: widened to 32 bits in the
+// register set, the widening (an AND after the load) was placed right after
+// the first tile's request and waited for it before the next was requested.
 template <int KD>
 struct Packed {
   typename ChunkOf<KD>::type k[4], v[4];
-  uint32_t ks[4], vs[4];
+  typename ChunkOf<KD>::scale ks[4], vs[4];
 };
 
 __device__ inline f16x2 fp4x2(uint32_t w, int sel) {
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   note_total(a, w, rng.ptot);
   long long seq_start = rng.start_first;
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
-    const int L = uniform(clamped_len(a, b));
+    const int L = seq_len(a, rng, b);
     const int npages = (L + g.T - 1) / g.T;
     const long long first = seq_start;
     seq_start += npages;
@@ -518,16 +523,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     // (column lr, k-group lg) holds quarter lg of its column's query row,
     // 8 values per product.  The column's largest magnitude (from the bf16
     // bit patterns, over its 4 lanes) sets a power of two that puts it in
-    // [2^14, 2^15).
-    auto load_queries = [&]() {
+    // [2^14, 2^15).  The loads are requested before the first tile's and
+    // are unconditional (a padding column reads head 0's row and zeroes
+    // it), so that waiting for them leaves the tile's loads in flight.
+    u32x4 qraw[KD / 32];
+    auto request_queries = [&]() {
       const uint16_t* qrow = a.q + ((long long)b * a.hq + head) * KD + lg * (KD / 4);
+#pragma unroll
+      for (int i = 0; i < KD / 32; ++i) qraw[i] = load_q8(qrow, i);
+    };
+    auto load_queries = [&]() {
       u32x4 raw[KD / 32];
 #pragma unroll
-      for (int i = 0; i < KD / 32; ++i) raw[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (col_ok) {
-#pragma unroll
-        for (int i = 0; i < KD / 32; ++i) raw[i] = load_q8(qrow, i);
-      }
+      for (int i = 0; i < KD / 32; ++i) raw[i] = col_ok ? qraw[i] : (u32x4){0u, 0u, 0u, 0u};
       uint32_t mb = 0;
 #pragma unroll
       for (int i = 0; i < KD / 32; ++i)
@@ -581,9 +589,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
     static_assert(kSets == 2 || kSets == 3, "2 or 3 register sets");
     Packed pk0, pk1, pk2;
     int n0 = 0, n1 = 0, n2 = 0;
-    int sl_next = slot_for(0);
-    issue(pk0, n0, tile_at(0), sl_next);  // requested before the queries are prepared
-    sl_next = slot_for(1);
+    // Start of the segment, three rounds of requests: the queries and the
+    // first two page-table entries, then the first tile, whose loads are
+    // issued before the queries are waited for.  The empty asm statements
+    // pin that order (the compiler would otherwise use each entry before
+    // requesting the next, and convert the queries before the tile's loads).
+    request_queries();
+    const int pg0 = page_of(tile_at(0)), pg1 = page_of(tile_at(1 < nk ? 1 : 0));
+    int e0 = bt_row[pg0 < (int)p_hi ? pg0 : (int)p_hi - 1];
+    int e1 = bt_row[pg1 < (int)p_hi ? pg1 : (int)p_hi - 1];
+    asm volatile("" : "+s"(e0), "+s"(e1));
+    int sl_next = (0 < nk && pg0 < (int)p_hi) ? e0 : -1;
+    const int sl_after = (1 < nk && pg1 < (int)p_hi) ? e1 : -1;
+    issue(pk0, n0, tile_at(0), sl_next);
+#pragma unroll
+    for (int i = 0; i < KD / 32; ++i) asm volatile("" : "+v"(qraw[i]) : : "memory");
+    sl_next = sl_after;
     if constexpr (kSets == 3) {
       issue(pk1, n1, tile_at(1 < nk ? 1 : 0), sl_next);
       sl_next = slot_for(2);

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   note_total(a, w, rng.ptot);
   long long seq_start = rng.start_first;
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
-    const int L = uniform(clamped_len(a, b));
+    const int L = seq_len(a, rng, b);
     const int npages = (L + g.T - 1) / g.T;
     const long long first = seq_start;
     seq_start += npages;

@@ -27,7 +27,11 @@ __device__ inline int pages_of(const DecodeArgs& a, int b) {
   return (clamped_len(a, b) + a.g.T - 1) / a.g.T;
 }
 
+// floor(w P / nwg), in 32-bit arithmetic whenever P nwg fits (a 64-bit
+// division is a long software sequence on the startup path)
 __device__ inline long long range_begin(long long ptot, int w, int nwg) {
+  if (ptot <= (long long)(0xFFFFFFFFu / (unsigned)nwg))
+    return (long long)((unsigned)w * (unsigned)ptot / (unsigned)nwg);
   return (long long)w * ptot / nwg;
 }
 
@@ -59,6 +63,7 @@ struct BalancedRange {
   long long p_end;
   int b_first;            // first sequence with pages in the range (batch if none)
   long long start_first;  // index of its first page in the concatenation
+  int len0;               // lane l: clamped length of sequence l (l < 64)
 };
 
 // Wave-level inclusive prefix sum of an int over 64 lanes.
@@ -72,11 +77,17 @@ __device__ inline int wave_incl_scan(int v) {
   return v;
 }
 
-// Computed by every wave on its own (no LDS, no barrier).
+// Computed by every wave on its own (no LDS, no barrier).  The first 64
+// lengths are read once and kept (len0; most batches have at most 64
+// sequences), so that the scan, the range search and the segment loop wait
+// for one round of length loads.
 __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, BalancedRange& r) {
   const int lane = threadIdx.x & 63;
-  long long tot = 0;
-  for (int base = 0; base < a.batch; base += 64) {
+  r.len0 = lane < a.batch ? clamped_len(a, lane) : 0;
+  const int np0 = (r.len0 + a.g.T - 1) / a.g.T;
+  const int incl0 = wave_incl_scan(np0);
+  long long tot = __shfl(incl0, 63);
+  for (int base = 64; base < a.batch; base += 64) {
     int b = base + lane;
     int np = b < a.batch ? pages_of(a, b) : 0;
     tot += __shfl(wave_incl_scan(np), 63);
@@ -91,8 +102,8 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
   long long run = 0;
   for (int base = 0; base < a.batch; base += 64) {
     int b = base + lane;
-    int np = b < a.batch ? pages_of(a, b) : 0;
-    int incl = wave_incl_scan(np);
+    int np = base == 0 ? np0 : (b < a.batch ? pages_of(a, b) : 0);
+    int incl = base == 0 ? incl0 : wave_incl_scan(np);
     bool hit = np > 0 && run + incl > r.p_begin;
     unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
     if (m) {
@@ -103,6 +114,12 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
     }
     run = uniform(run + __shfl(incl, 63));
   }
+}
+
+// Clamped length of sequence b (wave-uniform), from the lengths the range
+// search kept when b < 64.
+__device__ inline int seq_len(const DecodeArgs& a, const BalancedRange& r, int b) {
+  return b < 64 ? __builtin_amdgcn_readlane(r.len0, b) : uniform(clamped_len(a, b));
 }
 
 // Records for the merge which workgroups hold sequence b's first and last
