@@ -146,12 +146,12 @@ def stream_yardsticks(torch, src, dst, stream, calls=COPY_CALLS):
 WARM_SECONDS = 0.25
 
 
-def warm_up(torch, step, min_calls):
-    """Run step() at least min_calls times and for at least WARM_SECONDS of
+def warm_up(torch, step, min_calls, seconds=WARM_SECONDS):
+    """Run step() at least min_calls times and for at least `seconds` of
     wall time, synchronizing at the end."""
     t0 = time.perf_counter()
     i = 0
-    while i < min_calls or time.perf_counter() - t0 < WARM_SECONDS:
+    while i < min_calls or time.perf_counter() - t0 < seconds:
         step(i)
         i += 1
         if i >= min_calls:
@@ -692,11 +692,14 @@ def main():
     # ---- the headline workload: K timed steps ---------------------------
     legs = Legs(K, torch, name, args.gs)
 
-    def warm_step(i):  # one untimed step: every leg once
-        for leg in legs.order:
-            legs.calls[leg][i % SETS]()
-
-    warm_up(torch, warm_step, args.warmup)
+    # untimed warm-up: each leg in a block of its own, back to back and after
+    # the cache flush, as the timed blocks run (interleaved with the codec
+    # legs, a decode call instead pays for their write-back: in a kernel
+    # trace the warm-up's calls then misstate the timed ones)
+    for leg in legs.order:
+        evict()
+        warm_up(torch, lambda i, leg=leg: legs.calls[leg][i % SETS](), args.warmup,
+                WARM_SECONDS / len(legs.order))
     t0 = time.perf_counter()
     evs = {}
     for leg in legs.order:

@@ -48,7 +48,7 @@ LEG_SOURCES = {
     "append": ("codec.hip", "common.hpp"),
     "gather": ("codec.hip", "common.hpp"),
     "decode": ("decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip", "decode_mla.hip",
-               "common.hpp"),
+               "decode_plan.hpp", "common.hpp"),
 }
 
 
