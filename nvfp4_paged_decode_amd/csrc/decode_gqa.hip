@@ -21,8 +21,11 @@
 //            E4M3 scale, summed over the 8 lanes of a stream by DPP;
 //   softmax: online per stream, one rescale per page at most;
 //   P.V:     rows are taken in pairs so that dot2 runs along the token
-//            axis: (p_r sv_r, p_r' sv_r') . (c_r[d], c_r'[d]), where sv is
-//            the value block scale; accumulation in fp32.
+//            axis: (p_r, p_r') . (v_r[d], v_r'[d]) in fp16 with fp32
+//            accumulation.  A value v = c sv (E2M1 code times the block's
+//            E4M3 scale: at most 6 significant bits, in [2^-10, 2688]) is
+//            exact in fp16; p is rounded to fp16 once, and the denominator
+//            sums those same rounded values.
 // The 8 streams of a wave are merged at the end of each sequence segment.
 //
 // Work split.  The pages of all sequences, concatenated in batch order,
@@ -38,6 +41,7 @@ namespace kvfp4 {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = 128;
@@ -55,6 +59,16 @@ __device__ inline uint32_t fp4x2_to_bf16x2(uint32_t w, int sel) {
     default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3); break;
   }
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// E2M1 codes of byte `sel` of w -> two exact fp16 values.
+__device__ inline f16x2 fp4x2_to_f16x2(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
 }
 
 // Value of an E4M3FN scale byte (OCP E4M3FN is gfx950's fp8 format; the
@@ -204,22 +218,23 @@ __device__ inline void process_pair(Stream<G>& st, const Pair& pr, float qscale)
     grew |= mt[i] > st.m[i];
   }
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(grew) != 0, 0)) rescale<G>(st, mt);
-  // P.V along the token axis: (p0 sv0, p1 sv1) . (c0[d], c1[d])
+  // P.V along the token axis: (p0, p1) . (v0[d], v1[d]), v = c sv exact
+  // in fp16
+  const _Float16 sv0 = (_Float16)scale_value(pr.vs0), sv1 = (_Float16)scale_value(pr.vs1);
+  const f16x2 s0 = {sv0, sv0}, s1 = {sv1, sv1};
   uint32_t va[8], vb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    va[j] = fp4x2_to_bf16x2(j < 4 ? pr.v0.x : pr.v0.y, j & 3);
-    vb[j] = fp4x2_to_bf16x2(j < 4 ? pr.v1.x : pr.v1.y, j & 3);
+    va[j] = __builtin_bit_cast(uint32_t, fp4x2_to_f16x2(j < 4 ? pr.v0.x : pr.v0.y, j & 3) * s0);
+    vb[j] = __builtin_bit_cast(uint32_t, fp4x2_to_f16x2(j < 4 ? pr.v1.x : pr.v1.y, j & 3) * s1);
   }
-  const float sv0 = scale_value(pr.vs0), sv1 = scale_value(pr.vs1);
-  uint32_t pp[G];
+  f16x2 pp[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const float p0 = __builtin_amdgcn_exp2f(sc[i] - st.m[i]);
-    const float p1 = __builtin_amdgcn_exp2f(sc[G + i] - st.m[i]);
-    st.l[i] += p0 + p1;
-    bf16x2 w = {(__bf16)(p0 * sv0), (__bf16)(p1 * sv1)};
-    pp[i] = __builtin_bit_cast(uint32_t, w);
+    const _Float16 p0 = (_Float16)__builtin_amdgcn_exp2f(sc[i] - st.m[i]);
+    const _Float16 p1 = (_Float16)__builtin_amdgcn_exp2f(sc[G + i] - st.m[i]);
+    st.l[i] += (float)p0 + (float)p1;
+    pp[i] = (f16x2){p0, p1};
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -227,8 +242,8 @@ __device__ inline void process_pair(Stream<G>& st, const Pair& pr, float qscale)
     const uint32_t hi = __builtin_amdgcn_perm(vb[j], va[j], 0x07060302u);  // element 2j+1
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      st.acc[i][2 * j] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[i]), as_bf16x2(lo), st.acc[i][2 * j], false);
-      st.acc[i][2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[i]), as_bf16x2(hi), st.acc[i][2 * j + 1], false);
+      st.acc[i][2 * j] = __builtin_amdgcn_fdot2(pp[i], __builtin_bit_cast(f16x2, lo), st.acc[i][2 * j], false);
+      st.acc[i][2 * j + 1] = __builtin_amdgcn_fdot2(pp[i], __builtin_bit_cast(f16x2, hi), st.acc[i][2 * j + 1], false);
     }
   }
 }

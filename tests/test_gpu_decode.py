@@ -388,3 +388,43 @@ def test_decode_late_dominant_score(name):
     packed = oracle_pool(wl, gs)
     out, lse = gpu_decode(wl, dev(packed), gs)
     check(wl, gs, packed, out, lse, what=f"{name} late dominant score")
+
+
+# (nt, T, H, D, Hq, v_dim): every balanced kernel
+FULL_SCALE = {
+    "valu_gqa": (2, 16, 2, 128, 4, 128),
+    "mfma_gqa": (2, 64, 8, 128, 32, 128),
+    "mfma_gqa_D64": (2, 16, 8, 64, 32, 64),
+    "mla": (1, 64, 1, 576, 128, 512),
+}
+
+
+@pytest.mark.parametrize("gs_last", [1.0 / 2688.0, 2.0 ** -8])
+@pytest.mark.parametrize("name", list(FULL_SCALE))
+def test_decode_full_scale_values(name, gs_last):
+    """Every value of the last tensor (V; for MLA the latent, so the keys
+    too) encodes to the format's largest finite magnitude, E2M1 6 times
+    E4M3 448 = 2688, with random signs: the partials the kernels hand to
+    the merge (o / l before the tensor scale: fp16 for MLA) span the
+    format's whole range.  The tensor scale, applied after the merge, keeps
+    the outputs O(1) (values of 1 and 10.5), where the absolute part of the
+    tolerance is meaningful: at |v| = 2688 any 16-bit rounding of the
+    probabilities would exceed it for outputs that cancel to near zero."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = FULL_SCALE[name]
+    lens = [7 * T + 3, 2 * T, 5]
+    wl = W.geometry_case(180 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    rng = np.random.default_rng(181)
+    neg = rng.random(wl.hot_pool[:, nt - 1].shape) < 0.5
+    top = np.float32(round(2688.0 * gs_last, 6))  # 1 and 10.5: exact in bf16
+    wl.hot_pool[:, nt - 1] = W.f32_to_bf16_bits(np.where(neg, -top, top).astype(np.float32))
+    gs = np.ones(nt, np.float32)
+    gs[-1] = gs_last
+    packed = oracle_pool(wl, gs)
+    g = O.Geometry(*wl.geometry)
+    full = wl.block_table[0, :int(wl.seq_lens[0]) // T]  # sequence 0's full pages
+    for slot in full:
+        _, sc = O.split_packed_page(packed[slot], g)
+        assert np.all(sc[-1] == 0x7E), "every block of the last tensor at scale 448"
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=f"{name} full-scale values, gs {gs_last}")
