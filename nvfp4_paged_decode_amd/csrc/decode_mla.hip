@@ -75,9 +75,6 @@ constexpr int kRowData = kD / 2, kRowScale = kD / 16;  // packed bytes per row
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 15.f;  // p = 2^(s - m) <= 2^15 stays finite in fp16
-#ifndef KVFP4_MLA_HB1  // 1: 16 heads a wave above 64 heads (eight waves)
-#define KVFP4_MLA_HB1 0
-#endif
 #ifndef KVFP4_MLA_KA
 #define KVFP4_MLA_KA 2
 #endif
@@ -697,16 +694,10 @@ bool mla_supported(const Geom& g, int hq, int v_dim) {
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream) {
   if (!mla_supported(a.g, a.hq, a.v_dim) || a.nwg <= 0) return hipErrorInvalidValue;
   if (((uintptr_t)a.ws_oh & 15) != 0 || ((uintptr_t)a.q & 15) != 0) return hipErrorInvalidValue;
-  // up to 64 heads: 16 a wave (one to four waves); more: 32 a wave (four),
-  // or with KVFP4_MLA_HB1 16 a wave (up to eight)
-#if KVFP4_MLA_HB1
-  if (a.hq > 112) return launch_nw<8, 1>(a, stream);
-  if (a.hq > 96) return launch_nw<7, 1>(a, stream);
-  if (a.hq > 80) return launch_nw<6, 1>(a, stream);
-  if (a.hq > 64) return launch_nw<5, 1>(a, stream);
-#else
+  // up to 64 heads: 16 a wave (one to four waves); more: 32 a wave (four;
+  // eight waves of 16 heads, whose fragments then feed one head block each,
+  // spill and took 875 against 285 us on 128 heads)
   if (a.hq > 64) return launch_nw<4, 2>(a, stream);
-#endif
   switch ((a.hq + 15) / 16) {
     case 1: return launch_nw<1, 1>(a, stream);
     case 2: return launch_nw<2, 1>(a, stream);
