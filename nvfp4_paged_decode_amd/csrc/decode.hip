@@ -220,7 +220,7 @@ constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
 // columns (8 groups of 32 threads request 64 slots per round, so a sequence
 // split over up to 64 workgroups is merged after one round of partial
 // loads), else 128 (wide rows: one group; more threads measured slower).
-constexpr int kBalMergeWide = 128, kBalMergeNarrow = 256;
+constexpr int kBalMergeWide = 64, kBalMergeNarrow = 256;
 
 // Merge for the balanced kernels: sequence b's partials sit in slots w + b
 // for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
@@ -451,13 +451,16 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   } else {
     const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_oh & 15) == 0 &&
                      ((uintptr_t)a.out & 7) == 0;
-    // the balanced kernels have v_dim <= 512: one f32x4 column block a thread
+    // the balanced kernels have v_dim <= 512: up to 128 columns, one 4-column
+    // block a thread over 256 threads; wider rows (MLA), one wave of 64
+    // threads with two blocks each (one wave per (head, sequence) keeps the
+    // whole grid resident at once)
     if (a.v_dim <= 128) {
       auto kernel = vec ? merge_balanced_kernel<true, 1, kBalMergeNarrow>
                         : merge_balanced_kernel<false, 1, kBalMergeNarrow>;
       hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeNarrow), 0, stream, a);
     } else {
-      auto kernel = vec ? merge_balanced_kernel<true, 1, kBalMergeWide>
+      auto kernel = vec ? merge_balanced_kernel<true, 2, kBalMergeWide>
                         : merge_balanced_kernel<false, 1, kBalMergeWide>;
       hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeWide), 0, stream, a);
     }
