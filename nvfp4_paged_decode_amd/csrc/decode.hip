@@ -220,7 +220,7 @@ constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
 // columns (8 groups of 32 threads request 64 slots per round, so a sequence
 // split over up to 64 workgroups is merged after one round of partial
 // loads), else 128 (wide rows: one group; more threads measured slower).
-constexpr int kBalMergeWide = 64, kBalMergeNarrow = 256;
+constexpr int kBalMergeWide = 64, kBalMergeNarrow = 256, kBalMergeNarrowFew = 128;
 
 // Merge for the balanced kernels: sequence b's partials sit in slots w + b
 // for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
@@ -236,9 +236,9 @@ constexpr int kBalMergeWide = 64, kBalMergeNarrow = 256;
 // loads, and the groups combine through LDS.  VEC (v_dim % 4 == 0, 16-byte
 // aligned partials, 8-byte aligned out): a thread owns 4 columns;
 // otherwise one column per thread, G = 1.
-template <bool VEC, int K4, int kMergeThreads>
+template <bool VEC, int K4, int kMergeThreads, int kCols>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
-  static_assert(!VEC || K4 * 4 * kMergeThreads >= 512, "v_dim up to 512");
+  static_assert(!VEC || K4 * 4 * kMergeThreads >= kCols, "v_dim up to kCols");
   const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ float s_m[kMergeThreads], s_l[kMergeThreads];
   __shared__ f32x4 s_acc[kMergeThreads];
@@ -451,18 +451,32 @@ hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& a, hipStream_
   } else {
     const bool vec = a.v_dim % 4 == 0 && ((uintptr_t)a.ws_oh & 15) == 0 &&
                      ((uintptr_t)a.out & 7) == 0;
-    // the balanced kernels have v_dim <= 512: up to 128 columns, one 4-column
-    // block a thread over 256 threads; wider rows (MLA), one wave of 64
-    // threads with two blocks each (one wave per (head, sequence) keeps the
-    // whole grid resident at once)
+    auto launch = [&](auto threads_c, auto k4_c, auto cols_c) {
+      constexpr int kT = decltype(threads_c)::value, kK4 = decltype(k4_c)::value,
+                    kC = decltype(cols_c)::value;
+      auto kernel = vec ? merge_balanced_kernel<true, kK4, kT, kC>
+                        : merge_balanced_kernel<false, 1, kT, kC>;
+      hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kT), 0, stream, a);
+    };
+    // the balanced kernels have v_dim <= 512.  Up to 128 columns: one
+    // 4-column block a thread, and G = threads / (v_dim / 4) groups of
+    // slots, kMergeBatch slots a group a round; with equal lengths a
+    // sequence has about nwg / batch + 1 holders, so 128 threads (32 slots a
+    // round for v_dim 128) when those fit, else 256 (64 a round; 128
+    // threads measured 4.3 against 5.1 us on 32 sequences of 8 holders,
+    // and 5.2 against 4.5 us on 8 sequences of about 32).  Wider
+    // rows (MLA): one wave of 64 threads with two blocks each, one wave per
+    // (head, sequence), which keeps the whole grid resident at once.
     if (a.v_dim <= 128) {
-      auto kernel = vec ? merge_balanced_kernel<true, 1, kBalMergeNarrow>
-                        : merge_balanced_kernel<false, 1, kBalMergeNarrow>;
-      hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeNarrow), 0, stream, a);
+      if (a.nwg / a.batch + 2 <= (kBalMergeNarrowFew / 32) * kMergeBatch)
+        launch(std::integral_constant<int, kBalMergeNarrowFew>{}, std::integral_constant<int, 1>{},
+               std::integral_constant<int, 128>{});
+      else
+        launch(std::integral_constant<int, kBalMergeNarrow>{}, std::integral_constant<int, 1>{},
+               std::integral_constant<int, 128>{});
     } else {
-      auto kernel = vec ? merge_balanced_kernel<true, 2, kBalMergeWide>
-                        : merge_balanced_kernel<false, 1, kBalMergeWide>;
-      hipLaunchKernelGGL(kernel, dim3(a.hq, a.batch), dim3(kBalMergeWide), 0, stream, a);
+      launch(std::integral_constant<int, kBalMergeWide>{}, std::integral_constant<int, 2>{},
+             std::integral_constant<int, 512>{});
     }
   }
   return hipGetLastError();
