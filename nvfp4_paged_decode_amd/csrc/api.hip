@@ -487,6 +487,8 @@ int32_t decode_call(const kvfp4_geometry* g, const void* packed_pool, int32_t pa
   a.splits = plan.splits;
   a.pages_per_split = plan.pages_per_split;
   a.nwg = plan.nwg;
+  // pads need P nwg < 2^31 (P <= batch * max_pages_per_seq)
+  a.seg_pad = (long long)batch * max_pages_per_seq * plan.nwg < (1LL << 31) ? plan.seg_pad : 0;
   size_t partials = plan.kernel == 0 ? (size_t)batch * num_q_heads * plan.splits
                                      : (size_t)(plan.nwg + batch) * num_q_heads;
   if (plan.kernel == 0) {  // generic kernel: fp32 partial outputs

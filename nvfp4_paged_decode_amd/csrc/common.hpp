@@ -188,6 +188,7 @@ struct DecodeArgs {
   int splits;
   int pages_per_split;
   int nwg;
+  int seg_pad;           // balanced kernels: pages of a segment pad (0: none)
   float* ws_o;           // generic kernel: partial outputs, v_dim floats each
   // balanced kernels: partial outputs divided by their sum, v_dim fp16 each
   // (a weighted average of value rows: |o / l| <= 2688, which fp16 holds)
@@ -195,7 +196,8 @@ struct DecodeArgs {
   float* ws_ml;          // partial (max, sum), scores in log2 units
   // Balanced kernels: the first and last workgroup whose range holds pages
   // of sequence b ([batch][2], written for every sequence with pages), then
-  // the batch's page count; the merge reads these instead of rescanning.
+  // the length of the split (pages and pads); the merge reads these instead
+  // of rescanning.
   int32_t* ws_idx;
 };
 
@@ -205,6 +207,7 @@ struct DecodePlan {
   int splits;            // generic kernel
   int pages_per_split;   // generic kernel
   int nwg;               // balanced kernels
+  int seg_pad;           // balanced kernels: pages of a segment pad
   size_t workspace_bytes;
 };
 

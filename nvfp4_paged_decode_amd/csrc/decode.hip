@@ -216,17 +216,19 @@ __device__ inline uint32_t bf16_rne_bits(float x) {
 }
 
 constexpr int kMergeBatch = 8;  // slots whose partials a group requests at once
-// Threads of the balanced merge: 256 when a partial row is at most 128
-// columns (8 groups of 32 threads request 64 slots per round, so a sequence
-// split over up to 64 workgroups is merged after one round of partial
-// loads), else 128 (wide rows: one group; more threads measured slower).
+// Threads of the balanced merge.  Rows of at most 128 columns: 256 (8
+// groups of 32 threads request 64 slots per round, so a sequence split over
+// up to 64 workgroups is merged after one round of partial loads), or 128
+// when the batch's sequences have few holders (32 slots per round; fewer
+// threads, less to combine).  Wider rows (MLA): one wave of 64.  The
+// launcher below picks one.
 constexpr int kBalMergeWide = 64, kBalMergeNarrow = 256, kBalMergeNarrowFew = 128;
 
 // Merge for the balanced kernels: sequence b's partials sit in slots w + b
 // for the workgroups w whose page ranges overlap b's pages, w_lo..w_hi
-// (recorded by the decode kernel with the batch's page count).  One
+// (recorded by the decode kernel with the length of the split).  One
 // workgroup per (head, sequence), two rounds of global reads: the
-// sequence's length, slot range and the batch's page count together, then
+// sequence's length, slot range and the split's length together, then
 // every partial at once.  Loads are unconditional, from slot and column
 // indices clamped into range, and whether a slot holds a partial is decided
 // after they are all issued: loads under a condition become branches that
@@ -254,8 +256,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
   w_lo = w_lo < 0 ? 0 : (w_lo > nwg - 1 ? nwg - 1 : w_lo);
   w_hi = w_hi < w_lo ? w_lo : (w_hi > nwg - 1 ? nwg - 1 : w_hi);
   if (L == 0 || ptot <= 0) w_hi = w_lo - 1;
-  // slot v + b holds a partial when v's page range is not empty, which
-  // every range is when the batch has at least one page per workgroup
+  // slot v + b (w_lo <= v <= w_hi) holds a partial when v's range is not
+  // empty, which every range is when the split has at least one page (real
+  // or pad) per workgroup; ranges between w_lo and w_hi lie within b's pages
   const bool all_hold = ptot >= nwg;
   auto holds = [&](int v) {
     return all_hold || (long long)v * ptot / nwg < (long long)(v + 1) * ptot / nwg;
@@ -398,10 +401,14 @@ DecodePlan plan_decode(const Geom& g, int batch, int hq, int v_dim, int max_seq_
     long long pages_ub = (long long)batch * pages_max;
     long long nwg = target < pages_ub ? target : pages_ub;
     p.nwg = (int)(nwg > 0 ? nwg : 1);
+    // a segment pad is about 128 tokens of pages (a second segment's start
+    // and stream merge cost about as long as streaming that many); none for
+    // batches over 64 sequences or pages of more than 256 tokens
+    p.seg_pad = batch <= 64 ? (128 + g.T / 2) / g.T : 0;
     p.splits = 0;
     p.pages_per_split = 0;
     // partial outputs (fp16), their (max, sum) (fp32), then the merge's
-    // index ([batch][2] + the page count, padded)
+    // index ([batch][2] + the length of the split, padded)
     p.workspace_bytes =
         (size_t)(p.nwg + batch) * hq * ((size_t)v_dim * sizeof(uint16_t) + 2 * sizeof(float)) +
         (((size_t)2 * batch + 1) * sizeof(int32_t) + 15) / 16 * 16;

@@ -368,8 +368,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_gqa_mfma_kernel(DecodeArgs
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
     const int L = seq_len(a, rng, b);
     const int npages = (L + g.T - 1) / g.T;
-    const long long first = seq_start;
-    seq_start += npages;
+    const long long first = seq_first_page(rng, b, seq_start);
+    seq_start = first + npages;
     const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;

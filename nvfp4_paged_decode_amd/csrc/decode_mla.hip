@@ -74,7 +74,6 @@ constexpr int kPitch = 592;        // fp16 per staged row (296 dwords = 8 mod 32
 constexpr int kRowData = kD / 2, kRowScale = kD / 16;  // packed bytes per row
 constexpr float kNoMax = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kHeadroom = 15.f;  // p = 2^(s - m) <= 2^15 stays finite in fp16
 #ifndef KVFP4_MLA_KA
 #define KVFP4_MLA_KA 2
 #endif
@@ -241,8 +240,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mla_kernel(DecodeArgs a) {
   for (int b = rng.b_first; b < a.batch && seq_start < rng.p_end; ++b) {
     const int L = seq_len(a, rng, b);
     const int npages = (L + g.T - 1) / g.T;
-    const long long first = seq_start;
-    seq_start += npages;
+    const long long first = seq_first_page(rng, b, seq_start);
+    seq_start = first + npages;
     const long long p_lo = rng.p_begin > first ? rng.p_begin - first : 0;
     const long long p_hi = rng.p_end - first < npages ? rng.p_end - first : npages;
     if (p_lo >= p_hi) continue;

@@ -1,13 +1,14 @@
 // Balanced split-K over the pages of a whole batch (device side).
 //
 // The pages of all sequences, concatenated in batch order, form one list of
-// P pages (sequence b contributes ceil(L_b / T) of them).  Workgroup w of
-// nwg owns pages [floor(w P / nwg), floor((w+1) P / nwg)).  Every range is
+// P pages (sequence b contributes ceil(L_b / T) of them), with the pads
+// described below between some sequences.  Workgroup w of nwg owns
+// [floor(w P / nwg), floor((w+1) P / nwg)) of that list.  Every range is
 // contiguous and ranges are monotone in w, so the (workgroup, sequence)
 // pairs that overlap are indexed without collision by w + b: this is the
-// partial slot the workgroup writes for that sequence.  Kernels and the
-// merge compute the same ranges from seq_lens with the same integer
-// arithmetic.
+// partial slot the workgroup writes for that sequence.  Every workgroup
+// computes the same ranges from seq_lens with the same integer arithmetic;
+// the merge reads which workgroups held each sequence from the workspace.
 #pragma once
 
 #include "common.hpp"
@@ -57,23 +58,43 @@ __device__ inline long long uniform(long long v) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// Segment pads.  A workgroup whose range holds the end of one sequence and
+// the start of the next walks two segments: it starts twice (queries,
+// page-table entries, the first tiles' wait with nothing else of its own in
+// flight) and merges its streams twice.  Each sequence boundary that the
+// plain split puts inside a range is therefore given a pad of a.seg_pad
+// virtual pages (about 128 tokens' worth, set by the plan) in front of the
+// next sequence's pages: the split is taken over real and pad pages
+// together, so the workgroups around such a boundary take fewer real pages.
+// Boundaries that fall on a range start cost no second segment and get no
+// pad, so a batch whose sequences split evenly keeps the plain split.  The
+// plan sets pads only for batches of at most 64 sequences, whose lengths the
+// range search keeps in registers.
+
 struct BalancedRange {
-  long long ptot;         // pages in the batch
-  long long p_begin;      // this workgroup's pages [p_begin, p_end)
+  long long ptot;         // length of the split: the batch's pages plus pads
+  long long p_begin;      // this workgroup's share [p_begin, p_end) of it
   long long p_end;
   int b_first;            // first sequence with pages in the range (batch if none)
-  long long start_first;  // index of its first page in the concatenation
+  long long start_first;  // its start in the split (its pad, if it has one)
   int len0;               // lane l: clamped length of sequence l (l < 64)
+  int pad;                // pages of a pad
+  unsigned long long padmask;  // bit b: sequence b's pages follow a pad
 };
 
-// Wave-level inclusive prefix sum of an int over 64 lanes.
+// Wave-level inclusive prefix sum of an int over 64 lanes, on DPP lane
+// moves (no LDS round trips): a Hillis-Steele scan within each row of 16
+// lanes (row_shr 1, 2, 4, 8), then the row totals, row_bcast:15 adding lane
+// 15 of each row to the next row (rows 1 and 3) and row_bcast:31 adding
+// lane 31 to rows 2 and 3.  A lane whose source lies outside its row, or
+// whose row the mask leaves out, adds 0.
 __device__ inline int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -86,13 +107,34 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
   r.len0 = lane < a.batch ? clamped_len(a, lane) : 0;
   const int np0 = (r.len0 + a.g.T - 1) / a.g.T;
   const int incl0 = wave_incl_scan(np0);
-  long long tot = __shfl(incl0, 63);
+  long long tot = __builtin_amdgcn_readlane(incl0, 63);
   for (int base = 64; base < a.batch; base += 64) {
     int b = base + lane;
     int np = b < a.batch ? pages_of(a, b) : 0;
-    tot += __shfl(wave_incl_scan(np), 63);
+    tot += __builtin_amdgcn_readlane(wave_incl_scan(np), 63);
   }
   tot = uniform(tot);
+  // pads: sequence `lane` starts at page s of the plain split, and s starts
+  // a range (s = floor(w P / nwg) for some w) exactly when a multiple of P
+  // lies in [s nwg, s nwg + nwg): when (s nwg) mod P is 0 or above P - nwg.
+  // The plan sets pads only where P nwg < 2^31, so 32-bit arithmetic holds;
+  // the quotient comes from an fp32 estimate (within one of the truth, as
+  // s nwg / P < nwg), corrected once each way.
+  r.pad = a.seg_pad;
+  r.padmask = 0;
+  int vincl0 = incl0;  // end of the lane's sequence in the split, pads included
+  if (r.pad > 0 && tot > nwg) {
+    const unsigned P = (unsigned)tot, sn = (unsigned)(incl0 - np0) * (unsigned)nwg;
+    const unsigned q = (unsigned)((float)sn * __builtin_amdgcn_rcpf((float)P));
+    int rem = (int)(sn - q * P);
+    rem += rem < 0 ? (int)P : 0;
+    rem -= rem >= (int)P ? (int)P : 0;
+    const bool padded = np0 > 0 && rem != 0 && rem <= (int)(P - (unsigned)nwg);
+    r.padmask = __builtin_amdgcn_ballot_w64(padded);
+    const unsigned long long upto = lane == 63 ? ~0ull : (2ull << lane) - 1ull;
+    vincl0 = incl0 + r.pad * __builtin_popcountll(r.padmask & upto);
+    tot = uniform(tot + (long long)r.pad * __builtin_popcountll(r.padmask));
+  }
   r.ptot = tot;
   r.p_begin = range_begin(tot, w, nwg);
   r.p_end = range_begin(tot, w + 1, nwg);
@@ -103,17 +145,24 @@ __device__ inline void balanced_range(const DecodeArgs& a, int w, int nwg, Balan
   for (int base = 0; base < a.batch; base += 64) {
     int b = base + lane;
     int np = base == 0 ? np0 : (b < a.batch ? pages_of(a, b) : 0);
-    int incl = base == 0 ? incl0 : wave_incl_scan(np);
+    int incl = base == 0 ? vincl0 : wave_incl_scan(np);
     bool hit = np > 0 && run + incl > r.p_begin;
     unsigned long long m = __builtin_amdgcn_ballot_w64(hit);
     if (m) {
       int l0 = __builtin_ctzll(m);
+      const int padb = ((r.padmask >> l0) & 1) ? r.pad : 0;
       r.b_first = uniform(base + l0);
-      r.start_first = uniform(run + __shfl(incl - np, l0));
+      r.start_first = uniform(run + __builtin_amdgcn_readlane(incl - np, l0) - padb);
       return;
     }
-    run = uniform(run + __shfl(incl, 63));
+    run = uniform(run + __builtin_amdgcn_readlane(incl, 63));
   }
+}
+
+// Where sequence b's pages begin in the split, given where its share of the
+// split begins (`start`: its pad, if it has one).
+__device__ inline long long seq_first_page(const BalancedRange& r, int b, long long start) {
+  return start + ((b < 64 && ((r.padmask >> b) & 1ull)) ? r.pad : 0);
 }
 
 // Clamped length of sequence b (wave-uniform), from the lengths the range
@@ -132,7 +181,7 @@ __device__ inline void note_segment(const DecodeArgs& a, int w, int b, long long
   }
 }
 
-// Workgroup 0 records the batch's page count (whether or not its range is empty).
+// Workgroup 0 records the length of the split (whether or not its range is empty).
 __device__ inline void note_total(const DecodeArgs& a, int w, long long ptot) {
   if (w == 0 && threadIdx.x == 0) a.ws_idx[2 * a.batch] = (int32_t)ptot;
 }

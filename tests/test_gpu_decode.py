@@ -196,6 +196,49 @@ def test_decode_more_sequences_than_workgroups(name):
     assert np.all(out[empty] == 0) and np.all(lse[empty] == -np.inf)
 
 
+def inner_boundaries(lens, T, nwg):
+    """Sequence starts that fall strictly inside a workgroup's range of the
+    plain balanced split (pages [floor(w P / nwg), floor((w+1) P / nwg)))."""
+    npg = [(int(L) + T - 1) // T for L in lens]
+    P = sum(npg)
+    starts = {(w * P) // nwg for w in range(nwg + 1)}
+    out, s = [], 0
+    for n in npg:
+        if n > 0 and s > 0 and s not in starts:
+            out.append(s)
+        s += n
+    return out
+
+
+# (nt, T, H, D, Hq, v_dim), one per balanced kernel
+PADDED = {
+    "valu_gqa": (2, 16, 2, 128, 4, 128),
+    "mfma_gqa": (2, 16, 8, 128, 32, 128),
+    "mla": (1, 64, 1, 576, 128, 512),
+}
+
+
+@pytest.mark.parametrize("name", list(PADDED))
+def test_decode_sequence_boundaries_inside_ranges(name):
+    """Ragged sequences with more pages than workgroups: sequence starts
+    fall inside workgroup ranges, where the split inserts pad pages (the
+    workgroups around such a start take fewer real pages), with empty and
+    one-page sequences between the others."""
+    require_gpu()
+    nt, T, H, D, Hq, v_dim = PADDED[name]
+    unit = 16 if T == 16 else 64
+    lens = np.array([700, 1900, 33, 0, 1250, 2600, 411, 1, 977], dtype=np.int64) * unit // 16
+    hint = int(lens.max())
+    nwg = min(torch.cuda.get_device_properties(0).multi_processor_count,
+              len(lens) * ((hint + T - 1) // T))
+    assert inner_boundaries(lens, T, nwg), "no sequence start inside a range"
+    wl = W.geometry_case(110 + len(name), nt=nt, T=T, H=H, D=D, Hq=Hq, v_dim=v_dim, lens=lens)
+    gs = wl.gs_calibrated
+    packed = oracle_pool(wl, gs)
+    out, lse = gpu_decode(wl, dev(packed), gs)
+    check(wl, gs, packed, out, lse, what=name)
+
+
 NO_LSE = {
     "valu_tiny": lambda: W.tiny(seed=21),
     "mfma_gqa": lambda: W.llama3_8b(seed=22, batch=3, context=300),
