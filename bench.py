@@ -105,6 +105,7 @@ def append_bytes(geometry, tokens: int, elem_bytes: int) -> int:
 # Each leg's traffic mix, for reading its bandwidth against a plain stream of
 # the same mix: decode reads (the merge's few writes aside); the encoder reads
 # 32 bytes of bf16 for every 9 it writes, the decoder the reverse.
+# the streaming legs' traffic mixes (the page-list sort, a few KiB, has none)
 LEG_MIX = {"decode": "read", "quantize": "read4_write1", "dequantize": "read1_write4"}
 YARDSTICK_KINDS = {"read": (0, 1.0), "write": (1, 1.0), "read4_write1": (2, 1.25),
                    "read1_write4": (3, 1.25)}
@@ -516,22 +517,34 @@ class Legs:
         self.hot = [hot0] + [hot0.clone() for _ in range(SETS - 1)]
         self.src = torch.from_numpy(np.ascontiguousarray(src, np.int32)).to(dev)
         self.dst = torch.from_numpy(np.ascontiguousarray(dst, np.int32)).to(dev)
+        # The step's first leg sorts the page list by hot slot (the library's
+        # kvfp4_sort_page_list); both codec legs take the sorted list, so
+        # the workgroups running at once touch neighbouring slots.
+        self.src_sorted = torch.empty_like(self.src)
+        self.dst_sorted = torch.empty_like(self.dst)
+        K.kvfp4_sort_page_list(self.src, self.src_sorted, self.dst, self.dst_sorted,
+                               num_pages=self.pages)
         pb = K.kvfp4_packed_page_bytes(self.geometry)
         self.packed = [torch.zeros((self.num_slots, pb), dtype=torch.uint8, device=dev)
                        for _ in range(SETS)]
         self.back = [torch.empty_like(hot0) for _ in range(SETS)]
         self.K = K
         G, gs = self.geometry, self.gs
+        sort = lambda: K.kvfp4_sort_page_list(self.src, self.src_sorted, self.dst,
+                                              self.dst_sorted, num_pages=self.pages)
         self.calls = {
+            "sort": [sort] * SETS,
             "quantize": [lambda r=r: K.kvfp4_quantize_pages(G, self.hot[r], self.packed[r],
-                                                            self.pages, gs, self.src, self.dst)
+                                                            self.pages, gs, self.src_sorted,
+                                                            self.dst_sorted)
                          for r in range(SETS)],
             "dequantize": [lambda r=r: K.kvfp4_dequantize_pages(G, self.packed[r], self.back[r],
-                                                                self.pages, gs, self.dst,
-                                                                self.src)
+                                                                self.pages, gs, self.dst_sorted,
+                                                                self.src_sorted)
                            for r in range(SETS)],
         }
-        self.leg_bytes = {"quantize": codec_bytes(G, self.pages),
+        # the sort reads both lists and writes their sorted copies
+        self.leg_bytes = {"sort": 16 * self.pages, "quantize": codec_bytes(G, self.pages),
                           "dequantize": codec_bytes(G, self.pages)}
         if self.wl is not None:
             wl = self.wl
@@ -553,18 +566,20 @@ class Legs:
                 for r in range(SETS)]
             self.db = decode_bytes(wl)
             self.leg_bytes["decode"] = self.db["bytes"]
-        self.order = [k for k in ("quantize", "decode", "dequantize") if k in self.calls]
+        self.order = [k for k in ("sort", "quantize", "decode", "dequantize") if k in self.calls]
 
     def describe(self) -> str:
         if self.wl is None:
             return (f"cold_pages: {self.pages} pages x {self.geometry} (tensors, tokens, heads, "
-                    f"dims); step = encode + decode of every page")
+                    f"dims); step = sort the page list by hot slot + encode + decode of every "
+                    f"page")
         wl = self.wl
         nt, T, H, D = self.geometry
         return (f"{self.name}: batch {wl.batch}, {wl.num_q_heads} q / {H} KV heads, head_dim "
                 f"{D}, v_dim {wl.v_dim}, context {int(wl.seq_lens.min())}-"
                 f"{int(wl.seq_lens.max())} (sum {int(wl.seq_lens.sum())}), page {T}; step = "
-                f"encode {self.pages} pages + decode attention + decode {self.pages} pages")
+                f"sort the page list by hot slot + encode {self.pages} pages + decode "
+                f"attention + decode {self.pages} pages")
 
     def free(self):
         for k in list(vars(self)):
@@ -580,7 +595,7 @@ def leg_report(legs, name, ms, iso=None, mixes=None, copy=None) -> dict:
     gbs = b / (ms * 1e-3) / 1e9
     r = {"avg_us": round(ms * 1e3, 2), "bytes": b, "GB/s": round(gbs, 1),
          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    if mixes and LEG_MIX[name] in mixes:
+    if mixes and LEG_MIX.get(name) in mixes:
         r["frac_mix_yardstick"] = round(gbs / mixes[LEG_MIX[name]]["GB/s"], 4)
     if copy is not None:
         r["frac_copy_yardstick"] = round(gbs / copy["GB/s"], 4)
@@ -807,10 +822,40 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def time_slot_order(K, torch, legs, stream, evict, steps, warmup) -> dict:
+    """The step's codec legs (same pages, same pools, steady state) with the
+    page list sorted by hot slot, as the step runs them, and with the list
+    as given -- the pool's slots in a random order, as a cache's pages would
+    lie.  The kernels take pages in list order; the results are the same
+    either way, the bandwidth is not."""
+    G, gs, n = legs.geometry, legs.gs, legs.pages
+    lists = {"as_given": (legs.src, legs.dst), "sorted": (legs.src_sorted, legs.dst_sorted)}
+    legs_fn = {
+        "quantize": lambda r, s, d: K.kvfp4_quantize_pages(G, legs.hot[r], legs.packed[r], n, gs,
+                                                           s, d),
+        "dequantize": lambda r, s, d: K.kvfp4_dequantize_pages(G, legs.packed[r], legs.back[r], n,
+                                                               gs, d, s),
+    }
+    out = {}
+    for leg, fn in legs_fn.items():
+        res = {}
+        for tag, (s, d) in lists.items():
+            calls = [lambda r=r, s=s, d=d: fn(r, s, d) for r in range(SETS)]
+            evict()
+            ms = time_block(torch, stream, calls, steps, warmup)
+            gbs = legs.leg_bytes[leg] / (ms * 1e6)
+            res[tag] = {"avg_us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        out[leg] = res
+    return out
+
+
 def run_extras(K, torch, legs, stream, evict, args) -> dict:
     """The "next" paths, timed beside the step (never part of it)."""
     wl, G, gs = legs.wl, legs.geometry, legs.gs
     return {
+        "codec_slot_order": time_slot_order(K, torch, legs, stream, evict, args.steps,
+                                            args.warmup),
         "token_rows": time_append(K, torch, wl, G, gs, legs.hot[0], legs.packed[0], stream,
                                   evict, args.steps, args.warmup),
         "host_offload": time_offload(K, torch, wl, G, gs, legs.hot[0], stream,

@@ -29,7 +29,8 @@ KVFP4_ROWS_FP8_E4M3 = 1
 #: Every function the header declares (checked by the CPU tests).
 EXPORTS = (
     "kvfp4_hot_page_bytes", "kvfp4_packed_page_bytes", "kvfp4_quantize_pages",
-    "kvfp4_dequantize_pages", "kvfp4_append_quantize", "kvfp4_gather_dequantize",
+    "kvfp4_dequantize_pages", "kvfp4_sort_page_list", "kvfp4_append_quantize",
+    "kvfp4_gather_dequantize",
     "kvfp4_packed_page_bytes_rope", "kvfp4_quantize_pages_rope", "kvfp4_dequantize_pages_rope",
     "kvfp4_decode_workspace_bytes",
     "kvfp4_paged_decode_attention", "kvfp4_paged_decode_attention_noalloc",
@@ -100,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     lib.kvfp4_quantize_pages.restype = I32
     lib.kvfp4_dequantize_pages.argtypes = codec
     lib.kvfp4_dequantize_pages.restype = I32
+    lib.kvfp4_sort_page_list.argtypes = [P, P, I32, P, P, P]
+    lib.kvfp4_sort_page_list.restype = I32
     lib.kvfp4_append_quantize.argtypes = [G, P, I32, I32, P, P, P, I32, P, P]
     lib.kvfp4_append_quantize.restype = I32
     lib.kvfp4_gather_dequantize.argtypes = [G, P, I32, P, P, I32, P, I32, P, P]
@@ -244,6 +247,24 @@ def kvfp4_dequantize_pages(geometry, packed_pool, hot_pool, num_pages: int, glob
         _pages(packed_pool, kvfp4_packed_page_bytes(g)),
         _ptr(src_slots), _ptr(hot_pool), _pages(hot_pool, kvfp4_hot_page_bytes(g)),
         _ptr(dst_slots), int(num_pages), _scales(global_scale, g.num_kv_tensors), _stream(stream)))
+
+
+def kvfp4_sort_page_list(key, key_out, other=None, other_out=None, num_pages=None,
+                         stream=None) -> None:
+    """Sort the pairs (key[i], other[i]) by key into (key_out, other_out):
+    ascending as unsigned 32-bit values, equal keys in input order.  Pass
+    the codec calls' hot-pool slots as ``key``; the codec then takes the
+    pages in slot order."""
+    lib = load_library()
+    n = int(key.numel() if num_pages is None else num_pages)
+    _int32(key, "key", n)
+    _int32(key_out, "key_out", n)
+    if (other is None) != (other_out is None):
+        raise ValueError("other and other_out must both be given or both be None")
+    _int32(other, "other", n)
+    _int32(other_out, "other_out", n)
+    _check(lib.kvfp4_sort_page_list(_ptr(key), _ptr(other), n, _ptr(key_out), _ptr(other_out),
+                                    _stream(stream)))
 
 
 def kvfp4_packed_page_bytes_rope(geometry, rope) -> int:

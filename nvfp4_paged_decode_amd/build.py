@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libkvfp4.so")
 YARDSTICK_LIB = os.path.join(PKG, "libkvfp4_yardstick.so")
 
 SOURCES = ["api.hip", "codec.hip", "decode.hip", "decode_gqa.hip", "decode_gqa_mfma.hip",
-           "decode_mla.hip", "rope.hip"]
+           "decode_mla.hip", "order.hip", "rope.hip"]
 
 # gfx950 only.  Packed-fp32 VALU ops are switched off (the host pass warns
 # that it does not know the feature; harmless).  No fast-math: the codec

@@ -228,6 +228,29 @@ int32_t kvfp4_dequantize_pages(const kvfp4_geometry* g, const void* packed_pool,
   return ok();
 }
 
+int32_t kvfp4_sort_page_list(const int32_t* key, const int32_t* other, int32_t num_pages,
+                             int32_t* key_out, int32_t* other_out, void* stream) {
+  if (num_pages < 0) return fail(KVFP4_ERR_INVALID_ARG, "num_pages = %d < 0", num_pages);
+  if (num_pages == 0) return ok();
+  if (!key || !key_out)
+    return fail(KVFP4_ERR_INVALID_ARG, "NULL key list (key=%p key_out=%p)", (const void*)key,
+                (void*)key_out);
+  if ((other == nullptr) != (other_out == nullptr))
+    return fail(KVFP4_ERR_INVALID_ARG, "other and other_out must both be given or both be NULL");
+  const uintptr_t n4 = (uintptr_t)num_pages * sizeof(int32_t);
+  auto overlap = [n4](const void* a, const void* b) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return a && b && x < y + n4 && y < x + n4;
+  };
+  if (overlap(key_out, key) || overlap(key_out, other) || overlap(other_out, key) ||
+      overlap(other_out, other) || overlap(key_out, other_out))
+    return fail(KVFP4_ERR_INVALID_ARG, "sort outputs overlap each other or the inputs");
+  hipError_t e = kvfp4::launch_sort_pages(key, other, num_pages, key_out, other_out,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KVFP4_ERR_HIP, "sort launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t kvfp4_packed_page_bytes_rope(const kvfp4_geometry* g, const kvfp4_rope_layout* rope) {
   if (!rope_valid(g, rope)) return 0;
   return (size_t)(to_geom(g).packed_bytes() + rope_ext_bytes(g, rope));

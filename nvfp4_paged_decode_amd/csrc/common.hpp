@@ -127,6 +127,22 @@ __device__ inline uint32_t bf16_rne_from_f64(double v, int tie_bias = 0) {
   return sign | bits;
 }
 
+// Wave-level inclusive prefix sum of an int over 64 lanes, on DPP lane
+// moves (no LDS round trips): a Hillis-Steele scan within each row of 16
+// lanes (row_shr 1, 2, 4, 8), then the row totals, row_bcast:15 adding lane
+// 15 of each row to the next row (rows 1 and 3) and row_bcast:31 adding
+// lane 31 to rows 2 and 3.  A lane whose source lies outside its row, or
+// whose row the mask leaves out, adds 0.
+__device__ inline int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Internal launchers (host side).  All validate nothing: the C ABI did.
 // ---------------------------------------------------------------------------
@@ -153,6 +169,9 @@ hipError_t launch_rope_decode(const Geom& g, int rope_dims, int mode, long long 
                               const void* packed, int packed_pages, const int32_t* src, void* hot,
                               int hot_pages, const int32_t* dst, int num_pages, const float* gs,
                               hipStream_t stream);
+
+hipError_t launch_sort_pages(const int32_t* key, const int32_t* other, int num_pages,
+                             int32_t* key_out, int32_t* other_out, hipStream_t stream);
 
 // Raises a kernel's dynamic-LDS limit once per device (the setting is
 // idempotent; doing it once keeps it out of launches a caller may be

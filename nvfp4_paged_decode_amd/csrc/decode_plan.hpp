@@ -82,22 +82,6 @@ struct BalancedRange {
   unsigned long long padmask;  // bit b: sequence b's pages follow a pad
 };
 
-// Wave-level inclusive prefix sum of an int over 64 lanes, on DPP lane
-// moves (no LDS round trips): a Hillis-Steele scan within each row of 16
-// lanes (row_shr 1, 2, 4, 8), then the row totals, row_bcast:15 adding lane
-// 15 of each row to the next row (rows 1 and 3) and row_bcast:31 adding
-// lane 31 to rows 2 and 3.  A lane whose source lies outside its row, or
-// whose row the mask leaves out, adds 0.
-__device__ inline int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
 // Computed by every wave on its own (no LDS, no barrier).  The first 64
 // lengths are read once and kept (len0; most batches have at most 64
 // sequences), so that the scan, the range search and the segment loop wait

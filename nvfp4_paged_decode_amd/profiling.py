@@ -43,6 +43,7 @@ CSRC = os.path.join(PKG, "csrc")
 #: Kernel sources each benchmark leg's kernels are compiled from (the
 #: launchers that set their grids included).
 LEG_SOURCES = {
+    "sort": ("order.hip", "common.hpp"),
     "quantize": ("codec.hip", "common.hpp"),
     "dequantize": ("codec.hip", "common.hpp"),
     "append": ("codec.hip", "common.hpp"),

@@ -53,6 +53,31 @@ def _q(lib, g, num_pages=4, gs=(1.0, 1.0), hot=FAKE, packed=FAKE, hot_pages=8, p
                                     None, packed, packed_pages, None, num_pages, arr, None)
 
 
+@pytest.mark.parametrize("case,msg", [
+    (dict(n=-1), "num_pages"),
+    (dict(key=None), "NULL key"),
+    (dict(key_out=None), "NULL key"),
+    (dict(other_out=None), "both"),                     # other given, other_out missing
+    (dict(other=None), "both"),
+    (dict(key_out=FAKE + 8), "overlap"),               # into key's 16 bytes
+    (dict(other_out=0x3000 - 4), "overlap"),           # ends inside key_out
+    (dict(other_out=0x2000), "overlap"),               # same as other
+])
+def test_sort_rejects_invalid_arguments(lib, case, msg):
+    """kvfp4_sort_page_list validates before launching anything (pointers
+    are never dereferenced: every call here fails validation)."""
+    a = dict(key=FAKE, other=0x2000, n=4, key_out=0x3000, other_out=0x4000)
+    a.update(case)
+    st = lib.kvfp4_sort_page_list(a["key"], a["other"], a["n"], a["key_out"], a["other_out"],
+                                  None)
+    assert st == K.KVFP4_ERR_INVALID_ARG
+    assert msg in lib.kvfp4_last_error_message().decode()
+
+
+def test_sort_zero_pages_is_a_noop(lib):
+    assert lib.kvfp4_sort_page_list(None, None, 0, None, None, None) == K.KVFP4_OK
+
+
 @pytest.mark.parametrize("case", [
     dict(g=None),
     dict(g=K.Geometry(2, 64, 8, 100)),

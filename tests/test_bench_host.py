@@ -44,7 +44,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_every_leg_has_a_mix_yardstick():
-    """Each timed leg is read against a stream of its own traffic mix, and
+    """Each streaming leg is read against a stream of its own traffic mix, and
     the mixes' byte factors match the directions they move (1 GiB on the
     reference side, a quarter of it on the other)."""
     assert set(bench.LEG_MIX) == {"decode", "quantize", "dequantize"}
