@@ -80,8 +80,10 @@ def short_name(name: str) -> str:
 
 def leg_of(kernel: str) -> str | None:
     """Benchmark leg a kernel belongs to."""
-    if kernel.startswith("quantize_kernel"):
+    if kernel.startswith(("quantize_kernel", "quantize_rounds_kernel")):
         return "quantize"
+    if kernel.startswith("sort_pages_kernel"):
+        return "sort"
     if kernel.startswith("dequantize_kernel"):
         return "dequantize"
     if kernel.startswith("append_kernel"):

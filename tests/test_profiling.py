@@ -61,6 +61,19 @@ def test_leg_digests_cover_their_sources():
     assert P.source_digest("quantize") == P.source_digest("dequantize")
 
 
+def test_every_step_kernel_has_its_leg():
+    """Each kernel the benchmark's step launches maps to its leg (traffic
+    lines and rooflines are read per leg)."""
+    ns = "void kvfp4::(anonymous namespace)::"
+    for name, leg in [("quantize_kernel(kvfp4::Geom)", "quantize"),
+                      ("quantize_rounds_kernel(kvfp4::Geom)", "quantize"),
+                      ("dequantize_kernel(kvfp4::Geom)", "dequantize"),
+                      ("sort_pages_kernel(int const*)", "sort"),
+                      ("decode_gqa_mfma_kernel<128, 2, 1>(kvfp4::DecodeArgs)", "decode"),
+                      ("merge_balanced_kernel<true, 1, 128, 128>(kvfp4::DecodeArgs)", "decode")]:
+        assert P.leg_of(P.short_name(ns + name)) == leg, name
+
+
 def test_names_outside_the_library_namespace_are_kept():
     """The benchmark's stream yardsticks live in an anonymous namespace of
     their own: they keep their names and belong to no leg."""
