@@ -33,24 +33,6 @@ constexpr int kSortSlots = 32768;  // keys the table holds (128 KiB of LDS)
 constexpr size_t kSortLds = (size_t)kSortRun * 8 > (size_t)kSortSlots * 4
                                 ? (size_t)kSortRun * 8 : (size_t)kSortSlots * 4;
 
-// Exclusive prefix sum of one int per thread over the workgroup; `total`
-// gets the sum.  Uses wave_sums[kSortWaves]; ends with a barrier.
-__device__ inline int block_excl_scan(int v, int* wave_sums, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < kSortWaves; ++w) {
-    const int s = wave_sums[w];
-    before += w < wave ? s : 0;
-    all += s;
-  }
-  total = all;
-  __syncthreads();  // wave_sums may be reused
-  return before + incl - v;
-}
-
 __global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(
     const int32_t* __restrict__ key, const int32_t* __restrict__ other, int n,
     int32_t* __restrict__ key_out, int32_t* __restrict__ other_out) {
@@ -95,21 +77,33 @@ __global__ __launch_bounds__(kSortThreads) void sort_pages_kernel(
     __syncthreads();
   }
   if (s_bad == 0) {
-    // thread t reads out table places [t c, t c + c), in order
+    // Read the table out in order: wave w owns places [w R / 16, (w+1) R / 16)
+    // and walks them 64 at a time; a ballot over the occupied places gives
+    // each lane its output position, so consecutive lanes write consecutive
+    // entries.  One pass counts, a scan over the waves places them, a
+    // second pass writes.
     const int slots = s_max + 1;
-    const int c = (slots + kSortThreads - 1) / kSortThreads;
-    const int p0 = tid * c < slots ? tid * c : slots;
-    const int p1 = p0 + c < slots ? p0 + c : slots;
-    int mine = 0;
-    for (int p = p0; p < p1; ++p) mine += table[p] >= 0 ? 1 : 0;
-    int total;
-    int o = base + block_excl_scan(mine, s_wave, total);
-    for (int p = p0; p < p1; ++p) {
-      const int i = table[p];
-      if (i < 0) continue;
-      key_out[o] = p;
-      if (other_out) other_out[o] = other[base + i];
-      ++o;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q0 = (int)((long long)wave * slots / kSortWaves);
+    const int q1 = (int)((long long)(wave + 1) * slots / kSortWaves);
+    int count = 0;
+    for (int q = q0; q < q1; q += 64) {
+      const bool hit = q + lane < q1 && table[q + lane] >= 0;
+      count += __builtin_popcountll(__builtin_amdgcn_ballot_w64(hit));
+    }
+    if (lane == 0) s_wave[wave] = count;
+    __syncthreads();
+    int o = base;
+    for (int w = 0; w < wave; ++w) o += s_wave[w];
+    for (int q = q0; q < q1; q += 64) {
+      const int i = q + lane < q1 ? table[q + lane] : -1;
+      const unsigned long long hits = __builtin_amdgcn_ballot_w64(i >= 0);
+      if (i >= 0) {
+        const int at = o + (int)__builtin_popcountll(hits & ((1ull << lane) - 1ull));
+        key_out[at] = q + lane;
+        if (other_out) other_out[at] = other[base + i];
+      }
+      o += (int)__builtin_popcountll(hits);
     }
     return;
   }
