@@ -168,7 +168,13 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
 
 // Cache-policy bits of the codec's streaming loads and stores.  Each input
 // line is read by one load instruction and never again, so those loads are
-// non-temporal (nt); non-temporal stores measured slower and stay default.
+// non-temporal (nt).  The page decoder's stores (bf16 pages, 4 bytes out
+// for each byte in) are non-temporal too: with the page list in slot order
+// and calls back to back it took 234.5 against 249.9 us per call with them
+// (a single call after a cache flush: 241 against 221 us, the cached stores
+// then draining after the kernel).  The encoder's stores stay default:
+// non-temporal, they gained 3.5 us on Llama-3-8B pages but cost 28 us on MLA
+// pages and 10% of the offload rate into pinned host memory.
 #ifndef KVFP4_CODEC_LOAD_AUX
 #define KVFP4_CODEC_LOAD_AUX 2
 #endif
@@ -180,6 +186,9 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
 #endif
 #ifndef KVFP4_CODEC_STORE_AUX
 #define KVFP4_CODEC_STORE_AUX 0
+#endif
+#ifndef KVFP4_DEQUANT_STORE_AUX
+#define KVFP4_DEQUANT_STORE_AUX 2
 #endif
 // One lane's half block (8 bf16 values in `a`) of tensor t -> the block's
 // E4M3 scale code (identical in both lanes of the pair) and the 4 data bytes
@@ -516,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
         decode8(dw[u], row, flip, o);
         if (hb < hhi)
           __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rout, hb * 16, 0,
-                                                 KVFP4_CODEC_STORE_AUX);
+                                                 KVFP4_DEQUANT_STORE_AUX);
       }
     }
   }
