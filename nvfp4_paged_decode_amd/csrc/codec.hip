@@ -172,9 +172,11 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
 // for each byte in) are non-temporal too: with the page list in slot order
 // and calls back to back it took 234.5 against 249.9 us per call with them
 // (a single call after a cache flush: 241 against 221 us, the cached stores
-// then draining after the kernel).  The encoder's stores stay default:
-// non-temporal, they gained 3.5 us on Llama-3-8B pages but cost 28 us on MLA
-// pages and 10% of the offload rate into pinned host memory.
+// then draining after the kernel).  The encoder's data words are stored
+// non-temporal (back to back: Llama-3-8B pages 256.5 against 262.2 us, MLA
+// pages 312.6 against 327.7 us) and its scale bytes default: byte stores,
+// four to a line from different waves, made non-temporal cost 28 us on MLA
+// pages.
 #ifndef KVFP4_CODEC_LOAD_AUX
 #define KVFP4_CODEC_LOAD_AUX 2
 #endif
@@ -189,6 +191,9 @@ __device__ inline uint32_t encode_pair(uint32_t raw, const Thr& t, uint32_t k15,
 #endif
 #ifndef KVFP4_DEQUANT_STORE_AUX
 #define KVFP4_DEQUANT_STORE_AUX 2
+#endif
+#ifndef KVFP4_QUANT_DATA_STORE_AUX
+#define KVFP4_QUANT_DATA_STORE_AUX 2
 #endif
 // One lane's half block (8 bf16 values in `a`) of tensor t -> the block's
 // E4M3 scale code (identical in both lanes of the pair) and the 4 data bytes
@@ -257,7 +262,7 @@ __device__ inline void encode_round(const QuantLds& s, Rsrc rin, Rsrc rout, int 
     // are given an offset past the buffer: the store is dropped
     const bool in = hb < hpp;
     __builtin_amdgcn_raw_buffer_store_b32(word, rout, in ? hb * 4 : kNoStore, 0,
-                                          KVFP4_CODEC_STORE_AUX);
+                                          KVFP4_QUANT_DATA_STORE_AUX);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, rout,
                                          in && (hb & 1) == 0 ? data_bytes + blk : kNoStore, 0,
                                          KVFP4_CODEC_STORE_AUX);
