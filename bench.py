@@ -102,10 +102,10 @@ def append_bytes(geometry, tokens: int, elem_bytes: int) -> int:
     return tokens * (per * elem_bytes + per * 9 // 16 + 8)
 
 
-# Each leg's traffic mix, for reading its bandwidth against a plain stream of
-# the same mix: decode reads (the merge's few writes aside); the encoder reads
-# 32 bytes of bf16 for every 9 it writes, the decoder the reverse.
-# the streaming legs' traffic mixes (the page-list sort, a few KiB, has none)
+# Each streaming leg's traffic mix, for reading its bandwidth against a plain
+# stream of the same mix: decode reads (the merge's few writes aside); the
+# encoder reads 32 bytes of bf16 for every 9 it writes, the decoder the
+# reverse.  The page-list sort (a few KiB) has none.
 LEG_MIX = {"decode": "read", "quantize": "read4_write1", "dequantize": "read1_write4"}
 YARDSTICK_KINDS = {"read": (0, 1.0), "write": (1, 1.0), "read4_write1": (2, 1.25),
                    "read1_write4": (3, 1.25)}
