@@ -87,38 +87,16 @@ struct QuantLds {
 
 __device__ inline uint32_t dup_half(uint32_t x) { return (x & 0xFFFFu) | (x << 16); }
 
-__device__ inline void build_quant_tables(QuantLds& s, int nt, float gs0, float gs1) {
-  const double mu[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-  if (threadIdx.x < 2) s.inv6gs[threadIdx.x] = 1.0 / (6.0 * (double)(threadIdx.x ? gs1 : gs0));
-  for (int i = threadIdx.x; i < nt * 128; i += blockDim.x) {
-    int t = i >> 7, j = i & 127;
-    double gs = t == 0 ? (double)gs0 : (double)gs1;
-    uint32_t th = kPad;
-    if (j < 126) {  // E4M3 midpoint between codes j and j+1, times 6 gs
-      double mid = 0.5 * ((double)e4m3_to_float(j) + (double)e4m3_to_float(j + 1));
-      th = gt_threshold(mid * 6.0 * gs, (j & 1) == 0);
-    }
-    s.e4m3[t][j] = (uint16_t)th;
-    double sb = (double)e4m3_to_float(j);
-    uint32_t T[7];
-    for (int k = 0; k < 7; ++k) {
-      uint32_t v = kPad;
-      if (j >= 1 && j <= 126) v = gt_threshold(mu[k] * sb * gs, (k & 1) == 0);
-      T[k] = v;
-    }
-    const uint32_t d51 = (T[5] - T[1]) & 0xFFFFu, d40 = (T[4] - T[0]) & 0xFFFFu;
-    const uint32_t d20 = (T[2] - T[0]) & 0xFFFFu;
-    const uint32_t dd = (((T[6] - T[4]) & 0xFFFFu) - d20) & 0xFFFFu;
-    s.thr[t][j][0] = (u32x4){dup_half(T[0]), dup_half(T[1]), dup_half(T[3]), dup_half(d51)};
-    s.thr[t][j][1] = (u32x4){dup_half(d40), dup_half(d20), dup_half(dd), 0u};
-  }
-}
-
-// bf16_bits_directed for a positive fp64 normal x, without branches (the
-// round-unit encoder builds its tables for every round, so the build is on
-// each workgroup's path): x = m 2^(e - 52); the bf16 step at x is
-// 2^(max(e, -126) - 7), and a shift past m's 53 bits leaves 0 with m as the
-// remainder, so capping the shift at 63 changes nothing.
+// Directed rounding of a positive fp64 normal x to a bf16 bit pattern: the
+// largest bf16 <= x (up = false) or the smallest bf16 >= x (up = true), with
+// +inf / the largest finite value past the range.  For non-negative values
+// bf16 bit patterns order like the values, so an exact fp64 threshold M
+// becomes an integer threshold t on magnitude bits: v > t <=> value > M is
+// t = down(M); value >= M is t = up(M) - 1.  Written without branches (the
+// encoders build their tables on every workgroup's path): x = m 2^(e - 52);
+// the bf16 step at x is 2^(max(e, -126) - 7), and a shift past m's 53 bits
+// leaves 0 with m as the remainder, so capping the shift at 63 changes
+// nothing.
 __device__ __forceinline__ uint32_t bf16_bits_directed_normal(double x, bool up) {
   const uint64_t b = (uint64_t)__double_as_longlong(x);
   const int e = (int)(b >> 52) - 1023;
@@ -130,13 +108,16 @@ __device__ __forceinline__ uint32_t bf16_bits_directed_normal(double x, bool up)
   const long long cap = up ? 0x7F80 : 0x7F7F;
   return (uint32_t)(bits < cap ? bits : cap);
 }
-// build_quant_tables for tensors [t0, t0 + tn) (tn <= 2), the same tables:
-// each scale code's eight thresholds (seven element thresholds and the
-// scale threshold) are computed by two threads, four each and without
-// branches; then each code's seven element thresholds are turned into its
-// two rows.  Fixed trip counts (a thread-strided loop here made the compiler
-// keep the buffer descriptors in VGPRs); forced inline (as a call it spilled
-// through scratch).  Ends with a barrier.
+// The encoder's tables for tensors [t0, t0 + tn) (tn <= 2): per scale code
+// j, the scale threshold (the E4M3 midpoint between codes j and j + 1, times
+// 6 gs, strict for even j) and the seven element thresholds (E2M1 midpoints
+// times the code's scale times gs, strict for even k), as integer
+// thresholds on bf16 magnitude bits.  Each code's eight thresholds are
+// computed by two threads, four each and without branches; then each code's
+// seven element thresholds are turned into its two rows.  Fixed trip counts
+// (a thread-strided loop here made the compiler keep the buffer descriptors
+// in VGPRs); forced inline (as a call it spilled through scratch).  Ends
+// with a barrier.
 struct QuantRaw {
   uint16_t t[2][128][8];  // element thresholds T0..T6 per tensor and code
 };
@@ -345,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint8_t* __restrict__ packed, int packed_pages, const int32_t* __restrict__ dst,
     int num_pages, float gs0, float gs1) {
   __shared__ QuantLds s;
-  build_quant_tables(s, g.nt, gs0, gs1);
-  __syncthreads();
+  __shared__ QuantRaw raw;
+  build_quant_tables_items(s, raw, 0, g.nt, gs0, gs1);
   const int hpp = (int)(g.elems() / 8);  // half-blocks per page
   const int bpt = g.blocks_per_tensor();
   const int data_bytes = (int)g.data_bytes();
@@ -464,6 +445,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     const int32_t* __restrict__ page_rows, uint8_t* __restrict__ packed, int packed_pages,
     float gs0, float gs1) {
   __shared__ QuantLds s;
+  __shared__ QuantRaw raw;
   // The C ABI bounds num_tokens * half-blocks per token below 2^31.
   const uint32_t hd8 = (uint32_t)(g.H * g.D / 8);     // half-blocks per tensor row (even)
   const uint32_t hpt = (uint32_t)g.nt * hd8;           // half-blocks per token
@@ -480,8 +462,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   for (int u = 0; u < kUnroll; ++u)
     append_load<kFp8>(in[u], first + u * kThreads + threadIdx.x, total, hpt, hd8, rows, slots,
                       page_rows);
-  build_quant_tables(s, g.nt, gs0, gs1);
-  __syncthreads();
+  build_quant_tables_items(s, raw, 0, g.nt, gs0, gs1);
   // the loop bound is uniform over the workgroup: every lane runs the body,
   // since the DPP exchange needs both halves of a block
   for (uint32_t base = first; base < total; base += stride) {

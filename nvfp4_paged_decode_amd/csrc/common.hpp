@@ -33,32 +33,6 @@ struct Geom {
   __host__ __device__ int blocks_per_tensor() const { return T * H * (D / kBlock); }
 };
 
-// ---------------------------------------------------------------------------
-// Directed rounding of a non-negative fp64 value to a bf16 bit pattern.
-// Used to turn exact fp64 rounding thresholds into integer thresholds on
-// bf16 bit patterns (for non-negative floats, bit patterns order like the
-// values they encode).
-// ---------------------------------------------------------------------------
-__device__ inline uint32_t bf16_bits_directed(double x, bool up) {
-  if (!(x > 0.0)) return 0u;
-  int E;
-  (void)frexp(x, &E);               // x = f * 2^E, f in [0.5, 1)
-  int e = E - 1;                    // floor(log2 x)
-  if (e < -126) e = -126;           // bf16 subnormals share the 2^-126 spacing base
-  if (e > 200) return up ? 0x7F80u : 0x7F7Fu;
-  double y = ldexp(x, 7 - e);       // exact: x / 2^(e-7), in [0, 256)
-  double k = up ? ceil(y) : floor(y);
-  long long bits = ((long long)(e + 126) << 7) + (long long)k;
-  if (up) return bits > 0x7F80 ? 0x7F80u : (uint32_t)bits;
-  return bits > 0x7F7F ? 0x7F7Fu : (uint32_t)bits;
-}
-
-// Threshold t on bf16 magnitude bits v such that  v > t  <=>  value > M
-// (strict) or value >= M (non-strict), for an exact fp64 M > 0.
-__device__ inline uint32_t gt_threshold(double M, bool strict) {
-  return strict ? bf16_bits_directed(M, false) : bf16_bits_directed(M, true) - 1u;
-}
-
 // 4 floats as fp16 (round to nearest even), packed for one 8-byte store,
 // and back.  The unpack works on the two 32-bit words with shifts: a
 // bit_cast of a vector element (w.y) to a 2 x fp16 vector compiled to a
